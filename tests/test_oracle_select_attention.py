@@ -1,0 +1,183 @@
+"""Pins of the oracle's LUT/proxy (Eq. (6), (27)), hybrid selection (Eq. (7)-(10)) and attention."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import scope_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --- Eq. (27) and check (a) -------------------------------------------------
+
+def test_eq27_lut_sum_equals_product_code_inner_product():
+    rng = np.random.default_rng(0)
+    split, d, N, Cq, Cm = (16, 24, 24), 64, 300, 7, 9
+    qc = rng.standard_normal((Cq, d))
+    kc = rng.standard_normal((Cm, d))
+    codes = rng.integers(0, Cm, (N, 3))
+    P = O.lookup_tables(qc, kc, split)
+    s = O.proxy_logits(P, codes, d)
+    offs = [0, 16, 40]
+    khat = np.concatenate([kc[codes[:, m], o:o + dm] for m, (o, dm) in enumerate(zip(offs, split))], 1)
+    np.testing.assert_allclose(s, qc @ khat.T / 8.0, rtol=1e-12, atol=1e-12)
+
+
+def test_check_a_proxy_is_exact_logit_when_every_key_is_its_own_centroid():
+    w = workloads.small("a", 2, 3, 4, 64, (16, 24, 24), "f32", 24, 24, H=1, iters=3)
+    q, k, v = workloads.generate(w)
+    r = O.workload_head(w, 0, q[0], k[0], v[0])
+    # every query / key sub-vector is its own centroid
+    np.testing.assert_array_equal(np.sort(r["q_labels"]), np.arange(24))
+    exact = r["q_rope"] @ r["k_rope"].T / 8.0
+    qc = r["q_centroids"][r["q_labels"]]         # row i -> centroid of query i == query i
+    np.testing.assert_array_equal(qc, r["q_rope"])
+    s_rows = r["scores"][r["q_labels"]]          # proxy logits of each query's own cluster
+    np.testing.assert_allclose(s_rows, exact, rtol=1e-12, atol=1e-12)
+
+
+# --- Top-p (Eq. (7)) --------------------------------------------------------
+
+def test_top_p_closed_form_when_all_scores_tie():
+    for N, rho in [(256, 0.9), (100, 0.5), (17, 0.31)]:
+        t = O.top_p_count(np.full(N, 0.37), rho)
+        assert t == math.ceil(Fraction(rho).limit_denominator(1000) * N)
+    s = np.zeros((1, 256))
+    t, b, kh, r, sel = O.hybrid_select(s, np.array([5]), 0.9, 0.0)
+    assert t[0] == 231 and r[0] == 231
+    np.testing.assert_array_equal(sel[0], np.arange(231))
+
+
+def test_top_p_limits():
+    s = np.array([0.1, 3.0, 3.0, -1.0, 2.0])
+    assert O.top_p_count(s, 1e-12) == 1
+    assert O.key_order(s)[0] == 1                  # equal logits: lower index first
+    assert O.top_p_count(s, 1.0) == 5
+
+
+def _top_p_brute(s, rho):
+    # t = 1 + #{positions whose inclusive prefix mass < rho}, prefix by (s desc, j asc)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    N = len(s)
+    cnt = 0
+    for j in range(N):
+        before = [(s[i] > s[j]) or (s[i] == s[j] and i <= j) for i in range(N)]
+        if math.fsum(p[before]) < rho:
+            cnt += 1
+    return min(cnt + 1, N)
+
+
+def test_top_p_matches_sort_free_brute_force():
+    rng = np.random.default_rng(4)
+    for trial in range(30):
+        N = int(rng.integers(2, 40))
+        s = np.round(rng.standard_normal(N) * 2, 1)   # rounding makes ties
+        rho = float(rng.uniform(0.05, 0.99))
+        assert O.top_p_count(s, rho) == _top_p_brute(s, rho)
+
+
+def test_golden_hand_examples():
+    with open(os.path.join(GOLDEN, "select_worked_example.json")) as f:
+        doc = json.load(f)
+    for ex in doc["examples"]:
+        s = np.log(np.array(ex["weights"], dtype=np.float64))
+        n = np.array(ex["n"])
+        t, b, kh, r, sel = O.hybrid_select(s, n, ex["rho"], ex["alpha"])
+        assert t.tolist() == ex["t"]
+        assert b.tolist() == ex["b"]
+        assert kh == ex["k_head"]
+        assert r.tolist() == ex["r"]
+        assert [x.tolist() for x in sel] == ex["sel"]
+
+
+# --- k_head (Eq. (9)) and r_c (Eq. (10)) -------------------------------------
+
+def test_k_head_examples_and_bounds():
+    assert O.k_head_of([3, 1], [2, 7]) == 4          # 13/4 -> 4
+    assert O.k_head_of([2, 2], [3, 5]) == 4          # exactly 4
+    assert O.k_head_of([1, 0, 5], [100, 1, 1]) == 18  # 105/6 = 17.5 -> 18
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        n = rng.integers(0, 50, 20)
+        n[0] += 1
+        b = rng.integers(1, 10000, 20)
+        kh = O.k_head_of(n, b)
+        mean = Fraction(int((n * b).sum()), int(n.sum()))
+        assert kh - 1 < mean <= kh
+        assert b[n > 0].min() <= kh <= b[n > 0].max()
+
+
+def test_selection_invariants_and_nesting():
+    rng = np.random.default_rng(9)
+    Cq, N = 6, 200
+    s = rng.standard_normal((Cq, N)) * 1.5
+    s[:, 50:60] = s[:, 50:51]                        # a tie group
+    n = np.array([10, 0, 40, 3, 70, 77])
+    prev = None
+    for rho in (0.5, 0.7, 0.9, 0.95):
+        t, b, kh, r, sel = O.hybrid_select(s, n, rho, 0.05)
+        assert np.all(b >= t) and np.all(b >= math.ceil(0.05 * N))
+        assert r[1] == 0 and len(sel[1]) == 0
+        for c in range(Cq):
+            if n[c]:
+                assert r[c] == max(b[c], kh) and len(sel[c]) == r[c]
+                assert np.all(np.diff(sel[c]) > 0)
+                # selected keys score at least as high as every key left out
+                out = np.setdiff1d(np.arange(N), sel[c])
+                if len(out):
+                    assert s[c, sel[c]].min() >= s[c, out].max()
+        if prev is not None:
+            for c in range(Cq):
+                assert set(prev[c]).issubset(set(sel[c]))
+        prev = sel
+
+
+# --- attention ----------------------------------------------------------------
+
+def test_rho_one_is_dense_attention():
+    rng = np.random.default_rng(10)
+    N, d, Cq = 90, 64, 4
+    q, k, v = rng.standard_normal((3, N, d))
+    labels = rng.integers(0, Cq, N)
+    sel = [np.arange(N)] * Cq
+    out = O.sparse_attention(q, k, v, labels, sel)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None])[0].numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_single_key_gives_that_value_and_convexity():
+    rng = np.random.default_rng(11)
+    N, d = 40, 64
+    q, k, v = rng.standard_normal((3, N, d))
+    labels = np.arange(N) % 3
+    out = O.sparse_attention(q, k, v, labels, [np.array([7]), np.array([2, 9, 30]), np.array([5])])
+    np.testing.assert_array_equal(out[labels == 0], np.broadcast_to(v[7], out[labels == 0].shape))
+    sub = v[[2, 9, 30]]
+    o1 = out[labels == 1]
+    assert np.all(o1 <= sub.max(0) + 1e-12) and np.all(o1 >= sub.min(0) - 1e-12)
+
+
+def test_tiny_end_to_end_invariants():
+    w = workloads.CONFIGS["tiny"]
+    q, k, v = workloads.generate(w)
+    for bh in range(w.BH):
+        r = O.workload_head(w, bh, q[bh], k[bh], v[bh])
+        n = r["n"]
+        assert n.sum() == w.N and r["k_head"] == O.k_head_of(n, r["b"])
+        assert np.all(r["t"] >= 1) and np.all(r["r"] <= w.N)
+        assert sorted(r["perm_q"].tolist()) == list(range(w.N))
+        assert r["q_off"][-1] == w.N
+        # rho = 1 on the same clustering is dense attention
+        d = O.workload_head(w, bh, q[bh], k[bh], v[bh], rho=1.0)
+        logit = d["q_rope"] @ d["k_rope"].T / 8.0
+        p = np.exp(logit - logit.max(1, keepdims=True))
+        dense = (p @ v[bh]) / p.sum(1, keepdims=True)
+        np.testing.assert_allclose(d["out"], dense, atol=1e-12)
