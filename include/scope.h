@@ -1,0 +1,137 @@
+/*
+ * scope.h - C ABI of the SCOPE sparse-attention hot path for video DiTs,
+ * built for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "SCOPE: Subspace Clustering with Online Per-Head Top-K Estimation
+ * for Sparse Video Attention" (arXiv 2608.12780).  The abstract fixes the
+ * pipeline (3D-RoPE-aligned key subspace clustering, LUT proxy scores,
+ * hybrid Top-p with an online per-head Top-k, exact attention over the
+ * selected original keys and values); the pith.science review of the paper
+ * quotes Eq. (3), (6)-(10) and (27) and the hyper-parameters.
+ *
+ * One attention layer is split into two calls:
+ *   scope_plan   - per (batch, head): 3D RoPE on Q/K; k-means of the queries
+ *                  (Cq clusters) and of the key T/H/W channel subspaces (Cm
+ *                  centroids each; Eq. (3)); lookup tables of query-centroid .
+ *                  key-subspace-centroid dot products; proxy logits (Eq. (6));
+ *                  Top-p counts t_c (Eq. (7)), base counts b_c (Eq. (8)),
+ *                  k_head (Eq. (9)), final counts r_c (Eq. (10)) and the
+ *                  selected key sets S_c.
+ *   scope_attend - o_i = softmax over j in S_c(i) of <q'_i, k'_j>/sqrt(d),
+ *                  times v_j, on the original post-RoPE keys and values.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers; the caller allocates and owns
+ *     every buffer (the library never allocates, frees or keeps state).
+ *   - Q, K, V, Q', K' and O are [B][H][N][d] contiguous, N = T*Hg*Wg, token
+ *     n = (t*Hg + h)*Wg + w; element type per scope_params.dtype (bf16 as
+ *     raw uint16 bit patterns, or fp32).  Base pointers must be 256-byte
+ *     aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t); no call synchronises the
+ *     host.  Results become visible in stream order.
+ *   - Parameter errors are reported synchronously, before any launch.  No
+ *     C++ exception crosses the ABI.
+ *   - Calls that overlap in time must use distinct workspaces and plans.
+ */
+#ifndef SCOPE_H
+#define SCOPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SCOPE_OK = 0,
+  SCOPE_ERR_INVALID = 1,      /* bad parameter, null or misaligned pointer */
+  SCOPE_ERR_UNSUPPORTED = 2,  /* valid but not implemented (d not in {64, 128}) */
+  SCOPE_ERR_WORKSPACE = 3,    /* workspace smaller than scope_workspace_size() */
+  SCOPE_ERR_CAPACITY = 4,     /* plan buffer smaller than the sizes below */
+  SCOPE_ERR_HIP = 5           /* a HIP launch or runtime call failed */
+} scope_status;
+
+typedef enum { SCOPE_F32 = 0, SCOPE_BF16 = 1 } scope_dtype;
+
+/* scope_params.flags */
+#define SCOPE_USE_INIT_CENTROIDS 0x1u /* start Lloyd from plan->q_centroids / k_centroids
+                                         instead of seeded k-means++ */
+
+typedef struct {
+  int32_t B, H;            /* batch and heads; every (b, h) is independent */
+  int32_t T, Hg, Wg;       /* latent grid; N = T*Hg*Wg tokens */
+  int32_t d;               /* head dim, 64 or 128 */
+  int32_t d_t, d_h, d_w;   /* 3D-RoPE channel ranges [T | H | W], each even, sum d */
+  int32_t Cq;              /* query clusters, 1..N */
+  int32_t Cm;              /* centroids per key subspace (CT = CH = CW), 1..min(N, 32767) */
+  int32_t iters;           /* Lloyd iterations after seeding, 0..1000 */
+  double rope_base;        /* RoPE base, > 1 (10000) */
+  double rho;              /* Top-p threshold of Eq. (7), 0 < rho <= 1 */
+  double alpha;            /* fixed Top-k floor of Eq. (8) as a fraction of N, 0..1 */
+  uint64_t seed;           /* k-means++ draws: SplitMix64 outputs */
+  int32_t dtype;           /* scope_dtype */
+  uint32_t flags;          /* SCOPE_USE_INIT_CENTROIDS */
+} scope_params;
+
+/* Device buffers of one plan (all caller-allocated; sizes in elements).
+ * Required by scope_plan and scope_attend: perm_q .. status.
+ * Optional (may be NULL; when set, scope_plan writes the intermediate there,
+ * and SCOPE_USE_INIT_CENTROIDS reads initial centroids from there):
+ * q_centroids .. lut. */
+typedef struct {
+  int32_t* perm_q;       /* [B*H][N]: tokens grouped by query cluster, ascending inside a cluster */
+  int32_t* q_off;        /* [B*H][Cq+1]: cluster c of head bh is perm_q[bh][q_off[c] .. q_off[c+1]) */
+  int32_t* counts_t;     /* [B*H][Cq]: Top-p counts t_c (Eq. 7) */
+  int32_t* counts_b;     /* [B*H][Cq]: base counts b_c = max(t_c, ceil(alpha*N)) (Eq. 8) */
+  int32_t* counts_r;     /* [B*H][Cq]: final counts r_c (Eq. 10); 0 for empty clusters */
+  int32_t* k_head;       /* [B*H]: ceil(sum n_c b_c / sum n_c) (Eq. 9) */
+  int64_t* sel_off;      /* [B*H*Cq + 1]: CSR offsets into sel_idx, cluster-major over all heads */
+  int32_t* sel_idx;      /* [sel_capacity]: key indices of S_c, ascending inside each cluster */
+  int64_t sel_capacity;  /* elements of sel_idx; B*H*Cq*N always suffices */
+  int32_t* work;         /* [2*work_capacity]: attention work items (built by scope_plan) */
+  int64_t work_capacity; /* items; from scope_workspace_size */
+  int32_t* status;       /* [4]: [0] work items, [1] set if sum r_c > sel_capacity */
+  float* q_centroids;    /* [B*H][Cq][d] final query centroids (fp32) */
+  float* k_centroids;    /* [B*H][Cm][d] key centroids, row z = (mu^T_z | mu^H_z | mu^W_z) */
+  int32_t* q_labels;     /* [B*H][N] query cluster of each token */
+  uint16_t* k_codes;     /* [B*H][N][4] (z^T, z^H, z^W, 0) key subspace codes */
+  int32_t* seeds;        /* [B*H][4][max(Cq,Cm)] k-means++ centre indices (Q, T, H, W) */
+  double* lut;           /* [B*H][Cq][3][Cm] lookup tables P^m[c][z] (fp64) */
+} scope_plan_t;
+
+/* Sizes for a parameter set: workspace bytes for scope_plan, the worst-case
+ * sel_idx capacity (B*H*Cq*N) and the attention work-list capacity.
+ * Any output pointer may be NULL.  Returns SCOPE_ERR_INVALID /
+ * SCOPE_ERR_UNSUPPORTED for bad parameters. */
+scope_status scope_workspace_size(const scope_params* p, size_t* ws_bytes,
+                                  int64_t* sel_capacity_worst, int64_t* work_capacity);
+
+/* Stages RoPE .. selection.  q, k: pre-RoPE [B][H][N][d]; q_rope, k_rope:
+ * outputs of the same shape (the rotated Q'/K' that scope_attend reads).
+ * ws: device workspace of at least scope_workspace_size() bytes, 256-byte
+ * aligned; its contents are scratch.  If sum_c r_c exceeds
+ * plan->sel_capacity, plan->status[1] is set on the device, sel_idx is left
+ * incomplete and scope_attend skips every head. */
+scope_status scope_plan(const scope_params* p, const void* q, const void* k, void* q_rope,
+                        void* k_rope, scope_plan_t* plan, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Rebuilds plan->work and plan->status[0] from perm_q/q_off/counts_r/sel_off
+ * for a plan whose CSR was written by the caller (for instance copied from
+ * another implementation).  scope_plan already does this. */
+scope_status scope_plan_finalize(const scope_params* p, scope_plan_t* plan, hipStream_t stream);
+
+/* Stage attention: out[bh][i] = sum_{j in S_c(i)} softmax_j(<q'_i, k'_j>/sqrt(d)) v[bh][j].
+ * One kernel launch; needs no workspace. */
+scope_status scope_attend(const scope_params* p, const scope_plan_t* plan, const void* q_rope,
+                          const void* k_rope, const void* v, void* out, hipStream_t stream);
+
+/* Static string for a status code. */
+const char* scope_status_string(scope_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SCOPE_H */

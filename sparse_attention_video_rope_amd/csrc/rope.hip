@@ -1,0 +1,107 @@
+// Stage 1: 3D rotary position embedding of Q and K, fused with the cast to the
+// storage type.  The head channels are the concatenation of the temporal,
+// height and width ranges of 3D RoPE (the ranges SCOPE's key subspaces follow,
+// per the SCOPE abstract); inside a range of width d_m at offset o, channel
+// pair (o+2i, o+2i+1) of token (t, h, w) rotates by p * base^(-2i/d_m), with
+// p the token's t, h or w index.  The rotation is evaluated in fp64 and
+// rounded once to bf16 or fp32.  HBM-bound: 2 tensors x (read + write).
+#include "scope_device.hpp"
+#include "scope_internal.hpp"
+
+namespace scope {
+
+struct RopeArgs {
+  int BH, N, d, Hg, Wg;
+  int off1, off2;               // start of the H and W ranges
+  int dm[3], toff[3];
+};
+
+__global__ void rope_table_kernel(double2* tab, int n0, int n1, int n2, int dm0, int dm1, int dm2,
+                                  double base) {
+  int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n0 + n1 + n2) return;
+  int r = idx, dm = dm0;
+  if (r >= n0) { r -= n0; dm = dm1; if (r >= n1) { r -= n1; dm = dm2; } }
+  const int half = dm / 2, p = r / half, i = r % half;
+  const double theta = pow(base, -(2.0 * i) / dm);
+  double sn, cs;
+  sincos((double)p * theta, &sn, &cs);
+  tab[idx] = make_double2(cs, sn);
+}
+
+template <typename T> struct Vec8;
+template <> struct Vec8<uint16_t> {
+  uint16_t v[8];
+  __device__ void load(const uint16_t* p) { *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(p); }
+  __device__ void store(uint16_t* p) const { *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(v); }
+};
+template <> struct Vec8<float> {
+  float v[8];
+  __device__ void load(const float* p) {
+    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(p);
+    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ void store(float* p) const {
+    *reinterpret_cast<float4*>(p) = *reinterpret_cast<const float4*>(v);
+    *reinterpret_cast<float4*>(p + 4) = *reinterpret_cast<const float4*>(v + 4);
+  }
+};
+
+// One thread rotates 8 consecutive channels (4 pairs) of one token of Q or K.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                   T* __restrict__ qo, T* __restrict__ ko,
+                                                   const double2* __restrict__ tab, RopeArgs a) {
+  const int64_t per = (int64_t)a.BH * a.N * (a.d / 8);
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= 2 * per) return;
+  const int sel = gid >= per;
+  const int64_t r = gid - sel * per;
+  const int chunk = (int)(r % (a.d / 8));
+  const int64_t row = r / (a.d / 8);
+  const int n = (int)(row % a.N);
+  const int pos[3] = {n / (a.Hg * a.Wg), (n / a.Wg) % a.Hg, n % a.Wg};
+  const int64_t base = row * a.d + chunk * 8;
+  Vec8<T> x;
+  x.load((sel ? k : q) + base);
+#pragma unroll
+  for (int pi = 0; pi < 4; ++pi) {
+    const int ch = chunk * 8 + 2 * pi;
+    const int m = ch < a.off1 ? 0 : (ch < a.off2 ? 1 : 2);
+    const int o = m == 0 ? 0 : (m == 1 ? a.off1 : a.off2);
+    const double2 cs = tab[a.toff[m] + pos[m] * (a.dm[m] / 2) + (ch - o) / 2];
+    const double x0 = Elem<T>::ld(&x.v[2 * pi]), x1 = Elem<T>::ld(&x.v[2 * pi + 1]);
+    double y0, y1;
+    {
+#pragma clang fp contract(off)
+      y0 = x0 * cs.x - x1 * cs.y;
+      y1 = x0 * cs.y + x1 * cs.x;
+    }
+    Elem<T>::st(&x.v[2 * pi], y0);
+    Elem<T>::st(&x.v[2 * pi + 1], y1);
+  }
+  x.store((sel ? ko : qo) + base);
+}
+
+hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const void* k, void* qo,
+                       void* ko, const Workspace& w, hipStream_t s) {
+  const int n0 = g.T * g.dm[1] / 2, n1 = g.Hg * g.dm[2] / 2, n2 = g.Wg * g.dm[3] / 2;
+  rope_table_kernel<<<(n0 + n1 + n2 + 255) / 256, 256, 0, s>>>(w.rope_tab, n0, n1, n2, g.dm[1], g.dm[2],
+                                                               g.dm[3], p.rope_base);
+  RopeArgs a;
+  a.BH = g.BH; a.N = g.N; a.d = g.d; a.Hg = g.Hg; a.Wg = g.Wg;
+  a.off1 = g.off[2]; a.off2 = g.off[3];
+  a.dm[0] = g.dm[1]; a.dm[1] = g.dm[2]; a.dm[2] = g.dm[3];
+  a.toff[0] = 0; a.toff[1] = n0; a.toff[2] = n0 + n1;
+  const int64_t threads = 2 * (int64_t)g.BH * g.N * (g.d / 8);
+  const int blocks = (int)((threads + 255) / 256);
+  if (g.bf16)
+    rope_kernel<uint16_t><<<blocks, 256, 0, s>>>((const uint16_t*)q, (const uint16_t*)k, (uint16_t*)qo,
+                                                 (uint16_t*)ko, w.rope_tab, a);
+  else
+    rope_kernel<float><<<blocks, 256, 0, s>>>((const float*)q, (const float*)k, (float*)qo, (float*)ko,
+                                              w.rope_tab, a);
+  return hipGetLastError();
+}
+
+}  // namespace scope

@@ -1,0 +1,213 @@
+// C ABI of the SCOPE hot path: parameter validation, workspace layout and the
+// stage sequence of scope_plan / scope_attend (declared in include/scope.h).
+#include <math.h>
+#include <string.h>
+
+#include "scope_internal.hpp"
+
+namespace scope {
+
+static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+Geo make_geo(const scope_params& p) {
+  Geo g;
+  memset(&g, 0, sizeof(g));
+  g.BH = p.B * p.H;
+  g.T = p.T; g.Hg = p.Hg; g.Wg = p.Wg;
+  g.N = p.T * p.Hg * p.Wg;
+  g.d = p.d;
+  g.Cq = p.Cq; g.Cm = p.Cm; g.iters = p.iters;
+  g.off[0] = 0; g.dm[0] = p.d; g.C[0] = p.Cq;
+  g.off[1] = 0; g.dm[1] = p.d_t;
+  g.off[2] = p.d_t; g.dm[2] = p.d_h;
+  g.off[3] = p.d_t + p.d_h; g.dm[3] = p.d_w;
+  g.Cmax = p.Cq > p.Cm ? p.Cq : p.Cm;
+  g.DPmax = 0; g.CmaxPad = 0;
+  for (int m = 0; m < 4; ++m) {
+    if (m > 0) g.C[m] = p.Cm;
+    g.Cpad[m] = round_up(g.C[m], 32);
+    g.dpad[m] = round_up(g.dm[m], 16);
+    if (g.dpad[m] > g.DPmax) g.DPmax = g.dpad[m];
+    if (g.Cpad[m] > g.CmaxPad) g.CmaxPad = g.Cpad[m];
+  }
+  g.bf16 = p.dtype == SCOPE_BF16;
+  g.seed = p.seed;
+  return g;
+}
+
+Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
+  Workspace w;
+  memset(&w, 0, sizeof(w));
+  size_t o = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + o : nullptr;
+    o += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  const size_t BH = g.BH, N = g.N;
+  const int nrope = g.T * g.dm[1] / 2 + g.Hg * g.dm[2] / 2 + g.Wg * g.dm[3] / 2;
+  const size_t NB = (N + 63) / 64;
+  w.rope_tab = (double2*)take(sizeof(double2) * nrope);
+  w.d2 = (double*)take(8 * BH * 4 * N);
+  w.nearest = (int32_t*)take(4 * BH * 4 * N);
+  w.bsum = (double*)take(8 * BH * 4 * NB);
+  w.seeds = (int32_t*)take(4 * BH * 4 * g.Cmax);
+  w.qcent = (float*)take(4 * BH * g.Cq * g.d);
+  w.kcent = (float*)take(4 * BH * g.Cm * g.d);
+  w.cbf = (uint16_t*)take(2 * BH * 4 * g.CmaxPad * g.DPmax);
+  w.cnorm = (float*)take(4 * BH * 4 * g.CmaxPad);
+  w.labels = (int32_t*)take(4 * BH * 4 * N);
+  w.rlist = (int32_t*)take(4 * BH * 4 * N);
+  w.rcnt = (int32_t*)take(4 * (size_t)(g.iters + 1) * BH * 4);
+  w.perm = (int32_t*)take(4 * BH * 4 * N);
+  w.off = (int32_t*)take(4 * BH * 4 * (g.Cmax + 1));
+  w.codes = (uint16_t*)take(8 * BH * N);
+  w.qlab = (int32_t*)take(4 * BH * N);
+  w.lut = (double*)take(8 * BH * g.Cq * 3 * g.Cm);
+  w.csel = (ClusterSel*)take(sizeof(ClusterSel) * BH * g.Cq);
+  w.bytes = o;
+  if (plan) {
+    if (plan->seeds) w.seeds = plan->seeds;
+    if (plan->q_centroids) w.qcent = plan->q_centroids;
+    if (plan->k_centroids) w.kcent = plan->k_centroids;
+    if (plan->k_codes) w.codes = plan->k_codes;
+    if (plan->lut) w.lut = plan->lut;
+  }
+  return w;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static scope_status validate(const scope_params* p) {
+  if (!p) return SCOPE_ERR_INVALID;
+  if (p->B < 1 || p->H < 1 || p->T < 1 || p->Hg < 1 || p->Wg < 1) return SCOPE_ERR_INVALID;
+  if ((int64_t)p->B * p->H > 65535) return SCOPE_ERR_UNSUPPORTED;
+  const int64_t N = (int64_t)p->T * p->Hg * p->Wg;
+  if (N > MAX_N) return SCOPE_ERR_UNSUPPORTED;
+  if (p->d_t < 2 || p->d_h < 2 || p->d_w < 2 || (p->d_t | p->d_h | p->d_w) & 1) return SCOPE_ERR_INVALID;
+  if (p->d_t + p->d_h + p->d_w != p->d) return SCOPE_ERR_INVALID;
+  if (p->d != 64 && p->d != 128) return SCOPE_ERR_UNSUPPORTED;
+  if (p->Cq < 1 || p->Cm < 1 || p->Cq > N || p->Cm > N) return SCOPE_ERR_INVALID;
+  if (p->Cq > MAX_C || p->Cm > MAX_C) return SCOPE_ERR_UNSUPPORTED;
+  if (p->iters < 0 || p->iters > 1000) return SCOPE_ERR_INVALID;
+  if (!(p->rope_base > 1.0) || !isfinite(p->rope_base)) return SCOPE_ERR_INVALID;
+  if (!(p->rho > 0.0 && p->rho <= 1.0)) return SCOPE_ERR_INVALID;
+  if (!(p->alpha >= 0.0 && p->alpha <= 1.0)) return SCOPE_ERR_INVALID;
+  if (p->dtype != SCOPE_F32 && p->dtype != SCOPE_BF16) return SCOPE_ERR_INVALID;
+  if (p->flags & ~SCOPE_USE_INIT_CENTROIDS) return SCOPE_ERR_INVALID;
+  return SCOPE_OK;
+}
+
+static int64_t work_cap(const Geo& g) {
+  return (int64_t)g.BH * (g.Cq + (g.N + ATT_BM - 1) / ATT_BM);
+}
+
+static scope_status check_plan_core(const scope_plan_t* pl) {
+  if (!pl) return SCOPE_ERR_INVALID;
+  if (!pl->perm_q || !pl->q_off || !pl->counts_t || !pl->counts_b || !pl->counts_r || !pl->k_head ||
+      !pl->sel_off || !pl->sel_idx || !pl->work || !pl->status)
+    return SCOPE_ERR_INVALID;
+  if (!aligned(pl->sel_off, 8) || !aligned(pl->perm_q, 4) || !aligned(pl->q_off, 4) || !aligned(pl->sel_idx, 4) ||
+      !aligned(pl->counts_t, 4) || !aligned(pl->counts_b, 4) || !aligned(pl->counts_r, 4) ||
+      !aligned(pl->k_head, 4) || !aligned(pl->work, 8) || !aligned(pl->status, 4))
+    return SCOPE_ERR_INVALID;
+  if (pl->sel_capacity < 0 || pl->work_capacity < 0) return SCOPE_ERR_INVALID;
+  return SCOPE_OK;
+}
+
+static scope_status hip_status(hipError_t e) { return e == hipSuccess ? SCOPE_OK : SCOPE_ERR_HIP; }
+
+}  // namespace scope
+
+using namespace scope;
+
+extern "C" {
+
+const char* scope_status_string(scope_status s) {
+  switch (s) {
+    case SCOPE_OK: return "ok";
+    case SCOPE_ERR_INVALID: return "invalid argument";
+    case SCOPE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SCOPE_ERR_WORKSPACE: return "workspace too small";
+    case SCOPE_ERR_CAPACITY: return "plan buffer too small";
+    case SCOPE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+scope_status scope_workspace_size(const scope_params* p, size_t* ws_bytes, int64_t* sel_capacity_worst,
+                                  int64_t* work_capacity) {
+  const scope_status st = validate(p);
+  if (st != SCOPE_OK) return st;
+  const Geo g = make_geo(*p);
+  if (ws_bytes) *ws_bytes = carve(g, nullptr, nullptr).bytes;
+  if (sel_capacity_worst) *sel_capacity_worst = (int64_t)g.BH * g.Cq * g.N;
+  if (work_capacity) *work_capacity = work_cap(g);
+  return SCOPE_OK;
+}
+
+scope_status scope_plan(const scope_params* p, const void* q, const void* k, void* q_rope, void* k_rope,
+                        scope_plan_t* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
+  scope_status st = validate(p);
+  if (st != SCOPE_OK) return st;
+  st = check_plan_core(plan);
+  if (st != SCOPE_OK) return st;
+  if (!q || !k || !q_rope || !k_rope || !ws) return SCOPE_ERR_INVALID;
+  if (!aligned(q, 256) || !aligned(k, 256) || !aligned(q_rope, 256) || !aligned(k_rope, 256) || !aligned(ws, 256))
+    return SCOPE_ERR_INVALID;
+  const void* opt[] = {plan->q_centroids, plan->k_centroids, plan->q_labels, plan->k_codes, plan->seeds, plan->lut};
+  for (const void* o : opt)
+    if (o && !aligned(o, 8)) return SCOPE_ERR_INVALID;
+  if ((p->flags & SCOPE_USE_INIT_CENTROIDS) && (!plan->q_centroids || !plan->k_centroids)) return SCOPE_ERR_INVALID;
+  const Geo g = make_geo(*p);
+  if (plan->work_capacity < work_cap(g)) return SCOPE_ERR_CAPACITY;
+  const Workspace w = carve(g, plan, (char*)ws);
+  if (ws_bytes < w.bytes) return SCOPE_ERR_WORKSPACE;
+
+  hipError_t e = hipSuccess;
+#define STEP(x) do { e = (x); if (e != hipSuccess) return hip_status(e); } while (0)
+  STEP(launch_fill_i32(w.rcnt, 0, (size_t)(g.iters + 1) * g.BH * 4, stream));
+  STEP(launch_rope(g, *p, q, k, q_rope, k_rope, w, stream));
+  if (!(p->flags & SCOPE_USE_INIT_CENTROIDS)) STEP(launch_seed(g, q_rope, k_rope, w, stream));
+  STEP(launch_prep(g, w, stream));
+  STEP(launch_assign(g, q_rope, k_rope, w, 0, stream));
+  for (int it = 1; it <= g.iters; ++it) {
+    STEP(launch_update(g, q_rope, k_rope, w, stream));
+    STEP(launch_assign(g, q_rope, k_rope, w, it, stream));
+  }
+  STEP(launch_pack(g, w, plan->q_labels, stream));
+  STEP(launch_perm(g, w, plan->perm_q, plan->q_off, stream));
+  STEP(launch_lut(g, w, stream));
+  STEP(launch_topp(g, *p, w, plan->counts_t, plan->counts_b, stream));
+  STEP(launch_khead(g, *plan, stream));
+  STEP(launch_final_select(g, *p, w, *plan, stream));
+  STEP(launch_worklist(g, *plan, stream));
+#undef STEP
+  return SCOPE_OK;
+}
+
+scope_status scope_plan_finalize(const scope_params* p, scope_plan_t* plan, hipStream_t stream) {
+  scope_status st = validate(p);
+  if (st != SCOPE_OK) return st;
+  st = check_plan_core(plan);
+  if (st != SCOPE_OK) return st;
+  const Geo g = make_geo(*p);
+  if (plan->work_capacity < work_cap(g)) return SCOPE_ERR_CAPACITY;
+  return hip_status(launch_worklist(g, *plan, stream));
+}
+
+scope_status scope_attend(const scope_params* p, const scope_plan_t* plan, const void* q_rope, const void* k_rope,
+                          const void* v, void* out, hipStream_t stream) {
+  scope_status st = validate(p);
+  if (st != SCOPE_OK) return st;
+  st = check_plan_core(plan);
+  if (st != SCOPE_OK) return st;
+  if (!q_rope || !k_rope || !v || !out) return SCOPE_ERR_INVALID;
+  if (!aligned(q_rope, 256) || !aligned(k_rope, 256) || !aligned(v, 256) || !aligned(out, 256))
+    return SCOPE_ERR_INVALID;
+  const Geo g = make_geo(*p);
+  if (plan->work_capacity < work_cap(g)) return SCOPE_ERR_CAPACITY;
+  return hip_status(launch_attend(g, *plan, q_rope, k_rope, v, out, stream));
+}
+
+}  // extern "C"

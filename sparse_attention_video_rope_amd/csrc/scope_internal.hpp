@@ -1,0 +1,89 @@
+// Internal host/device interface of the SCOPE library: derived sizes, the
+// workspace carve-up and the kernel launchers.  Not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/scope.h"
+
+namespace scope {
+
+constexpr int ATT_BM = 128;     // queries per attention work item (4 waves x 32)
+constexpr int SEL_NB = 2048;    // histogram bins per level in the selection kernels
+constexpr int SEL_CAP = 2048;   // boundary candidates sorted in LDS
+constexpr int MAX_C = 1024;     // largest Cq / Cm supported
+constexpr int MAX_N = 1 << 20;  // largest token count supported
+
+// Geometry of the four clusterings of a head: 0 = queries (full d),
+// 1..3 = key channel ranges T, H, W.
+struct Geo {
+  int BH, N, d, T, Hg, Wg;
+  int Cq, Cm, iters;
+  int off[4], dm[4], C[4], Cpad[4], dpad[4];
+  int Cmax, CmaxPad, DPmax;
+  int bf16;                     // 1: bf16 storage, 0: fp32
+  uint64_t seed;
+};
+
+// Per-cluster state of the selection kernels.
+struct ClusterSel {
+  double smax, smin, scale1;    // proxy-logit range and level-1 bin scale
+  double tau;                   // logit at the Top-p boundary
+  int32_t m;                    // keys with logit == tau that are taken (lowest indices)
+  int32_t t;                    // Top-p count t_c
+  int32_t all;                  // 1: every key selected
+  int32_t pad;
+  uint64_t zfx;                 // fixed-point softmax mass of all keys
+  double pad2;
+};
+
+struct Workspace {
+  double2* rope_tab;            // cos/sin per (range, position, pair)
+  int rope_off[3];
+  double* d2;                   // [BH][4][N] k-means++ squared distance to the nearest centre
+  int32_t* nearest;             // [BH][4][N] index of that centre (bit 30: point is a centre)
+  double* bsum;                 // [BH][4][ceil(N/64)] per-64-point sums of d2
+  int32_t* seeds;               // [BH][4][Cmax]
+  float* qcent;                 // [BH][Cq][d]
+  float* kcent;                 // [BH][Cm][d]
+  uint16_t* cbf;                // [BH][4][CmaxPad][DPmax] bf16 centroids, zero padded
+  float* cnorm;                 // [BH][4][CmaxPad] ||bf16 centroid||^2 (FLT_MAX on padding)
+  int32_t* labels;              // [BH][4][N]
+  int32_t* rlist;               // [BH][4][N] points whose assignment is refined in fp64
+  int32_t* rcnt;                // [iters+1][BH][4]
+  int32_t* perm;                // [BH][4][N] points sorted by label (stable)
+  int32_t* off;                 // [BH][4][Cmax+1] cluster offsets into perm
+  uint16_t* codes;              // [BH][N][4]
+  int32_t* qlab;                // [BH][N] (final query labels)
+  double* lut;                  // [BH][Cq][3][Cm]
+  ClusterSel* csel;             // [BH][Cq]
+  size_t bytes;
+};
+
+Geo make_geo(const scope_params& p);
+// Lays the workspace out from `base` (nullptr: only computes .bytes).
+Workspace carve(const Geo& g, const scope_plan_t* plan, char* base);
+
+// ---- launchers (return hipGetLastError()) ---------------------------------
+hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const void* k, void* qo,
+                       void* ko, const Workspace& w, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
+hipError_t launch_seed(const Geo& g, const void* qr, const void* kr, const Workspace& w, hipStream_t s);
+hipError_t launch_prep(const Geo& g, const Workspace& w, hipStream_t s);
+hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Workspace& w, int iter,
+                         hipStream_t s);
+hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Workspace& w, hipStream_t s);
+hipError_t launch_pack(const Geo& g, const Workspace& w, int32_t* q_labels_out, hipStream_t s);
+hipError_t launch_perm(const Geo& g, const Workspace& w, int32_t* perm_q, int32_t* q_off, hipStream_t s);
+hipError_t launch_lut(const Geo& g, const Workspace& w, hipStream_t s);
+hipError_t launch_topp(const Geo& g, const scope_params& p, const Workspace& w, int32_t* ct, int32_t* cb,
+                       hipStream_t s);
+hipError_t launch_khead(const Geo& g, const scope_plan_t& plan, hipStream_t s);
+hipError_t launch_final_select(const Geo& g, const scope_params& p, const Workspace& w,
+                               const scope_plan_t& plan, hipStream_t s);
+hipError_t launch_worklist(const Geo& g, const scope_plan_t& plan, hipStream_t s);
+hipError_t launch_attend(const Geo& g, const scope_plan_t& plan, const void* qr, const void* kr,
+                         const void* v, void* out, hipStream_t s);
+
+}  // namespace scope

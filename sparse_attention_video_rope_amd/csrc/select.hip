@@ -1,0 +1,628 @@
+// Stages 3-5 of SCOPE (arXiv 2608.12780; equations as quoted on the
+// pith.science review page):
+//   LUT      P^m[c][z] = <qbar_c on range m, mu^m_z>, m in {T, H, W}
+//   proxy    s[c][j] = (1/sqrt(d)) (P^T[c][zT_j] + P^H[c][zH_j] + P^W[c][zW_j])   (Eq. 6)
+//   Top-p    t_c = smallest t whose first t keys, ordered by (s desc, j asc),
+//            hold softmax mass >= rho                                          (Eq. 7)
+//   base     b_c = max(t_c, ceil(alpha N))                                     (Eq. 8)
+//   k_head   ceil(sum_c n_c b_c / sum_c n_c)                                   (Eq. 9)
+//   final    r_c = max(b_c, k_head) for non-empty clusters, 0 otherwise; S_c =
+//            the first r_c keys in the same order, stored ascending          (Eq. 10)
+//
+// Selection never materialises the Cq x N score matrix: one workgroup per
+// query cluster streams the packed key codes (8 B per key) and recomputes each
+// logit from the cluster's three LUT rows in LDS.  The boundary key is found
+// with two levels of 2048 linear bins over [s_min, s_max] carrying exact
+// counts and fixed-point softmax mass (integer adds, so the result does not
+// depend on the order of the LDS atomics), followed by an exact sort of the
+// boundary bin by (s desc, j asc).  The softmax weight of key j is
+// exp(s_j - s_max), formed as the product of three per-subspace factors
+// exp(P^m/sqrt(d) - A_m) and exp(sum_m A_m - s_max).
+#include <float.h>
+
+#include "scope_device.hpp"
+#include "scope_internal.hpp"
+
+namespace scope {
+
+// ---------------------------------------------------------------------------
+// Stage 3: lookup tables, fp64 dot products of fp32 centroids.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void lut_kernel(Geo g, const float* __restrict__ qcent,
+                                                  const float* __restrict__ kcent, double* __restrict__ lut) {
+  const int c = blockIdx.x, bh = blockIdx.y, d = g.d, Cm = g.Cm;
+  __shared__ double qs[128];
+  if (threadIdx.x < d) qs[threadIdx.x] = (double)qcent[((size_t)bh * g.Cq + c) * d + threadIdx.x];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 3 * Cm; idx += 256) {
+    const int mm = idx / Cm, z = idx % Cm, o = g.off[mm + 1], dmm = g.dm[mm + 1];
+    const float* kr = kcent + ((size_t)bh * Cm + z) * d + o;
+    double acc = 0.0;
+    for (int ch = 0; ch < dmm; ++ch) acc += qs[o + ch] * (double)kr[ch];
+    lut[(((size_t)bh * g.Cq + c) * 3 + mm) * Cm + z] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared machinery of the selection kernels
+// ---------------------------------------------------------------------------
+constexpr int NT = 256;
+constexpr int BPT = SEL_NB / NT;      // histogram bins per thread in a walk
+
+struct SelArgs {
+  int N, Cq, Cm;
+  double inv_sqrt_d;                  // 1/sqrt(d), rounded once
+  double rho;
+  double fx_scale;                    // 2^S: fixed-point scale of softmax weights
+  int floor_a;                        // ceil(alpha N)
+};
+
+struct Sel {
+  const double *P0, *P1, *P2;         // LUT rows of the cluster
+  const double *E0, *E1, *E2;         // exp(P^m/sqrt(d) - A_m)
+  double F;                           // exp(sum_m A_m - s_max)
+  double inv_sqrt_d, fx;
+  double smax, scale1;
+  const ushort4* codes;               // [N] packed (zT, zH, zW, 0)
+  int N;
+};
+
+__device__ __forceinline__ double logit(const Sel& S, ushort4 z) {
+  return ((S.P0[z.x] + S.P1[z.y]) + S.P2[z.z]) * S.inv_sqrt_d;
+}
+__device__ __forceinline__ uint64_t weight_fx(const Sel& S, ushort4 z) {
+  return (uint64_t)__double2ull_rn(((S.E0[z.x] * S.E1[z.y]) * S.E2[z.z]) * S.F * S.fx);
+}
+__device__ __forceinline__ double bin_x(const Sel& S, double s) { return (S.smax - s) * S.scale1; }
+__device__ __forceinline__ int bin1_of(double x) { return min(max((int)x, 0), SEL_NB - 1); }
+__device__ __forceinline__ int bin2_of(double x, int b1) {
+  return min(max((int)((x - (double)b1) * SEL_NB), 0), SEL_NB - 1);
+}
+
+struct SelSmem {
+  int32_t* hc;       // [SEL_NB] counts
+  uint64_t* hm;      // [SEL_NB] fixed-point mass
+  double* cs;        // [SEL_CAP] candidate logits
+  int32_t* cj;       // [SEL_CAP] candidate key indices
+  uint64_t* cw;      // [SEL_CAP] candidate weights
+  uint64_t* u64tmp;  // [NT/64 + 1]
+  int64_t* i64tmp;   // [NT/64 + 1]
+  double* dtmp;      // [NT/64]
+  int32_t* misc;     // [8]
+};
+
+// Walk a histogram: first bin whose inclusive running weight (mass or count,
+// starting at the given bases) reaches `tgt`.  Returns the bin and the
+// running mass / count before it.
+__device__ int hist_walk(const SelSmem& sm, bool by_mass, uint64_t tgt, uint64_t baseM, int64_t baseC,
+                         uint64_t* beforeM, int64_t* beforeC) {
+  const int tid = threadIdx.x;
+  uint64_t lm = 0;
+  int64_t lc = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) { lm += sm.hm[tid * BPT + i]; lc += sm.hc[tid * BPT + i]; }
+  uint64_t totM;
+  int64_t totC;
+  const uint64_t exM = block_incl_scan<uint64_t, NT>(lm, sm.u64tmp, &totM) - lm;
+  const int64_t exC = block_incl_scan<int64_t, NT>(lc, sm.i64tmp, &totC) - lc;
+  uint64_t cm = baseM + exM;
+  int64_t cc = baseC + exC;
+  if (tid == NT - 1) {
+    // default (target beyond the total): the last bin
+    sm.misc[0] = SEL_NB - 1;
+    sm.u64tmp[NT / 64] = baseM + totM - sm.hm[SEL_NB - 1];
+    sm.i64tmp[NT / 64] = baseC + totC - sm.hc[SEL_NB - 1];
+  }
+  __syncthreads();
+  const bool mine = by_mass ? (cm < tgt && cm + lm >= tgt) : ((uint64_t)cc < tgt && (uint64_t)(cc + lc) >= tgt);
+  if (mine) {
+    for (int i = 0; i < BPT; ++i) {
+      const int b = tid * BPT + i;
+      const uint64_t nm = cm + sm.hm[b];
+      const int64_t nc = cc + sm.hc[b];
+      if (by_mass ? nm >= tgt : (uint64_t)nc >= tgt) {
+        sm.misc[0] = b;
+        sm.u64tmp[NT / 64] = cm;   // slot past the scan's per-wave area
+        sm.i64tmp[NT / 64] = cc;
+        break;
+      }
+      cm = nm;
+      cc = nc;
+    }
+  }
+  __syncthreads();
+  const int b = sm.misc[0];
+  *beforeM = sm.u64tmp[NT / 64];
+  *beforeC = sm.i64tmp[NT / 64];
+  __syncthreads();
+  return b;
+}
+
+// Boundary of the first `tgt` weight (mass or count) in the (s desc, j asc)
+// order: the logit tau of the boundary key, how many keys with logit tau are
+// taken (the lowest-indexed ones), and the total number of keys taken.
+struct Boundary {
+  double tau;
+  int m;
+  int count;
+};
+
+__device__ Boundary find_boundary(const Sel& S, const SelSmem& sm, bool by_mass, uint64_t tgt) {
+  const int tid = threadIdx.x, N = S.N;
+  // ---- level 1 ------------------------------------------------------------
+  for (int b = tid; b < SEL_NB; b += NT) { sm.hc[b] = 0; sm.hm[b] = 0; }
+  __syncthreads();
+  for (int j = tid; j < N; j += NT) {
+    const ushort4 z = S.codes[j];
+    const int b1 = bin1_of(bin_x(S, logit(S, z)));
+    atomicAdd(&sm.hc[b1], 1);
+    if (by_mass) atomicAdd((unsigned long long*)&sm.hm[b1], (unsigned long long)weight_fx(S, z));
+  }
+  __syncthreads();
+  uint64_t bm;
+  int64_t bc;
+  const int B1 = hist_walk(sm, by_mass, tgt, 0, 0, &bm, &bc);
+  // ---- level 2 ------------------------------------------------------------
+  for (int b = tid; b < SEL_NB; b += NT) { sm.hc[b] = 0; sm.hm[b] = 0; }
+  __syncthreads();
+  for (int j = tid; j < N; j += NT) {
+    const ushort4 z = S.codes[j];
+    const double x = bin_x(S, logit(S, z));
+    if (bin1_of(x) != B1) continue;
+    const int b2 = bin2_of(x, B1);
+    atomicAdd(&sm.hc[b2], 1);
+    if (by_mass) atomicAdd((unsigned long long*)&sm.hm[b2], (unsigned long long)weight_fx(S, z));
+  }
+  __syncthreads();
+  const int B2 = hist_walk(sm, by_mass, tgt, bm, bc, &bm, &bc);
+  const int ncand = sm.hc[B2];
+  Boundary r;
+  if (ncand <= SEL_CAP) {
+    // ---- exact resolution: sort the boundary bin by (s desc, j asc) --------
+    if (tid == 0) sm.misc[1] = 0;
+    __syncthreads();
+    for (int j = tid; j < N; j += NT) {
+      const ushort4 z = S.codes[j];
+      const double s = logit(S, z);
+      const double x = bin_x(S, s);
+      if (bin1_of(x) != B1 || bin2_of(x, B1) != B2) continue;
+      const int k = atomicAdd(&sm.misc[1], 1);
+      sm.cs[k] = s;
+      sm.cj[k] = j;
+      sm.cw[k] = by_mass ? weight_fx(S, z) : 0;
+    }
+    __syncthreads();
+    int P2 = 1;
+    while (P2 < ncand) P2 <<= 1;
+    for (int k = ncand + tid; k < P2; k += NT) { sm.cs[k] = -__builtin_inf(); sm.cj[k] = 0x7FFFFFFF; sm.cw[k] = 0; }
+    __syncthreads();
+    for (int size = 2; size <= P2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < P2 / 2; i += NT) {
+          const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const double s0 = sm.cs[lo], s1 = sm.cs[hi];
+          const int j0 = sm.cj[lo], j1 = sm.cj[hi];
+          const bool hi_first = s1 > s0 || (s1 == s0 && j1 < j0);
+          if (hi_first == up) {
+            sm.cs[lo] = s1; sm.cs[hi] = s0;
+            sm.cj[lo] = j1; sm.cj[hi] = j0;
+            const uint64_t w0 = sm.cw[lo];
+            sm.cw[lo] = sm.cw[hi]; sm.cw[hi] = w0;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    int kb;
+    if (by_mass) {
+      // running mass over the sorted candidates; first position reaching tgt
+      constexpr int PER = SEL_CAP / NT;
+      uint64_t lw = 0;
+      for (int i = 0; i < PER; ++i) { const int k = tid * PER + i; if (k < ncand) lw += sm.cw[k]; }
+      uint64_t tot;
+      uint64_t run = bm + block_incl_scan<uint64_t, NT>(lw, sm.u64tmp, &tot) - lw;
+      if (tid == 0) sm.misc[2] = ncand - 1;
+      __syncthreads();
+      for (int i = 0; i < PER; ++i) {
+        const int k = tid * PER + i;
+        if (k >= ncand) break;
+        if (run < tgt && run + sm.cw[k] >= tgt) { sm.misc[2] = k; break; }
+        run += sm.cw[k];
+      }
+      __syncthreads();
+      kb = sm.misc[2];
+    } else {
+      kb = (int)((int64_t)tgt - bc - 1);
+    }
+    r.tau = sm.cs[kb];
+    int k0 = kb;
+    while (k0 > 0 && sm.cs[k0 - 1] == r.tau) --k0;
+    r.m = kb - k0 + 1;
+    r.count = (int)bc + kb + 1;
+    __syncthreads();
+  } else {
+    // ---- many keys in one fine bin (ties): walk its distinct logits --------
+    double hi = __builtin_inf();
+    for (;;) {
+      double mx = -__builtin_inf();
+      for (int j = tid; j < N; j += NT) {
+        const double s = logit(S, S.codes[j]);
+        const double x = bin_x(S, s);
+        if (bin1_of(x) == B1 && bin2_of(x, B1) == B2 && s < hi) mx = fmax(mx, s);
+      }
+      const double g = block_max<double, NT>(mx, sm.dtmp);
+      if (!(g > -__builtin_inf())) {
+        // no logit left below `hi` (only if the histogram walk was inconsistent):
+        // close at the previous group
+        r.tau = hi;
+        r.m = 0;
+        r.count = (int)bc;
+        break;
+      }
+      uint64_t gm = 0;
+      int64_t gc = 0;
+      for (int j = tid; j < N; j += NT) {
+        const ushort4 z = S.codes[j];
+        if (logit(S, z) == g) { ++gc; if (by_mass) gm += weight_fx(S, z); }
+      }
+      gc = block_sum<int64_t, NT>(gc, sm.i64tmp);
+      gm = block_sum<uint64_t, NT>(gm, sm.u64tmp);
+      const bool here = by_mass ? bm + gm >= tgt : (uint64_t)(bc + gc) >= tgt;
+      if (!here) { bm += gm; bc += gc; hi = g; continue; }
+      r.tau = g;
+      if (!by_mass) {
+        r.m = (int)((int64_t)tgt - bc);
+      } else {
+        // ordered walk over the keys with logit g, in index order
+        int64_t rank = 0;
+        uint64_t run = bm;
+        int found = -1;
+        for (int j0 = 0; j0 < N && found < 0; j0 += NT * 8) {
+          uint64_t lw = 0;
+          int64_t lc = 0;
+          for (int i = 0; i < 8; ++i) {
+            const int j = j0 + tid * 8 + i;
+            if (j < N) { const ushort4 z = S.codes[j]; if (logit(S, z) == g) { lw += weight_fx(S, z); ++lc; } }
+          }
+          uint64_t totw;
+          int64_t totc;
+          uint64_t ew = run + block_incl_scan<uint64_t, NT>(lw, sm.u64tmp, &totw) - lw;
+          int64_t ec = rank + block_incl_scan<int64_t, NT>(lc, sm.i64tmp, &totc) - lc;
+          if (tid == 0) sm.misc[3] = -1;
+          __syncthreads();
+          if (ew < tgt && ew + lw >= tgt) {
+            for (int i = 0; i < 8; ++i) {
+              const int j = j0 + tid * 8 + i;
+              const ushort4 z = S.codes[j];
+              if (logit(S, z) != g) continue;
+              ew += weight_fx(S, z);
+              ++ec;
+              if (ew >= tgt) { sm.misc[3] = (int)ec; break; }
+            }
+          }
+          __syncthreads();
+          found = sm.misc[3];
+          run += totw;
+          rank += totc;
+          __syncthreads();
+        }
+        r.m = found > 0 ? found : (int)gc;
+      }
+      r.count = (int)bc + r.m;
+      break;
+    }
+  }
+  return r;
+}
+
+// Loads the cluster's LUT rows (and, for mass selection, the exp factors)
+// and computes s_min / s_max over the N keys.
+__device__ void setup_cluster(Sel& S, const SelArgs& a, const double* lutrow, const ushort4* codes, double* Pl,
+                              double* El, bool with_mass, const SelSmem& sm) {
+  const int tid = threadIdx.x, Cm = a.Cm;
+  for (int i = tid; i < 3 * Cm; i += NT) Pl[i] = lutrow[i];
+  __syncthreads();
+  S.P0 = Pl; S.P1 = Pl + Cm; S.P2 = Pl + 2 * Cm;
+  S.codes = codes;
+  S.N = a.N;
+  S.inv_sqrt_d = a.inv_sqrt_d;
+  S.fx = a.fx_scale;
+  double smax = -__builtin_inf(), smin = __builtin_inf();
+  for (int j = tid; j < a.N; j += NT) {
+    const double s = logit(S, codes[j]);
+    smax = fmax(smax, s);
+    smin = fmin(smin, s);
+  }
+  S.smax = block_max<double, NT>(smax, sm.dtmp);
+  const double lo = block_min<double, NT>(smin, sm.dtmp);
+  S.scale1 = S.smax > lo ? (double)SEL_NB / (S.smax - lo) : 0.0;
+  if (with_mass) {
+    double A[3];
+    for (int mm = 0; mm < 3; ++mm) {
+      double mx = -__builtin_inf();
+      for (int z = tid; z < Cm; z += NT) mx = fmax(mx, Pl[mm * Cm + z] * a.inv_sqrt_d);
+      A[mm] = block_max<double, NT>(mx, sm.dtmp);
+    }
+    for (int i = tid; i < 3 * Cm; i += NT) El[i] = exp(Pl[i] * a.inv_sqrt_d - A[i / Cm]);
+    S.E0 = El; S.E1 = El + Cm; S.E2 = El + 2 * Cm;
+    S.F = exp(((A[0] + A[1]) + A[2]) - S.smax);
+    __syncthreads();
+  }
+}
+
+__device__ SelSmem carve_sel(unsigned char* base, int Cm, double** Pl, double** El) {
+  SelSmem sm;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { unsigned char* p = base + o; o += (bytes + 15) & ~(size_t)15; return p; };
+  *Pl = reinterpret_cast<double*>(take(sizeof(double) * 3 * Cm));
+  *El = reinterpret_cast<double*>(take(sizeof(double) * 3 * Cm));
+  sm.hc = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * SEL_NB));
+  sm.hm = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * SEL_NB));
+  sm.cs = reinterpret_cast<double*>(take(sizeof(double) * SEL_CAP));
+  sm.cj = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * SEL_CAP));
+  sm.cw = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * SEL_CAP));
+  sm.u64tmp = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (NT / 64 + 2)));
+  sm.i64tmp = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * (NT / 64 + 2)));
+  sm.dtmp = reinterpret_cast<double*>(take(sizeof(double) * (NT / 64 + 2)));
+  sm.misc = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 8));
+  return sm;
+}
+
+static size_t sel_smem_bytes(int Cm) {
+  auto r = [](size_t b) { return (b + 15) & ~(size_t)15; };
+  return 2 * r(sizeof(double) * 3 * Cm) + r(4 * SEL_NB) + r(8 * SEL_NB) + r(8 * SEL_CAP) + r(4 * SEL_CAP) +
+         r(8 * SEL_CAP) + 3 * r(8 * (NT / 64 + 2)) + r(32);
+}
+
+// ---------------------------------------------------------------------------
+// Stage 5a: Top-p count t_c and base count b_c per (cluster, head).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void topp_kernel(SelArgs a, const double* __restrict__ lut,
+                                                  const ushort4* __restrict__ codes, ClusterSel* __restrict__ csel,
+                                                  int32_t* __restrict__ ct, int32_t* __restrict__ cb) {
+  const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  double *Pl, *El;
+  const SelSmem sm = carve_sel(smem_raw, a.Cm, &Pl, &El);
+  Sel S;
+  const bool take_all = a.rho >= 1.0;
+  setup_cluster(S, a, lut + ((size_t)bh * a.Cq + c) * 3 * a.Cm, codes + (size_t)bh * a.N, Pl, El, !take_all, sm);
+  ClusterSel st;
+  st.smax = S.smax;
+  st.scale1 = S.scale1;
+  st.smin = 0.0;
+  st.pad = 0;
+  st.pad2 = 0.0;
+  int t;
+  if (take_all) {
+    t = a.N;
+    st.all = 1;
+    st.tau = -__builtin_inf();
+    st.m = 0;
+    st.zfx = 0;
+  } else {
+    uint64_t z = 0;
+    for (int j = tid; j < a.N; j += NT) z += weight_fx(S, S.codes[j]);
+    z = block_sum<uint64_t, NT>(z, sm.u64tmp);
+    uint64_t tgt = (uint64_t)ceil(a.rho * (double)z);
+    tgt = tgt > z ? z : (tgt < 1 ? 1 : tgt);
+    const Boundary b = find_boundary(S, sm, true, tgt);
+    t = b.count;
+    st.all = t >= a.N;
+    st.tau = b.tau;
+    st.m = b.m;
+    st.zfx = z;
+  }
+  st.t = t;
+  if (tid == 0) {
+    const size_t i = (size_t)bh * a.Cq + c;
+    csel[i] = st;
+    ct[i] = t;
+    cb[i] = max(t, a.floor_a);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 5b: k_head (Eq. 9), r_c (Eq. 10) and the CSR offsets; one workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void khead_kernel(int BH, int Cq, int N, const int32_t* __restrict__ q_off,
+                                                     const int32_t* __restrict__ cb, int32_t* __restrict__ cr,
+                                                     int32_t* __restrict__ khead, int64_t* __restrict__ sel_off,
+                                                     int64_t capacity, int32_t* __restrict__ status) {
+  __shared__ int64_t tmp[17];
+  const int tid = threadIdx.x;
+  int64_t base = 0;
+  for (int bh = 0; bh < BH; ++bh) {
+    int64_t num = 0, den = 0;
+    for (int c = tid; c < Cq; c += 1024) {
+      const int64_t n = q_off[(size_t)bh * (Cq + 1) + c + 1] - q_off[(size_t)bh * (Cq + 1) + c];
+      num += n * cb[(size_t)bh * Cq + c];
+      den += n;
+    }
+    num = block_sum<int64_t, 1024>(num, tmp);
+    den = block_sum<int64_t, 1024>(den, tmp);
+    const int64_t kh = den > 0 ? (num + den - 1) / den : 0;
+    if (tid == 0) khead[bh] = (int32_t)kh;
+    for (int c0 = 0; c0 < Cq; c0 += 1024) {
+      const int c = c0 + tid;
+      int64_t r = 0;
+      if (c < Cq) {
+        const int64_t n = q_off[(size_t)bh * (Cq + 1) + c + 1] - q_off[(size_t)bh * (Cq + 1) + c];
+        const int64_t b = cb[(size_t)bh * Cq + c];
+        r = n > 0 ? (b > kh ? b : kh) : 0;
+        if (r > N) r = N;
+        cr[(size_t)bh * Cq + c] = (int32_t)r;
+      }
+      int64_t tot;
+      const int64_t inc = block_incl_scan<int64_t, 1024>(r, tmp, &tot);
+      if (c < Cq) sel_off[(size_t)bh * Cq + c] = base + inc - r;
+      base += tot;
+    }
+  }
+  if (tid == 0) {
+    sel_off[(size_t)BH * Cq] = base;
+    status[1] = base > capacity ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 5c: S_c = first r_c keys in (s desc, j asc) order, written in
+// ascending index order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void final_select_kernel(SelArgs a, const double* __restrict__ lut,
+                                                          const ushort4* __restrict__ codes,
+                                                          const ClusterSel* __restrict__ csel,
+                                                          const int32_t* __restrict__ cr,
+                                                          const int64_t* __restrict__ sel_off,
+                                                          int32_t* __restrict__ sel_idx,
+                                                          const int32_t* __restrict__ status) {
+  const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const size_t ci = (size_t)bh * a.Cq + c;
+  const int r = cr[ci];
+  if (r == 0 || status[1]) return;
+  int32_t* out = sel_idx + sel_off[ci];
+  const ClusterSel st = csel[ci];
+  if (st.all || r >= a.N) {
+    for (int j = tid; j < a.N; j += NT) out[j] = j;
+    return;
+  }
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  double *Pl, *El;
+  const SelSmem sm = carve_sel(smem_raw, a.Cm, &Pl, &El);
+  const int Cm = a.Cm;
+  for (int i = tid; i < 3 * Cm; i += NT) Pl[i] = lut[ci * 3 * Cm + i];
+  __syncthreads();
+  Sel S;
+  S.P0 = Pl; S.P1 = Pl + Cm; S.P2 = Pl + 2 * Cm;
+  S.codes = codes + (size_t)bh * a.N;
+  S.N = a.N;
+  S.inv_sqrt_d = a.inv_sqrt_d;
+  S.fx = a.fx_scale;
+  S.smax = st.smax;
+  S.scale1 = st.scale1;
+  double tau;
+  int m;
+  if (r == st.t) {
+    tau = st.tau;
+    m = st.m;
+  } else {
+    const Boundary b = find_boundary(S, sm, false, (uint64_t)r);
+    tau = b.tau;
+    m = b.m;
+  }
+  // ordered compaction: each thread owns 16 consecutive keys of a 4096-key chunk
+  constexpr int KPT = 16;
+  int64_t selBase = 0, tieBase = 0;
+  for (int j0 = 0; j0 < a.N; j0 += NT * KPT) {
+    uint32_t gt = 0, eq = 0;
+    for (int i = 0; i < KPT; ++i) {
+      const int j = j0 + tid * KPT + i;
+      if (j < a.N) {
+        const double s = logit(S, S.codes[j]);
+        gt |= (uint32_t)(s > tau) << i;
+        eq |= (uint32_t)(s == tau) << i;
+      }
+    }
+    const int ngt = __popc(gt), neq = __popc(eq);
+    int64_t totTie;
+    const int64_t exTie = tieBase + block_incl_scan<int64_t, NT>(neq, sm.i64tmp, &totTie) - neq;
+    int64_t take = (int64_t)m - exTie;
+    take = take < 0 ? 0 : (take > neq ? neq : take);
+    const int64_t nsel = ngt + take;
+    int64_t totSel;
+    int64_t pos = selBase + block_incl_scan<int64_t, NT>(nsel, sm.i64tmp, &totSel) - nsel;
+    int64_t tr = exTie;
+    for (int i = 0; i < KPT; ++i) {
+      const int j = j0 + tid * KPT + i;
+      const bool take1 = ((gt >> i) & 1u) || (((eq >> i) & 1u) && tr++ < m);
+      if (take1) { if (pos < r) out[pos] = j; ++pos; }
+    }
+    selBase += totSel;
+    tieBase += totTie;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention work list: one item per (cluster, 128-query chunk), cluster-major
+// in (head, cluster) order; one workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void worklist_kernel(int BH, int Cq, const int32_t* __restrict__ q_off,
+                                                        const int32_t* __restrict__ cr, int32_t* __restrict__ work,
+                                                        int64_t cap, int32_t* __restrict__ status) {
+  __shared__ int64_t tmp[17];
+  const int tid = threadIdx.x;
+  const int64_t total = (int64_t)BH * Cq;
+  int64_t base = 0;
+  for (int64_t i0 = 0; i0 < total; i0 += 1024) {
+    const int64_t i = i0 + tid;
+    int64_t items = 0;
+    if (i < total) {
+      const int bh = (int)(i / Cq), c = (int)(i % Cq);
+      const int n = q_off[(size_t)bh * (Cq + 1) + c + 1] - q_off[(size_t)bh * (Cq + 1) + c];
+      items = (cr[i] > 0 && n > 0) ? (n + ATT_BM - 1) / ATT_BM : 0;
+    }
+    int64_t tot;
+    int64_t pos = base + block_incl_scan<int64_t, 1024>(items, tmp, &tot) - items;
+    for (int64_t k = 0; k < items && pos + k < cap; ++k) {
+      work[2 * (pos + k)] = (int32_t)i;
+      work[2 * (pos + k) + 1] = (int32_t)k;
+    }
+    base += tot;
+  }
+  if (tid == 0) status[0] = (int32_t)(base < cap ? base : cap);
+}
+
+// ---- launchers ----------------------------------------------------------------
+
+static SelArgs sel_args(const Geo& g, const scope_params& p) {
+  SelArgs a;
+  a.N = g.N; a.Cq = g.Cq; a.Cm = g.Cm;
+  a.inv_sqrt_d = 1.0 / sqrt((double)g.d);
+  a.rho = p.rho;
+  int lg = 0;
+  while ((1ll << lg) < (int64_t)g.N + 1) ++lg;
+  a.fx_scale = ldexp(1.0, 62 - lg);
+  a.floor_a = (int)ceil(p.alpha * (double)g.N);
+  return a;
+}
+
+static void allow_big_lds(const void* fn, size_t bytes) {
+  if (bytes > 64 * 1024) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+hipError_t launch_lut(const Geo& g, const Workspace& w, hipStream_t s) {
+  lut_kernel<<<dim3(g.Cq, g.BH), 256, 0, s>>>(g, w.qcent, w.kcent, w.lut);
+  return hipGetLastError();
+}
+
+hipError_t launch_topp(const Geo& g, const scope_params& p, const Workspace& w, int32_t* ct, int32_t* cb,
+                       hipStream_t s) {
+  const size_t lds = sel_smem_bytes(g.Cm);
+  allow_big_lds((const void*)topp_kernel, lds);
+  topp_kernel<<<dim3(g.Cq, g.BH), NT, lds, s>>>(sel_args(g, p), w.lut, (const ushort4*)w.codes, w.csel, ct, cb);
+  return hipGetLastError();
+}
+
+hipError_t launch_khead(const Geo& g, const scope_plan_t& plan, hipStream_t s) {
+  khead_kernel<<<1, 1024, 0, s>>>(g.BH, g.Cq, g.N, plan.q_off, plan.counts_b, plan.counts_r, plan.k_head,
+                                  plan.sel_off, plan.sel_capacity, plan.status);
+  return hipGetLastError();
+}
+
+hipError_t launch_final_select(const Geo& g, const scope_params& p, const Workspace& w,
+                               const scope_plan_t& plan, hipStream_t s) {
+  const size_t lds = sel_smem_bytes(g.Cm);
+  allow_big_lds((const void*)final_select_kernel, lds);
+  final_select_kernel<<<dim3(g.Cq, g.BH), NT, lds, s>>>(sel_args(g, p), w.lut, (const ushort4*)w.codes, w.csel,
+                                                        plan.counts_r, plan.sel_off, plan.sel_idx, plan.status);
+  return hipGetLastError();
+}
+
+hipError_t launch_worklist(const Geo& g, const scope_plan_t& plan, hipStream_t s) {
+  worklist_kernel<<<1, 1024, 0, s>>>(g.BH, g.Cq, plan.q_off, plan.counts_r, plan.work, plan.work_capacity,
+                                      plan.status);
+  return hipGetLastError();
+}
+
+}  // namespace scope

@@ -1,0 +1,106 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry
+point, and rejects bad parameters before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_video_rope_amd as sav
+from sparse_attention_video_rope_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "scope.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(scope_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sav.load()
+    names = declared_symbols()
+    assert names == ["scope_attend", "scope_plan", "scope_plan_finalize", "scope_status_string",
+                     "scope_workspace_size"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_header():
+    # 12 int32, 3 double, uint64, int32, uint32 -> 88 bytes; plan: 18 pointer-sized fields
+    assert ctypes.sizeof(_lib.Params) == 88
+    assert ctypes.sizeof(_lib.PlanStruct) == 18 * 8
+
+
+def test_status_strings():
+    lib = sav.load()
+    assert lib.scope_status_string(0) == b"ok"
+    assert lib.scope_status_string(3) == b"workspace too small"
+    assert lib.scope_status_string(99) == b"unknown status"
+
+
+def good(**kw):
+    args = dict(B=1, H=2, T=4, Hg=8, Wg=8, d=64, split=(16, 24, 24), Cq=8, Cm=8)
+    args.update(kw)
+    return sav.make_params(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(split=(16, 24, 22)), 1),            # split does not sum to d
+    (dict(split=(15, 25, 24)), 1),            # odd range
+    (dict(d=96, split=(32, 32, 32)), 2),      # unsupported head dim
+    (dict(Cq=0), 1), (dict(Cm=257), 1),       # Cm > N
+    (dict(Cq=300, T=8, Hg=16, Wg=16, Cm=2000), 2),   # beyond the supported cluster count
+    (dict(rho=0.0), 1), (dict(rho=1.5), 1), (dict(alpha=-0.1), 1),
+    (dict(iters=-1), 1), (dict(rope_base=1.0), 1),
+])
+def test_invalid_parameters(kw, code):
+    p = good(**kw)
+    st = sav.load().scope_workspace_size(ctypes.byref(p), None, None, None)
+    assert st == code
+
+
+def test_workspace_size_and_capacities():
+    p = good()
+    ws, sel, work = sav.sizes(p)
+    assert ws > 0 and sel == 2 * 8 * 256 and work == 2 * (8 + 2)
+    # monotone in the token count
+    ws2, _, _ = sav.sizes(good(T=8))
+    assert ws2 > ws
+
+
+def test_plan_rejects_null_pointers_before_launch():
+    lib = sav.load()
+    p = good()
+    plan = _lib.PlanStruct()
+    st = lib.scope_plan(ctypes.byref(p), None, None, None, None, ctypes.byref(plan), None, 0, None)
+    assert st == 1
+    st = lib.scope_attend(ctypes.byref(p), ctypes.byref(plan), None, None, None, None, None)
+    assert st == 1
+    st = lib.scope_plan_finalize(ctypes.byref(p), None, None)
+    assert st == 1
+
+
+def test_plan_rejects_misaligned_and_small_workspace():
+    lib = sav.load()
+    p = good()
+    plan = _lib.PlanStruct()
+    fake = 1 << 20                     # never dereferenced: validation fails first
+    for name in ("perm_q", "q_off", "counts_t", "counts_b", "counts_r", "k_head", "sel_off", "sel_idx", "work",
+                 "status"):
+        setattr(plan, name, fake)
+    _, _, work = sav.sizes(p)
+    plan.work_capacity = work
+    plan.sel_capacity = 10
+    st = lib.scope_plan(ctypes.byref(p), fake + 2, fake, fake, fake, ctypes.byref(plan), fake, 1 << 40, None)
+    assert st == 1                      # q misaligned
+    st = lib.scope_plan(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(plan), fake, 16, None)
+    assert st == 3                      # workspace too small
+    plan.work_capacity = work - 1
+    st = lib.scope_plan(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(plan), fake, 1 << 40, None)
+    assert st == 4                      # work list too small
+    p.flags = _lib.SCOPE_USE_INIT_CENTROIDS
+    plan.work_capacity = work
+    st = lib.scope_plan(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(plan), fake, 1 << 40, None)
+    assert st == 1                      # init centroids requested but not given

@@ -1,0 +1,175 @@
+"""GPU parity of every stage against the oracle, at sizes the oracle finishes in
+seconds.  The shapes span several tiles of each kernel with ragged tails
+(128-query attention chunks, 64-key gather chunks, 32-centroid MFMA blocks,
+256-point assignment tiles)."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_video_rope_amd as sav
+import workloads
+from oracle import scope_oracle as O
+from tests.scope_gpu import (assert_attention, assert_rope, gpu_sel, labels_match_or_near_tie, run_gpu, say, to_dev,
+                             to_np)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    workloads.small("s64", 5, 9, 11, 64, (16, 24, 24), "bf16", 3, 40, index=101),
+    workloads.small("s128", 4, 10, 13, 128, (44, 42, 42), "bf16", 4, 37, index=102),
+    workloads.small("s128h", 3, 11, 17, 128, (16, 56, 56), "bf16", 5, 33, index=103),
+    workloads.small("s64f", 3, 6, 7, 64, (16, 24, 24), "f32", 4, 9, index=104),
+    workloads.small("s128f", 2, 5, 9, 128, (44, 42, 42), "f32", 3, 7, index=105, H=1),
+]
+IDS = [w.name for w in SMALL]
+
+_cache = {}
+
+
+def oracle_heads(w, rho=None, **kw):
+    key = (w, rho, tuple(sorted(kw.items())))
+    if key not in _cache:
+        q, k, v = workloads.generate(w)
+        _cache[key] = [O.workload_head(w, bh, q[bh], k[bh], v[bh], rho=rho, **kw) for bh in range(w.BH)]
+    return _cache[key]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sav.load()
+
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_rope_matches_oracle(w):
+    say("rope", w.name)
+    g = run_gpu(w)
+    for bh, o in enumerate(oracle_heads(w)):
+        n = assert_rope(g["q_rope"][bh], o["q_rope"], w.dtype) + assert_rope(g["k_rope"][bh], o["k_rope"], w.dtype)
+        say(f"  head {bh}: {n} RoPE elements differ (within 1 ulp)")
+
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_kmeanspp_seeds_match_oracle(w):
+    say("seeds", w.name)
+    g = run_gpu(w)
+    for bh, o in enumerate(oracle_heads(w)):
+        assert g["seeds"][bh, 0, :w.Cq].tolist() == list(o["q_seeds"])
+        for m in range(3):
+            assert g["seeds"][bh, 1 + m, :w.Cm].tolist() == list(o["k_seeds"][m]), f"head {bh} subspace {m}"
+
+
+@pytest.mark.parametrize("iters", [0, 1, 3])
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_lloyd_teacher_forced(w, iters):
+    """Same initial centroids on both sides: assignments and centroids after `iters` rounds."""
+    say("lloyd", w.name, iters)
+    q, k, v = workloads.generate(w)
+    wi = w.with_(iters=iters)
+    init_q, init_k = [], []
+    for bh, o in enumerate(oracle_heads(w)):
+        init_q.append(o["q_rope"][o["q_seeds"]])
+        kc = np.zeros((w.Cm, w.d))
+        offs = O.subspace_offsets(w.split)
+        for m, (off, dm) in enumerate(zip(offs, w.split)):
+            kc[:, off:off + dm] = o["k_rope"][o["k_seeds"][m], off:off + dm]
+        init_k.append(kc)
+    g = run_gpu(wi, init_q=np.stack(init_q), init_k=np.stack(init_k), inputs=(q, k, v))
+    offs = O.subspace_offsets(w.split)
+    for bh, o in enumerate(oracle_heads(w)):
+        qr, kr = o["q_rope"], o["k_rope"]
+        ref = O.kmeans(qr, w.Cq, iters, w.dtype, 0, bh, 0, init=init_q[bh])
+        np.testing.assert_allclose(g["q_centroids"][bh], ref["centroids"], rtol=1e-6, atol=0)
+        n_bad = labels_match_or_near_tie(g["q_labels"][bh], ref["labels"], qr, ref["centroids"], w.dtype)
+        for m, (off, dm) in enumerate(zip(offs, w.split)):
+            X = kr[:, off:off + dm]
+            refk = O.kmeans(X, w.Cm, iters, w.dtype, 0, bh, 1 + m, init=init_k[bh][:, off:off + dm])
+            np.testing.assert_allclose(g["k_centroids"][bh][:, off:off + dm], refk["centroids"], rtol=1e-6, atol=0)
+            n_bad += labels_match_or_near_tie(g["k_codes"][bh][:, m], refk["labels"], X, refk["centroids"], w.dtype)
+        say(f"  head {bh}: {n_bad} near-tie label differences")
+
+
+def upload_oracle_plan(w, heads, pl):
+    """Writes the oracle's clustering and key sets into a plan's buffers."""
+    BH, N, Cq = w.BH, w.N, w.Cq
+    perm = np.concatenate([h["perm_q"] for h in heads]).astype(np.int32)
+    qoff = np.concatenate([h["q_off"] for h in heads]).astype(np.int32)
+    t = np.concatenate([h["t"] for h in heads]).astype(np.int32)
+    b = np.concatenate([h["b"] for h in heads]).astype(np.int32)
+    r = np.concatenate([h["r"] for h in heads]).astype(np.int32)
+    kh = np.array([h["k_head"] for h in heads], dtype=np.int32)
+    sels = [s for h in heads for s in h["sel"]]
+    off = np.concatenate([[0], np.cumsum([len(s) for s in sels])]).astype(np.int64)
+    idx = np.concatenate(sels).astype(np.int32) if off[-1] else np.zeros(1, np.int32)
+    for name, arr in (("perm_q", perm), ("q_off", qoff), ("counts_t", t), ("counts_b", b), ("counts_r", r),
+                      ("k_head", kh), ("sel_off", off)):
+        getattr(pl, name).copy_(torch.from_numpy(arr).cuda())
+    pl.sel_idx[:len(idx)].copy_(torch.from_numpy(idx).cuda())
+    pl.status.zero_()
+
+
+@pytest.mark.parametrize("rho", [0.9, 1.0, 0.3])
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_attend_on_oracle_plan(w, rho):
+    say("attend", w.name, rho)
+    heads = oracle_heads(w, rho=rho)
+    q, k, v = workloads.generate(w)
+    p = sav.params_for(w, rho=rho)
+    pl = sav.Plan(p, debug=False)
+    upload_oracle_plan(w, heads, pl)
+    sav.plan_finalize(p, pl)
+    qr = to_dev(np.stack([h["q_rope"] for h in heads]), w.dtype)
+    kr = to_dev(np.stack([h["k_rope"] for h in heads]), w.dtype)
+    out = to_np(sav.attend(p, pl, qr, kr, to_dev(v, w.dtype))).reshape(w.BH, w.N, w.d)
+    for bh, h in enumerate(heads):
+        mx, mn = assert_attention(out[bh], h["out"], w.dtype, f"{w.name} head {bh}")
+        say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
+
+
+def assert_plan_equal(w, g, heads):
+    """End-to-end plan equality (exact) on every head."""
+    for bh, o in enumerate(heads):
+        assert g["q_labels"][bh].tolist() == o["q_labels"].tolist(), f"head {bh} query labels"
+        assert np.array_equal(g["k_codes"][bh], o["k_codes"]), f"head {bh} key codes"
+        np.testing.assert_array_equal(g["q_centroids"][bh], o["q_centroids"])
+        np.testing.assert_array_equal(g["k_centroids"][bh], o["k_centroids"])
+        np.testing.assert_allclose(g["lut"][bh], np.transpose(o["lut"], (1, 0, 2)), rtol=1e-12, atol=1e-12)
+        assert g["perm_q"][bh].tolist() == o["perm_q"].tolist()
+        assert g["q_off"][bh].tolist() == o["q_off"].tolist()
+        assert g["t"][bh].tolist() == o["t"].tolist(), f"head {bh} t_c"
+        assert g["b"][bh].tolist() == o["b"].tolist()
+        assert int(g["k_head"][bh]) == o["k_head"]
+        assert g["r"][bh].tolist() == o["r"].tolist()
+        for c, (gs, os_) in enumerate(zip(gpu_sel(g, bh, w.Cq), o["sel"])):
+            assert np.array_equal(gs, os_), f"head {bh} cluster {c}: |S| {len(gs)} vs {len(os_)}"
+
+
+@pytest.mark.parametrize("rho", [0.9, 0.5])
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_end_to_end_matches_oracle(w, rho):
+    say("e2e", w.name, rho)
+    heads = oracle_heads(w, rho=rho)
+    g = run_gpu(w, rho=rho)
+    assert g["status"][1] == 0
+    assert_plan_equal(w, g, heads)
+    for bh, o in enumerate(heads):
+        mx, mn = assert_attention(g["out"][bh], o["out"], w.dtype, f"{w.name} head {bh}")
+        say(f"  head {bh}: max {mx:.2e} mean {mn:.2e} density {np.sum(o['n'] * o['r']) / w.N**2:.3f}")
+
+
+def test_tiny_config_end_to_end():
+    w = workloads.CONFIGS["tiny"]
+    say("tiny")
+    heads = oracle_heads(w)
+    g = run_gpu(w)
+    assert_plan_equal(w, g, heads)
+    for bh, o in enumerate(heads):
+        assert_attention(g["out"][bh], o["out"], w.dtype, f"tiny head {bh}")
+
+
+def test_alpha_floor_end_to_end():
+    w = SMALL[0].with_(alpha=0.4)
+    heads = oracle_heads(w)
+    g = run_gpu(w)
+    assert_plan_equal(w, g, heads)
