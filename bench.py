@@ -1,0 +1,167 @@
+"""Benchmark of the SCOPE hot path (plan + attend) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config cogvideox] [--rho 0.9]
+
+One step = scope_plan (3D RoPE, k-means++ and Lloyd on queries and the three
+key subspaces, LUT, proxy scoring, hybrid Top-p / k_head selection) plus
+scope_attend (gathered exact attention), on every head of one batch of
+synthetic inputs resident in HBM.  Prints one JSON line.
+
+  value      effective TFLOP/s on selected keys over the whole step:
+             4 d sum_c n_c r_c / (t_plan + t_attend)
+  roofline   the attention kernel (bf16 MFMA): its algorithmic flops per
+             launch / its average launch time, HIP events on its stream
+  cpu_baseline  the CPU oracle on one head of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="cogvideox")
+    ap.add_argument("--rho", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attend_traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters (used if present and current)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, rho):
+    """The oracle as it stands on one head of the workload (the same inputs)."""
+    import workloads
+    from oracle import scope_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    q, k, v = workloads.generate(w, [0])
+    t0 = time.perf_counter()
+    r = O.workload_head(w, 0, q[0], k[0], v[0], rho=rho)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.d * float(np.sum(r["n"] * r["r"]))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"head 0 of {w.BH} ({w.name}), full pipeline, {dt:.1f} s; effective TFLOP/s "
+                      f"on that head's selected keys",
+            "seconds": dt, "host_cpus": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (heads shard across GPUs, "
+                                   "see the design notes)"}))
+        sys.exit(2)
+    import torch
+    import sparse_attention_video_rope_amd as sav
+    import workloads
+
+    w = workloads.CONFIGS[a.config]
+    rho = w.rho if a.rho is None else a.rho
+    p = sav.params_for(w, rho=rho)
+    q, k, v = workloads.generate(w)
+    dev = torch.device("cuda:0")
+    to = lambda x: torch.from_numpy(x.reshape(-1)).to(torch.bfloat16 if w.dtype == "bf16" else torch.float32).to(dev)
+    qd, kd, vd = to(q), to(k), to(v)
+    del q, k, v
+    pl = sav.Plan(p, device=dev, debug=False)
+    qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+    out = torch.empty_like(vd)
+
+    def step():
+        sav.plan(p, qd, kd, pl, qr, kr)
+        sav.attend(p, pl, qr, kr, vd, out)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for e0, e1, e2 in ev:
+        e0.record()
+        sav.plan(p, qd, kd, pl, qr, kr)
+        e1.record()
+        sav.attend(p, pl, qr, kr, vd, out)
+        e2.record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / a.steps
+    plan_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    att_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+
+    n = (pl.q_off.view(w.BH, w.Cq + 1)[:, 1:] - pl.q_off.view(w.BH, w.Cq + 1)[:, :-1]).double()
+    r = pl.counts_r.view(w.BH, w.Cq).double()
+    pairs = float((n * r).sum())
+    flops = 4.0 * w.d * pairs
+    density = pairs / (w.BH * float(w.N) ** 2)
+    kh = pl.k_head.cpu().numpy()
+    status = pl.status.cpu().numpy()
+    assert status[1] == 0, "selected-key capacity overflow"
+
+    traffic = None
+    if os.path.exists(a.traffic_json):
+        try:
+            t = json.load(open(a.traffic_json))
+            if t.get("workload") == w.name and abs(t.get("rho", -1) - rho) < 1e-12 and \
+                    t.get("kernel_source_sha") == _attend_sha():
+                traffic = t.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    achieved = flops / (att_ms * 1e-3) / 1e12
+    line = {
+        "metric": "SCOPE attention layer latency (ms) + effective TFLOP/s on selected keys, 1 GPU",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded smooth-field Q/K + noise, V ~ N(0,1))",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "tokens": w.N,
+                   "grid": [w.T, w.Hg, w.Wg], "head_dim": w.d, "rope_split": list(w.split), "Cq": w.Cq,
+                   "Cm": w.Cm, "lloyd_iters": w.iters, "rho": rho, "alpha": w.alpha},
+        "latency_ms": {"step": round(ms, 4), "plan": round(plan_ms, 4), "attend": round(att_ms, 4)},
+        "attend_tflops": round(achieved, 2),
+        "density": round(density, 4),
+        "k_head": {"min": int(kh.min()), "mean": float(kh.mean()), "max": int(kh.max())},
+        "roofline": {"kernel": "attend_bf16_kernel" if w.dtype == "bf16" else "attend_f32_kernel",
+                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "wall_s": round(wall, 3),
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, rho)
+    print(json.dumps(line), flush=True)
+
+
+def _attend_sha():
+    import hashlib
+    src = os.path.join(ROOT, "sparse_attention_video_rope_amd", "csrc", "attend.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()
