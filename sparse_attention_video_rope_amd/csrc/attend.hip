@@ -19,6 +19,8 @@ namespace scope {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 struct AttArgs {
   int N, Cq;
@@ -41,8 +43,9 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a, const int32
   constexpr int BN = 64;                 // keys per chunk
   constexpr int KLD = D + 8;             // K tile row stride (elements)
   constexpr int VLD = BN + 4;            // V^T tile row stride (elements, 8-byte aligned rows)
-  constexpr int PIECES = BN * D / 8;     // 16-byte pieces per tile
-  constexpr int PPT = PIECES / 256;      // pieces per thread
+  constexpr int KPT = BN * D / 8 / 256;  // K 16-byte pieces per thread
+  constexpr int VPT = (BN / 2) * (D / 8) / 256;   // V key-pair pieces per thread
+  constexpr float RESCALE_LOG2 = 8.f;    // lazy rescale: p stays below 2^8
   __shared__ __align__(16) uint16_t Ks[2][BN * KLD];
   __shared__ __align__(16) uint16_t Vt[2][D * VLD];
 
@@ -76,37 +79,53 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a, const int32
   f32x16_t o[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) o[t] = f32x16_t{};
-  float mrun = -FLT_MAX, lsum = 0.f;
+  float mref = -__builtin_inff(), lsum = 0.f;   // running max (raw logit units) used for the exponent
+  const float cs = a.scale_log2;
 
   const int nchunks = (r + BN - 1) / BN;
   // key indices come from the plan; clamp so a malformed plan cannot read out of bounds
   auto key_at = [&](int i) -> size_t { const int j = keys[i]; return (size_t)min(max(j, 0), a.N - 1); };
-  uint4 kbuf[PPT], vbuf[PPT];
+  uint4 kbuf[KPT], vb0[VPT], vb1[VPT];
   auto gather = [&](int kc) {
     const int nk = min(BN, r - kc * BN);
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      // K: 16 lanes per row (row-major tile); V: one lane per row, so the
-      // transposed LDS writes of a wave hit consecutive addresses
+    for (int i = 0; i < KPT; ++i) {
       const int piece = tid + i * 256;
-      const int krow = piece / (D / 8), kc8 = piece % (D / 8);
-      const int vrow = piece % BN, vc8 = piece / BN;
-      kbuf[i] = krow < nk ? *reinterpret_cast<const uint4*>(kr + (hb + key_at(kc * BN + krow)) * D + kc8 * 8)
-                          : make_uint4(0, 0, 0, 0);
-      vbuf[i] = vrow < nk ? *reinterpret_cast<const uint4*>(vv + (hb + key_at(kc * BN + vrow)) * D + vc8 * 8)
-                          : make_uint4(0, 0, 0, 0);
+      const int row = piece / (D / 8), c8 = piece % (D / 8);
+      kbuf[i] = row < nk ? *reinterpret_cast<const uint4*>(kr + (hb + key_at(kc * BN + row)) * D + c8 * 8)
+                         : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      // V: one thread per (key pair, channel octet); the pair becomes 8 packed dwords of V^T
+      const int piece = tid + i * 256;
+      const int kp = piece % (BN / 2), oc = piece / (BN / 2);
+      const int r0 = 2 * kp;
+      vb0[i] = r0 < nk ? *reinterpret_cast<const uint4*>(vv + (hb + key_at(kc * BN + r0)) * D + oc * 8)
+                       : make_uint4(0, 0, 0, 0);
+      vb1[i] = r0 + 1 < nk ? *reinterpret_cast<const uint4*>(vv + (hb + key_at(kc * BN + r0 + 1)) * D + oc * 8)
+                           : make_uint4(0, 0, 0, 0);
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
+    for (int i = 0; i < KPT; ++i) {
       const int piece = tid + i * 256;
-      const int krow = piece / (D / 8), kc8 = piece % (D / 8);
-      const int vrow = piece % BN, vc8 = piece / BN;
-      *reinterpret_cast<uint4*>(&Ks[buf][krow * KLD + kc8 * 8]) = kbuf[i];
-      const uint16_t* e = reinterpret_cast<const uint16_t*>(&vbuf[i]);
+      const int row = piece / (D / 8), c8 = piece % (D / 8);
+      *reinterpret_cast<uint4*>(&Ks[buf][row * KLD + c8 * 8]) = kbuf[i];
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) Vt[buf][(vc8 * 8 + j) * VLD + vrow] = e[j];
+    for (int i = 0; i < VPT; ++i) {
+      const int piece = tid + i * 256;
+      const int kp = piece % (BN / 2), oc = piece / (BN / 2);
+      const uint32_t w0[4] = {vb0[i].x, vb0[i].y, vb0[i].z, vb0[i].w};
+      const uint32_t w1[4] = {vb1[i].x, vb1[i].y, vb1[i].z, vb1[i].w};
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&Vt[buf][(oc * 8) * VLD + 2 * kp]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dst[(2 * j) * (VLD / 2)] = __builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u);      // channel 2j
+        dst[(2 * j + 1) * (VLD / 2)] = __builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u);  // channel 2j+1
+      }
     }
   };
 
@@ -119,57 +138,63 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a, const int32
       f32x16_t s[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        s[st] = f32x16_t{};
         const uint16_t* arow = &Ks[buf][(st * 32 + col) * KLD + hi * 8];
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(arow), qb[0],
+                                                        f32x16_t{}, 0, 0, 0);
 #pragma unroll
-        for (int kb = 0; kb < D / 16; ++kb) {
+        for (int kb = 1; kb < D / 16; ++kb) {
           const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(arow + kb * 16);
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[kb], s[st], 0, 0, 0);
         }
       }
       const int kleft = r - kc * BN;
-      float mloc = -FLT_MAX;
+      if (kleft < BN) {
+        // partial last chunk: keys past the end get -inf
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = st * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-          const float x = key < kleft ? s[st][v] * a.scale_log2 : -FLT_MAX;
-          s[st][v] = x;
-          mloc = fmaxf(mloc, x);
-        }
+          for (int v = 0; v < 16; ++v)
+            if (st * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kleft) s[st][v] = -__builtin_inff();
       }
+      float mloc = -__builtin_inff();
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) mloc = fmaxf(mloc, fmaxf(s[st][v], s[st][v + 1]));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float mnew = fmaxf(mrun, mloc);
-      if (mnew > mrun) {
-        const float alpha = exp2f(mrun - mnew);
+      // lazy rescale: move the reference max only when the new max exceeds it by 2^8
+      const bool grow = (mloc - mref) * cs > RESCALE_LOG2;
+      if (__ballot(grow)) {
+        const float mnew = grow ? mloc : mref;
+        const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * cs);
         lsum *= alpha;
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
 #pragma unroll
           for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
-        mrun = mnew;
+        mref = mnew;
       }
+      const float mc = mref * cs;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          uint16_t pb[8];
+          bf16x2_t pk[4];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float x = s[st][half * 8 + i];
-            const float p = x == -FLT_MAX ? 0.f : exp2f(x - mrun);
-            pb[i] = f32_to_bf16(p);
-            lsum += bf16_to_f32(pb[i]);   // normalise by what the MFMA multiplies
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][half * 8 + 2 * i], cs, -mc));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][half * 8 + 2 * i + 1], cs, -mc));
+            lsum += p0 + p1;
+            pk[i] = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
           }
-          const bf16x8_t bp = *reinterpret_cast<bf16x8_t*>(pb);
+          const bf16x8_t bp = *reinterpret_cast<bf16x8_t*>(pk);
           const int base = st * 32 + half * 16 + 4 * hi;
 #pragma unroll
           for (int t = 0; t < D / 32; ++t) {
             const uint16_t* vrow = &Vt[buf][(t * 32 + col) * VLD + base];
-            uint16_t av[8];
-            *reinterpret_cast<uint2*>(av) = *reinterpret_cast<const uint2*>(vrow);
-            *reinterpret_cast<uint2*>(av + 4) = *reinterpret_cast<const uint2*>(vrow + 8);
+            uint2 av[2];
+            av[0] = *reinterpret_cast<const uint2*>(vrow);
+            av[1] = *reinterpret_cast<const uint2*>(vrow + 8);
             o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<bf16x8_t*>(av), bp, o[t], 0, 0, 0);
           }
         }
@@ -186,9 +211,9 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a, const int32
   for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      uint16_t e[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) e[i] = f32_to_bf16(o[t][g4 * 4 + i] * inv);
+      bf16x2_t e[2];
+      e[0] = __builtin_convertvector((f32x2_t){o[t][g4 * 4] * inv, o[t][g4 * 4 + 1] * inv}, bf16x2_t);
+      e[1] = __builtin_convertvector((f32x2_t){o[t][g4 * 4 + 2] * inv, o[t][g4 * 4 + 3] * inv}, bf16x2_t);
       *reinterpret_cast<uint2*>(orow + t * 32 + 8 * g4 + 4 * hi) = *reinterpret_cast<uint2*>(e);
     }
   }

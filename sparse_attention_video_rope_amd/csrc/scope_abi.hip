@@ -46,19 +46,15 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
   };
   const size_t BH = g.BH, N = g.N;
   const int nrope = g.T * g.dm[1] / 2 + g.Hg * g.dm[2] / 2 + g.Wg * g.dm[3] / 2;
-  const size_t NB = (N + 63) / 64;
   w.rope_tab = (double2*)take(sizeof(double2) * nrope);
   w.d2 = (double*)take(8 * BH * 4 * N);
   w.nearest = (int32_t*)take(4 * BH * 4 * N);
-  w.bsum = (double*)take(8 * BH * 4 * NB);
   w.seeds = (int32_t*)take(4 * BH * 4 * g.Cmax);
   w.qcent = (float*)take(4 * BH * g.Cq * g.d);
   w.kcent = (float*)take(4 * BH * g.Cm * g.d);
   w.cbf = (uint16_t*)take(2 * BH * 4 * g.CmaxPad * g.DPmax);
   w.cnorm = (float*)take(4 * BH * 4 * g.CmaxPad);
   w.labels = (int32_t*)take(4 * BH * 4 * N);
-  w.rlist = (int32_t*)take(4 * BH * 4 * N);
-  w.rcnt = (int32_t*)take(4 * (size_t)(g.iters + 1) * BH * 4);
   w.perm = (int32_t*)take(4 * BH * 4 * N);
   w.off = (int32_t*)take(4 * BH * 4 * (g.Cmax + 1));
   w.codes = (uint16_t*)take(8 * BH * N);
@@ -166,7 +162,6 @@ scope_status scope_plan(const scope_params* p, const void* q, const void* k, voi
 
   hipError_t e = hipSuccess;
 #define STEP(x) do { e = (x); if (e != hipSuccess) return hip_status(e); } while (0)
-  STEP(launch_fill_i32(w.rcnt, 0, (size_t)(g.iters + 1) * g.BH * 4, stream));
   STEP(launch_rope(g, *p, q, k, q_rope, k_rope, w, stream));
   if (!(p->flags & SCOPE_USE_INIT_CENTROIDS)) STEP(launch_seed(g, q_rope, k_rope, w, stream));
   STEP(launch_prep(g, w, stream));

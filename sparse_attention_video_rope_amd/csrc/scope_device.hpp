@@ -66,6 +66,40 @@ __device__ __forceinline__ T wave_min(T v) {
   return v;
 }
 
+// DPP lane move of an fp64 value (both 32-bit halves; lanes outside the pattern read 0).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, true);
+  return __hiloint2double(hi, lo);
+}
+
+// Sum over the 64 lanes of a wave, in a fixed order, without LDS: quad_perm
+// xor-1 / xor-2, row_half_mirror and row_mirror leave every lane of a 16-lane
+// row holding the row sum; the four row sums are then read from lanes 0, 16,
+// 32 and 48.  All 64 lanes must be active.
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v += dpp_f64<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);   // row_half_mirror
+  v += dpp_f64<0x140>(v);   // row_mirror
+  auto rl = [&](int l) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+  };
+  return (rl(0) + rl(16)) + (rl(32) + rl(48));
+}
+
+// Sum inside aligned groups of `n` lanes (n in {1, 2, 4, 8, 16}); every lane of
+// a group receives the group sum.  Fixed order, no LDS.
+__device__ __forceinline__ double group_sum_dpp(double v, int n) {
+  if (n >= 2) v += dpp_f64<0xB1>(v);    // xor 1
+  if (n >= 4) v += dpp_f64<0x4E>(v);    // xor 2
+  if (n >= 8) v += dpp_f64<0x141>(v);   // i <-> 7-i within 8
+  if (n >= 16) v += dpp_f64<0x140>(v);  // i <-> 15-i within 16
+  return v;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (fixed order).
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v) {

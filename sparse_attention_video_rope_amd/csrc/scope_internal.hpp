@@ -13,7 +13,7 @@ constexpr int ATT_BM = 128;     // queries per attention work item (4 waves x 32
 constexpr int SEL_NB = 2048;    // histogram bins per level in the selection kernels
 constexpr int SEL_CAP = 2048;   // boundary candidates sorted in LDS
 constexpr int MAX_C = 1024;     // largest Cq / Cm supported
-constexpr int MAX_N = 1 << 20;  // largest token count supported
+constexpr int MAX_N = 1 << 18;  // largest token count supported (16 groups of 16 rounds of 1024)
 
 // Geometry of the four clusterings of a head: 0 = queries (full d),
 // 1..3 = key channel ranges T, H, W.
@@ -42,16 +42,13 @@ struct Workspace {
   double2* rope_tab;            // cos/sin per (range, position, pair)
   int rope_off[3];
   double* d2;                   // [BH][4][N] k-means++ squared distance to the nearest centre
-  int32_t* nearest;             // [BH][4][N] index of that centre (bit 30: point is a centre)
-  double* bsum;                 // [BH][4][ceil(N/64)] per-64-point sums of d2
+  int32_t* nearest;             // [BH][4][N] uint16: index of that centre (bit 15: point is a centre)
   int32_t* seeds;               // [BH][4][Cmax]
   float* qcent;                 // [BH][Cq][d]
   float* kcent;                 // [BH][Cm][d]
   uint16_t* cbf;                // [BH][4][CmaxPad][DPmax] bf16 centroids, zero padded
   float* cnorm;                 // [BH][4][CmaxPad] ||bf16 centroid||^2 (FLT_MAX on padding)
   int32_t* labels;              // [BH][4][N]
-  int32_t* rlist;               // [BH][4][N] points whose assignment is refined in fp64
-  int32_t* rcnt;                // [iters+1][BH][4]
   int32_t* perm;                // [BH][4][N] points sorted by label (stable)
   int32_t* off;                 // [BH][4][Cmax+1] cluster offsets into perm
   uint16_t* codes;              // [BH][N][4]
