@@ -292,12 +292,18 @@ def hybrid_select(s: np.ndarray, n: np.ndarray, rho: float, alpha: float):
 # ---------------------------------------------------------------------------
 
 def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_labels: np.ndarray,
-                     sel: Sequence[np.ndarray]) -> np.ndarray:
-    """o_i = softmax_j in S_c(i) (<q_i, k_j>/sqrt(d)) v_j, fp64."""
+                     sel: Sequence[np.ndarray], only_rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """o_i = softmax_j in S_c(i) (<q_i, k_j>/sqrt(d)) v_j, fp64.
+
+    only_rows: compute just these query rows (the others stay zero).
+    """
     N, d = q.shape
     out = np.zeros((N, v.shape[1]), dtype=np.float64)
+    wanted = None if only_rows is None else np.zeros(N, dtype=bool)
+    if wanted is not None:
+        wanted[np.asarray(only_rows)] = True
     for c, keys in enumerate(sel):
-        rows = np.nonzero(q_labels == c)[0]
+        rows = np.nonzero((q_labels == c) & (True if wanted is None else wanted))[0]
         if len(rows) == 0:
             continue
         logit = (q[rows] @ k[keys].T) / np.sqrt(d)

@@ -219,6 +219,239 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a, const int32
   }
 }
 
+// bf16 path with two 32-query column tiles per wave (2 waves, 128 queries per
+// workgroup): every K / V^T operand read from LDS feeds two MFMAs, halving the
+// LDS traffic per flop, and the key indices of chunk kc+2 are loaded while
+// chunk kc is computed.
+template <int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void attend_bf16_x2_kernel(AttArgs a, const int32_t* __restrict__ work,
+                                                             const int32_t* __restrict__ status,
+                                                             const int32_t* __restrict__ perm_q,
+                                                             const int32_t* __restrict__ q_off,
+                                                             const int32_t* __restrict__ cr,
+                                                             const int64_t* __restrict__ sel_off,
+                                                             const int32_t* __restrict__ sel_idx,
+                                                             const uint16_t* __restrict__ qr,
+                                                             const uint16_t* __restrict__ kr,
+                                                             const uint16_t* __restrict__ vv,
+                                                             uint16_t* __restrict__ out) {
+  constexpr int NTH = 128;
+  constexpr int BN = 64;
+  constexpr int KLD = D + 8;
+  constexpr int VLD = BN + 4;
+  constexpr int KPT = BN * D / 8 / NTH;            // K 16-byte pieces per thread
+  constexpr int VPT = (BN / 2) * (D / 8) / NTH;    // V key-pair pieces per thread
+  constexpr int NIDX = KPT + 2 * VPT;              // key indices per thread per chunk
+  constexpr float RESCALE_LOG2 = 8.f;
+  __shared__ __align__(16) uint16_t Ks[2][BN * KLD];
+  __shared__ __align__(16) uint16_t Vt[2][D * VLD];
+
+  if (status[1]) return;
+  const int item = blockIdx.x;
+  if (item >= status[0]) return;
+  const int cid = work[2 * item], chunk = work[2 * item + 1];
+  const int bh = cid / a.Cq, c = cid % a.Cq;
+  const int32_t* qo = q_off + (size_t)bh * (a.Cq + 1);
+  const int q0 = qo[c] + chunk * ATT_BM;
+  const int nq = min(ATT_BM, qo[c + 1] - q0);
+  const int r = cr[cid];
+  const int32_t* keys = sel_idx + sel_off[cid];
+  const size_t hb = (size_t)bh * a.N;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, col = lane & 31, hi = lane >> 5;
+  const bool active = wv * 64 < nq;
+  int tok[2];
+  bool qvalid[2];
+  bf16x8_t qb[2][D / 16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int qi = wv * 64 + t * 32 + col;
+    qvalid[t] = qi < nq;
+    tok[t] = qvalid[t] ? min(max(perm_q[hb + q0 + qi], 0), a.N - 1) : 0;
+    const uint16_t* qrow = qr + (hb + tok[t]) * D + hi * 8;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      uint4 u = qvalid[t] ? *reinterpret_cast<const uint4*>(qrow + kb * 16) : make_uint4(0, 0, 0, 0);
+      qb[t][kb] = *reinterpret_cast<bf16x8_t*>(&u);
+    }
+  }
+  f32x16_t o[2][D / 32];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[t][dt] = f32x16_t{};
+  float mref[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.f, 0.f};
+  const float cs = a.scale_log2;
+  const int nchunks = (r + BN - 1) / BN;
+
+  // rows this thread gathers: K pieces i -> row (tid + i*NTH) / (D/8); V pairs i -> rows 2kp, 2kp+1
+  auto row_of = [&](int i) -> int {
+    if (i < KPT) return (tid + i * NTH) / (D / 8);
+    const int j = (i - KPT) >> 1, piece = tid + j * NTH;
+    return 2 * (piece % (BN / 2)) + ((i - KPT) & 1);
+  };
+  int kidx[NIDX];
+  auto load_idx = [&](int kc, int* dst) {
+    const int nk = min(BN, r - kc * BN);
+#pragma unroll
+    for (int i = 0; i < NIDX; ++i) {
+      const int rw = row_of(i);
+      const int j = rw < nk ? keys[kc * BN + rw] : -1;
+      dst[i] = j < 0 ? -1 : min(j, a.N - 1);
+    }
+  };
+  uint4 kbuf[KPT], vb0[VPT], vb1[VPT];
+  auto gather = [&](const int* ix) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c8 = (tid + i * NTH) % (D / 8);
+      kbuf[i] = ix[i] >= 0 ? *reinterpret_cast<const uint4*>(kr + (hb + ix[i]) * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int oc = (tid + i * NTH) / (BN / 2);
+      const int i0 = ix[KPT + 2 * i], i1 = ix[KPT + 2 * i + 1];
+      vb0[i] = i0 >= 0 ? *reinterpret_cast<const uint4*>(vv + (hb + i0) * D + oc * 8) : make_uint4(0, 0, 0, 0);
+      vb1[i] = i1 >= 0 ? *reinterpret_cast<const uint4*>(vv + (hb + i1) * D + oc * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int piece = tid + i * NTH;
+      const int row = piece / (D / 8), c8 = piece % (D / 8);
+      *reinterpret_cast<uint4*>(&Ks[buf][row * KLD + c8 * 8]) = kbuf[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int piece = tid + i * NTH;
+      const int kp = piece % (BN / 2), oc = piece / (BN / 2);
+      const uint32_t w0[4] = {vb0[i].x, vb0[i].y, vb0[i].z, vb0[i].w};
+      const uint32_t w1[4] = {vb1[i].x, vb1[i].y, vb1[i].z, vb1[i].w};
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&Vt[buf][(oc * 8) * VLD + 2 * kp]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dst[(2 * j) * (VLD / 2)] = __builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u);
+        dst[(2 * j + 1) * (VLD / 2)] = __builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u);
+      }
+    }
+  };
+
+  if (nchunks > 0) {
+    load_idx(0, kidx);
+    gather(kidx);
+    stash(0);
+    if (nchunks > 1) load_idx(1, kidx);
+  }
+  __syncthreads();
+  for (int kc = 0; kc < nchunks; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < nchunks) {
+      gather(kidx);                                // rows of chunk kc+1
+      if (kc + 2 < nchunks) load_idx(kc + 2, kidx);   // indices of chunk kc+2 (kidx is free again)
+    }
+    if (active) {
+      f32x16_t s[2][2];   // [query tile][key subtile]
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const uint16_t* arow = &Ks[buf][(st * 32 + col) * KLD + hi * 8];
+        bf16x8_t ak[D / 16];
+#pragma unroll
+        for (int kb = 0; kb < D / 16; ++kb) ak[kb] = *reinterpret_cast<const bf16x8_t*>(arow + kb * 16);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          s[t][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], qb[t][0], f32x16_t{}, 0, 0, 0);
+#pragma unroll
+          for (int kb = 1; kb < D / 16; ++kb)
+            s[t][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kb], qb[t][kb], s[t][st], 0, 0, 0);
+        }
+      }
+      const int kleft = r - kc * BN;
+      if (kleft < BN) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (st * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kleft) s[t][st][v] = -__builtin_inff();
+      }
+      float mc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float mloc = -__builtin_inff();
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) mloc = fmaxf(mloc, fmaxf(s[t][st][v], s[t][st][v + 1]));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const bool grow = (mloc - mref[t]) * cs > RESCALE_LOG2;
+        if (__ballot(grow)) {
+          const float mnew = grow ? mloc : mref[t];
+          const float alpha = __builtin_amdgcn_exp2f((mref[t] - mnew) * cs);
+          lsum[t] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[t][dt][v] *= alpha;
+          mref[t] = mnew;
+        }
+        mc[t] = mref[t] * cs;
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8_t bp[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            bf16x2_t pk[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][st][half * 8 + 2 * i], cs, -mc[t]));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][st][half * 8 + 2 * i + 1], cs, -mc[t]));
+              lsum[t] += p0 + p1;
+              pk[i] = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+            }
+            bp[t] = *reinterpret_cast<bf16x8_t*>(pk);
+          }
+          const int base = st * 32 + half * 16 + 4 * hi;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const uint16_t* vrow = &Vt[buf][(dt * 32 + col) * VLD + base];
+            uint2 av[2];
+            av[0] = *reinterpret_cast<const uint2*>(vrow);
+            av[1] = *reinterpret_cast<const uint2*>(vrow + 8);
+            const bf16x8_t avv = *reinterpret_cast<bf16x8_t*>(av);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              o[t][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avv, bp[t], o[t][dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (kc + 1 < nchunks) stash(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float ltot = lsum[t] + __shfl_xor(lsum[t], 32);
+    if (!qvalid[t]) continue;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    uint16_t* orow = out + (hb + tok[t]) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x2_t e[2];
+        e[0] = __builtin_convertvector((f32x2_t){o[t][dt][g4 * 4] * inv, o[t][dt][g4 * 4 + 1] * inv}, bf16x2_t);
+        e[1] = __builtin_convertvector((f32x2_t){o[t][dt][g4 * 4 + 2] * inv, o[t][dt][g4 * 4 + 3] * inv}, bf16x2_t);
+        *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g4 + 4 * hi) = *reinterpret_cast<uint2*>(e);
+      }
+    }
+  }
+}
+
 // fp32 storage: one thread per query, fp32 online softmax over the selected keys.
 template <int D>
 __global__ __launch_bounds__(ATT_BM) void attend_f32_kernel(AttArgs a, const int32_t* __restrict__ work,
@@ -272,8 +505,8 @@ hipError_t launch_attend(const Geo& g, const scope_plan_t& plan, const void* qr,
 #define SCOPE_ATT_ARGS a, plan.work, plan.status, plan.perm_q, plan.q_off, plan.counts_r, plan.sel_off, plan.sel_idx
   if (g.bf16) {
     if (g.d == 64)
-      attend_bf16_kernel<64><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
-                                                  (const uint16_t*)v, (uint16_t*)out);
+      attend_bf16_x2_kernel<64><<<grid, 128, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
+                                                     (const uint16_t*)v, (uint16_t*)out);
     else
       attend_bf16_kernel<128><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
                                                    (const uint16_t*)v, (uint16_t*)out);
