@@ -38,10 +38,11 @@ __device__ __forceinline__ double sqdist_row(const T* __restrict__ x, const doub
 // D^2 being the squared distance to the nearest centre chosen so far (fp64;
 // exact for bf16 data of ordinary range, so the summation order is
 // immaterial there).
-// Point p = r*1024 + tid belongs to round r; the rounds form groups of 8.
-// A wave's 64 points of a round are consecutive, so the running sum is taken
-// over (group, wave) sums, then over the rounds of the crossing (group,
-// wave), then over its lanes.
+// The points form groups of 8192; inside a group, wave w owns the 512
+// consecutive points starting at 512 w, one 64-point round per step of its
+// 8 rounds (lane = point mod 64).  So (group, wave, round, lane) is the index
+// order, and the running sum is taken over (group, wave) sums, then over the
+// rounds of the crossing (group, wave), then over its lanes.
 // The D^2 update skips a point whose current centre a has
 // ||c_s - a||^2 >= 4 D^2 (triangle inequality, Elkan ICML 2003): then
 // ||x - c_s|| >= D(x), so the result equals the unpruned update.  Each wave
@@ -131,8 +132,12 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
   while (lpr * 8 < dm) lpr <<= 1;
   const uint64_t stream = ((uint64_t)bh * 4 + m) << 20;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
+  // point of round k of the group starting at round r0 held by this thread:
+  // each wave owns SEED_RG*64 consecutive points of its group, so the order
+  // (group, wave, round, lane) is the index order
+  auto pidx = [&](int r0, int k) -> int { return r0 * SEED_NT + wv * (SEED_RG * 64) + k * 64 + lane; };
 
-  // group state: D^2 and packed 16-bit centre ids of rounds r0 .. r0+15
+  // group state: D^2 and packed 16-bit centre ids of this thread's 8 points of the group
   double gd2[SEED_RG];
   uint32_t gnr[SEED_RG / 2];
   auto nr_get = [&](int k) -> uint32_t { return (gnr[k >> 1] >> (16 * (k & 1))) & 0xFFFFu; };
@@ -141,13 +146,13 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
   };
   auto valid_mask = [&](int r0) {
     uint32_t vm = 0;
-    for (int k = 0; k < SEED_RG; ++k) vm |= (uint32_t)((r0 + k) * SEED_NT + tid < N) << k;
+    for (int k = 0; k < SEED_RG; ++k) vm |= (uint32_t)(pidx(r0, k) < N) << k;
     return vm;
   };
   auto load_group = [&](int r0, uint32_t vm) {
 #pragma unroll
     for (int k = 0; k < SEED_RG; ++k) {
-      const int p = (r0 + k) * SEED_NT + tid;
+      const int p = pidx(r0, k);
       const bool ok = (vm >> k) & 1u;
       gd2[k] = ok ? D2g[p] : 0.0;
       nr_set(k, ok ? (uint32_t)NRg[p] : NR_MARK);
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
 #pragma unroll
           for (int k = 0; k < SEED_RG; ++k) free_ |= (uint32_t)!(nr_get(k) & NR_MARK) << k;
           free_ &= vm;
-          if (free_) { atomicMin(&sh_lo, (r0 + __ffs(free_) - 1) * SEED_NT + tid); break; }
+          if (free_) { atomicMin(&sh_lo, pidx(r0, __ffs(free_) - 1)); break; }
         }
       } else if (mode == 1) {
         // rounding left the target at the very end: the last point with positive weight
@@ -225,18 +230,17 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
 #pragma unroll
           for (int k = 0; k < SEED_RG; ++k) posm |= (uint32_t)(gd2[k] > 0.0) << k;
           posm &= vm;
-          if (posm) { atomicMax(&sh_hi, (r0 + 31 - __clz(posm)) * SEED_NT + tid); break; }
+          if (posm) { atomicMax(&sh_hi, pidx(r0, 31 - __clz(posm))); break; }
         }
       } else if (wv == ww) {
         // the crossing wave: rounds of its group, then lanes of the crossing round
         const int r0 = gg * SEED_RG;
-        const int nrg = min(SEED_RG, R - r0);
         if (RESIDENT) {
 #pragma unroll
           for (int k = 0; k < SEED_RG; ++k) gscr[k * 64 + lane] = gd2[k];
         } else {
-          for (int k = 0; k < nrg; ++k) {
-            const int p = (r0 + k) * SEED_NT + tid;
+          for (int k = 0; k < SEED_RG; ++k) {
+            const int p = pidx(r0, k);
             gscr[k * 64 + lane] = p < N ? D2g[p] : 0.0;
           }
         }
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
         double excl = sh_excl;
         const double target = sh_target;
         int ksel = -1, klast = -1;
-        for (int k = 0; k < nrg; ++k) {
+        for (int k = 0; k < SEED_RG; ++k) {
           const double rs = wave_sum_dpp(gscr[k * 64 + lane]);
           if (rs > 0.0) klast = k;
           if (ksel < 0) { if (excl + rs > target) ksel = k; else excl += rs; }
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
         const uint64_t hit = __ballot(inc > target);
         const uint64_t pos = __ballot(v > 0.0);
         const int L = hit ? __ffsll((unsigned long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
-        if (lane == 0) sh_lo = (r0 + ksel) * SEED_NT + ww * 64 + L;
+        if (lane == 0) sh_lo = r0 * SEED_NT + ww * (SEED_RG * 64) + ksel * 64 + L;
         wave_sync_lds();
       }
       __syncthreads();
@@ -285,7 +289,16 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
     for (int gi = 0; gi < G; ++gi) {
       const int r0 = gi * SEED_RG;
       const uint32_t vm = valid_mask(r0);
-      if (!RESIDENT && s > 0) load_group(r0, vm);
+      if (!RESIDENT) {
+        if (s > 0) {
+          load_group(r0, vm);
+        } else {
+          // first pass: no stored state yet; points past N must not keep the
+          // previous group's values (they enter the wave sums below)
+#pragma unroll
+          for (int k = 0; k < SEED_RG; ++k) { gd2[k] = 0.0; nr_set(k, NR_MARK); }
+        }
+      }
       uint32_t mask = vm;
       if (s > 0) {
         mask = 0;   // points past N carry D^2 = 0, so the test prunes them
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
         while (mm) {
           const int k = __ffs(mm) - 1;
           mm &= mm - 1;
-          if (kk >= base && kk < base + SEED_LIST) lp[kk - base] = (r0 + k) * SEED_NT + tid;
+          if (kk >= base && kk < base + SEED_LIST) lp[kk - base] = pidx(r0, k);
           ++kk;
         }
         wave_sync_lds();
@@ -366,8 +379,8 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
         }
         wave_sync_lds();
       }
-      if (tid == ci % SEED_NT) {
-        const int kc = ci / SEED_NT - r0;   // uniform
+      if (ci / (SEED_RG * SEED_NT) == gi && tid == ((ci >> 9) & (SEED_NW - 1)) * 64 + (ci & 63)) {
+        const int kc = (ci >> 6) & (SEED_RG - 1);
 #pragma unroll
         for (int k = 0; k < SEED_RG; ++k) if (k == kc) { nr_set(k, nr_get(k) | NR_MARK); chg |= 1u << k; }
       }
@@ -376,7 +389,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
 #pragma unroll
         for (int k = 0; k < SEED_RG; ++k) {
           if ((chg >> k) & 1u) {
-            const int p = (r0 + k) * SEED_NT + tid;
+            const int p = pidx(r0, k);
             D2g[p] = gd2[k];
             NRg[p] = (uint16_t)nr_get(k);
           }

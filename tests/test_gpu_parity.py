@@ -173,3 +173,46 @@ def test_alpha_floor_end_to_end():
     heads = oracle_heads(w)
     g = run_gpu(w)
     assert_plan_equal(w, g, heads)
+
+
+# Above 8192 tokens the k-means++ kernel keeps D^2 and the nearest-centre ids
+# in global memory between draws instead of registers; these shapes take that
+# path, with a last group of point rounds that is only partly filled.
+LARGE = [
+    workloads.small("m64", 5, 43, 45, 64, (16, 24, 24), "bf16", 6, 12, index=106, H=1),
+    workloads.small("m128", 3, 37, 83, 128, (44, 42, 42), "bf16", 5, 9, index=107, H=1),
+    workloads.small("m64f", 2, 67, 71, 64, (16, 24, 24), "f32", 4, 6, index=108, H=1),
+]
+LARGE_IDS = [w.name for w in LARGE]
+
+
+@pytest.mark.parametrize("w", LARGE, ids=LARGE_IDS)
+def test_end_to_end_large_token_count(w):
+    say("e2e large", w.name, w.N)
+    heads = oracle_heads(w)
+    g = run_gpu(w)
+    assert g["status"][1] == 0
+    for bh, o in enumerate(heads):
+        assert g["seeds"][bh, 0, :w.Cq].tolist() == list(o["q_seeds"])
+        for m in range(3):
+            assert g["seeds"][bh, 1 + m, :w.Cm].tolist() == list(o["k_seeds"][m]), f"head {bh} subspace {m}"
+    assert_plan_equal(w, g, heads)
+    for bh, o in enumerate(heads):
+        mx, mn = assert_attention(g["out"][bh], o["out"], w.dtype, f"{w.name} head {bh}")
+        say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
+
+
+@pytest.mark.parametrize("grid", [(4, 61, 71), (7, 50, 77)])
+def test_kmeanspp_seeds_three_or_more_point_groups(grid):
+    """Seeds only, at 17324 and 26950 tokens (3 and 4 groups of 8192 points)."""
+    w = workloads.small("seedN", *grid, 64, (16, 24, 24), "bf16", 24, 24, index=109, H=1, iters=0)
+    say("seeds", grid, w.N)
+    q, k, _ = workloads.generate(w)
+    g = run_gpu(w, inputs=(q, k, k))
+    gridt = (w.T, w.Hg, w.Wg)
+    qr = O.round_storage(O.rope_3d(q[0], gridt, w.split, w.rope_base), w.dtype)
+    kr = O.round_storage(O.rope_3d(k[0], gridt, w.split, w.rope_base), w.dtype)
+    assert g["seeds"][0, 0, :w.Cq].tolist() == list(O.kmeanspp_seeds(qr, w.Cq, w.kmeans_seed, 0, 0))
+    for m, (off, dm) in enumerate(zip(O.subspace_offsets(w.split), w.split)):
+        want = O.kmeanspp_seeds(kr[:, off:off + dm], w.Cm, w.kmeans_seed, 0, 1 + m)
+        assert g["seeds"][0, 1 + m, :w.Cm].tolist() == list(want), f"subspace {m}"
