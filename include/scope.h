@@ -30,7 +30,12 @@
  *   - Work is enqueued on `stream` (a hipStream_t); no call synchronises the
  *     host.  Results become visible in stream order.
  *   - Parameter errors are reported synchronously, before any launch.  No
- *     C++ exception crosses the ABI.
+ *     C++ exception crosses the ABI.  SCOPE_ERR_INVALID: a size below 1, an
+ *     odd or non-positive channel range, d_t+d_h+d_w != d, Cq or Cm above N,
+ *     iters outside 0..1000, rope_base <= 1, rho outside (0, 1], alpha
+ *     outside [0, 1], an unknown dtype or flag, a null or misaligned pointer.
+ *     SCOPE_ERR_UNSUPPORTED: d not in {64, 128}, N > 262144, Cq or Cm above
+ *     1024, B*H > 65535.
  *   - Calls that overlap in time must use distinct workspaces and plans.
  */
 #ifndef SCOPE_H
@@ -60,12 +65,12 @@ typedef enum { SCOPE_F32 = 0, SCOPE_BF16 = 1 } scope_dtype;
                                          instead of seeded k-means++ */
 
 typedef struct {
-  int32_t B, H;            /* batch and heads; every (b, h) is independent */
-  int32_t T, Hg, Wg;       /* latent grid; N = T*Hg*Wg tokens */
+  int32_t B, H;            /* batch and heads; every (b, h) is independent; B*H <= 65535 */
+  int32_t T, Hg, Wg;       /* latent grid; N = T*Hg*Wg tokens, N <= 262144 */
   int32_t d;               /* head dim, 64 or 128 */
   int32_t d_t, d_h, d_w;   /* 3D-RoPE channel ranges [T | H | W], each even, sum d */
-  int32_t Cq;              /* query clusters, 1..N */
-  int32_t Cm;              /* centroids per key subspace (CT = CH = CW), 1..min(N, 32767) */
+  int32_t Cq;              /* query clusters, 1..N and at most 1024 */
+  int32_t Cm;              /* centroids per key subspace (CT = CH = CW), 1..N and at most 1024 */
   int32_t iters;           /* Lloyd iterations after seeding, 0..1000 */
   double rope_base;        /* RoPE base, > 1 (10000) */
   double rho;              /* Top-p threshold of Eq. (7), 0 < rho <= 1 */
