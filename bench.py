@@ -40,7 +40,79 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attend_traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (used if present and current)")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="one plan, 3 attention launches and 3 plain 256 MiB streaming copies (torch.neg), for "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the counter CSVs of two --profile-pass runs into --traffic-json")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+
+
+def profile_pass(a):
+    """Launches whose FETCH_SIZE / WRITE_SIZE counters give the attention kernel's HBM traffic.
+
+    The copy (torch.neg on 256 MiB of fp32) reads and writes COPY_BYTES each: the
+    ratio of its counters to COPY_BYTES calibrates the counters' unit."""
+    import torch
+    import sparse_attention_video_rope_amd as sav
+    import workloads
+    w = workloads.CONFIGS[a.config]
+    rho = w.rho if a.rho is None else a.rho
+    p = sav.params_for(w, rho=rho)
+    q, k, v = workloads.generate(w)
+    dev = torch.device("cuda:0")
+    to = lambda x: torch.from_numpy(x.reshape(-1)).to(torch.bfloat16 if w.dtype == "bf16" else torch.float32).to(dev)
+    qd, kd, vd = to(q), to(k), to(v)
+    pl = sav.Plan(p, device=dev, debug=False)
+    qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+    out = torch.empty_like(vd)
+    sav.plan(p, qd, kd, pl, qr, kr)
+    for _ in range(3):
+        sav.attend(p, pl, qr, kr, vd, out)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_pass": w.name, "rho": rho}), flush=True)
+
+
+def traffic_from(a):
+    """Per-launch HBM bytes of the attention kernel from two rocprofv3 counter CSVs."""
+    import csv
+    import workloads
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", a.traffic_from[0]), ("WRITE_SIZE", a.traffic_from[1])):
+        vals = per_kernel(path, counter)
+        att = [v for n, v in vals.items() if "attend_" in n]
+        cp = [v for n, v in vals.items() if "neg" in n]
+        if len(att) != 1 or len(cp) != 1:
+            raise SystemExit(f"{counter}: expected one attention and one copy kernel in {path}")
+        kib_att, kib_cp = float(np.mean(att[0])), float(np.mean(cp[0]))
+        factor = COPY_BYTES / (kib_cp * 1024.0)
+        out[counter] = {"attend_kib_per_launch": kib_att, "copy_kib_per_launch": kib_cp,
+                        "copy_bytes": COPY_BYTES, "factor": factor,
+                        "attend_bytes_per_launch": kib_att * 1024.0 * factor}
+    w = workloads.CONFIGS[a.config]
+    rho = w.rho if a.rho is None else a.rho
+    doc = {"workload": w.name, "rho": rho, "kernel_source_sha": _attend_sha(),
+           "bytes_per_launch": out["FETCH_SIZE"]["attend_bytes_per_launch"] +
+                               out["WRITE_SIZE"]["attend_bytes_per_launch"],
+           "counters": out}
+    with open(a.traffic_json, "w") as f:
+        json.dump(doc, f, indent=1)
+    print(json.dumps(doc))
 
 
 def cpu_baseline(w, rho):
@@ -66,10 +138,14 @@ def cpu_baseline(w, rho):
 
 def main():
     a = parse()
+    if a.traffic_from:
+        return traffic_from(a)
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (heads shard across GPUs, "
                                    "see the design notes)"}))
         sys.exit(2)
+    if a.profile_pass:
+        return profile_pass(a)
     import torch
     import sparse_attention_video_rope_amd as sav
     import workloads

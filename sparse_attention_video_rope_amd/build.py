@@ -35,9 +35,14 @@ def hipcc() -> str:
     return exe
 
 
+# per-file additions: the attention kernels never see NaN (finite inputs, masked
+# logits are -inf), so max() needs no NaN quieting of the MFMA results
+FILE_FLAGS = {"attend.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -3,9 +3,9 @@
 // computed over the selected original keys and values", SCOPE abstract):
 //   o_i = sum_{j in S_c(i)} softmax_j(<q'_i, k'_j> / sqrt(d)) v_j.
 //
-// bf16 path (gfx950, wave64): one workgroup per (cluster, 128-query chunk);
-// each of the 4 waves owns 32 queries whose Q rows stay in registers as MFMA
-// operands.  Selected keys are gathered 64 at a time into LDS (K row-major,
+// bf16 path (gfx950, wave64): one workgroup per (cluster, query chunk) work
+// item; each wave owns 32 (head dim 128) or 64 (head dim 64) queries whose Q
+// rows stay in registers as MFMA operands.  Selected keys are gathered 64 at a time into LDS (K row-major,
 // V transposed), double buffered.  Per 32-key subtile the wave computes
 // S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so each lane holds 16 logits of
 // one query: the online-softmax max and sum need one cross-lane exchange, and
@@ -21,6 +21,15 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// 16-byte row piece; a native vector (not the uint4 struct, whose whole-object
+// copies become memcpy through private memory)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Work item of this workgroup, or -1 (items past the device-side count exit).
+__device__ __forceinline__ int att_item(int n_work) {
+  const int item = blockIdx.x;
+  return item < n_work ? item : -1;
+}
 
 struct AttArgs {
   int N, Cq;
@@ -50,8 +59,8 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a, const int32
   __shared__ __align__(16) uint16_t Vt[2][D * VLD];
 
   if (status[1]) return;
-  const int item = blockIdx.x;
-  if (item >= status[0]) return;
+  const int item = att_item(status[0]);
+  if (item < 0) return;
   const int cid = work[2 * item], chunk = work[2 * item + 1];
   const int bh = cid / a.Cq, c = cid % a.Cq;
   const int32_t* qo = q_off + (size_t)bh * (a.Cq + 1);
@@ -219,44 +228,45 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a, const int32
   }
 }
 
-// bf16 path with two 32-query column tiles per wave (2 waves, 128 queries per
-// workgroup): every K / V^T operand read from LDS feeds two MFMAs, halving the
-// LDS traffic per flop, and the key indices of chunk kc+2 are loaded while
-// chunk kc is computed.
-template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void attend_bf16_x2_kernel(AttArgs a, const int32_t* __restrict__ work,
-                                                             const int32_t* __restrict__ status,
-                                                             const int32_t* __restrict__ perm_q,
-                                                             const int32_t* __restrict__ q_off,
-                                                             const int32_t* __restrict__ cr,
-                                                             const int64_t* __restrict__ sel_off,
-                                                             const int32_t* __restrict__ sel_idx,
-                                                             const uint16_t* __restrict__ qr,
-                                                             const uint16_t* __restrict__ kr,
-                                                             const uint16_t* __restrict__ vv,
-                                                             uint16_t* __restrict__ out) {
-  constexpr int NTH = 128;
+// bf16 path with two 32-query column tiles per wave (NW waves, 64*NW queries
+// per workgroup): every K / V^T operand read from LDS feeds two MFMAs, and the
+// key indices of chunk kc+2 are loaded while chunk kc is computed.  Gathers
+// are unconditional: indices past r_c repeat the last selected key (those
+// logits are masked to -inf), so no lane needs a branch or a zero fill.  The
+// row sum is taken over the bf16-rounded probabilities that feed the P V
+// product (dot2 with (1, 1)), so the normalisation matches the weights used.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attend_bf16_pair_kernel(
+    AttArgs a, const int32_t* __restrict__ work, const int32_t* __restrict__ status,
+    const int32_t* __restrict__ perm_q, const int32_t* __restrict__ q_off, const int32_t* __restrict__ cr,
+    const int64_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, const uint16_t* __restrict__ qr,
+    const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vv, uint16_t* __restrict__ out) {
+  constexpr int NTH = 64 * NW;
+  constexpr int BM = 64 * NW;
   constexpr int BN = 64;
   constexpr int KLD = D + 8;
   constexpr int VLD = BN + 4;
   constexpr int KPT = BN * D / 8 / NTH;            // K 16-byte pieces per thread
   constexpr int VPT = (BN / 2) * (D / 8) / NTH;    // V key-pair pieces per thread
+  static_assert(KPT * NTH == BN * D / 8 && VPT * NTH == (BN / 2) * (D / 8), "gather split");
   constexpr int NIDX = KPT + 2 * VPT;              // key indices per thread per chunk
   constexpr float RESCALE_LOG2 = 8.f;
   __shared__ __align__(16) uint16_t Ks[2][BN * KLD];
   __shared__ __align__(16) uint16_t Vt[2][D * VLD];
 
   if (status[1]) return;
-  const int item = blockIdx.x;
-  if (item >= status[0]) return;
+  const int item = att_item(status[0]);
+  if (item < 0) return;
   const int cid = work[2 * item], chunk = work[2 * item + 1];
   const int bh = cid / a.Cq, c = cid % a.Cq;
   const int32_t* qo = q_off + (size_t)bh * (a.Cq + 1);
-  const int q0 = qo[c] + chunk * ATT_BM;
-  const int nq = min(ATT_BM, qo[c + 1] - q0);
+  const int q0 = qo[c] + chunk * BM;
+  const int nq = min(BM, qo[c + 1] - q0);
   const int r = cr[cid];
   const int32_t* keys = sel_idx + sel_off[cid];
   const size_t hb = (size_t)bh * a.N;
+  const char* kbase = reinterpret_cast<const char*>(kr + hb * D);
+  const char* vbase = reinterpret_cast<const char*>(vv + hb * D);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, col = lane & 31, hi = lane >> 5;
   const bool active = wv * 64 < nq;
@@ -283,6 +293,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void a
   float mref[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.f, 0.f};
   const float cs = a.scale_log2;
   const int nchunks = (r + BN - 1) / BN;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // rows this thread gathers: K pieces i -> row (tid + i*NTH) / (D/8); V pairs i -> rows 2kp, 2kp+1
   auto row_of = [&](int i) -> int {
@@ -290,29 +301,28 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int j = (i - KPT) >> 1, piece = tid + j * NTH;
     return 2 * (piece % (BN / 2)) + ((i - KPT) & 1);
   };
+  // Raw key indices of a chunk, loaded one chunk ahead of their gather and left
+  // untouched until then: vmcnt retires loads in order, so any arithmetic on
+  // them here would make the wave wait for the row gathers issued before them.
   int kidx[NIDX];
   auto load_idx = [&](int kc, int* dst) {
-    const int nk = min(BN, r - kc * BN);
 #pragma unroll
-    for (int i = 0; i < NIDX; ++i) {
-      const int rw = row_of(i);
-      const int j = rw < nk ? keys[kc * BN + rw] : -1;
-      dst[i] = j < 0 ? -1 : min(j, a.N - 1);
-    }
+    for (int i = 0; i < NIDX; ++i) dst[i] = keys[min(kc * BN + row_of(i), r - 1)];
   };
-  uint4 kbuf[KPT], vb0[VPT], vb1[VPT];
+  // byte offset of a gathered row inside the head (index clamped to [0, N))
+  auto row_off = [&](int j) -> uint32_t { return (uint32_t)min(max(j, 0), a.N - 1) * (uint32_t)(D * 2); };
+  u32x4_t kbuf[KPT], vb0[VPT], vb1[VPT];
   auto gather = [&](const int* ix) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c8 = (tid + i * NTH) % (D / 8);
-      kbuf[i] = ix[i] >= 0 ? *reinterpret_cast<const uint4*>(kr + (hb + ix[i]) * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+      kbuf[i] = *reinterpret_cast<const u32x4_t*>(kbase + row_off(ix[i]) + c8 * 16);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int oc = (tid + i * NTH) / (BN / 2);
-      const int i0 = ix[KPT + 2 * i], i1 = ix[KPT + 2 * i + 1];
-      vb0[i] = i0 >= 0 ? *reinterpret_cast<const uint4*>(vv + (hb + i0) * D + oc * 8) : make_uint4(0, 0, 0, 0);
-      vb1[i] = i1 >= 0 ? *reinterpret_cast<const uint4*>(vv + (hb + i1) * D + oc * 8) : make_uint4(0, 0, 0, 0);
+      vb0[i] = *reinterpret_cast<const u32x4_t*>(vbase + row_off(ix[KPT + 2 * i]) + oc * 16);
+      vb1[i] = *reinterpret_cast<const u32x4_t*>(vbase + row_off(ix[KPT + 2 * i + 1]) + oc * 16);
     }
   };
   auto stash = [&](int buf) {
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int i = 0; i < KPT; ++i) {
       const int piece = tid + i * NTH;
       const int row = piece / (D / 8), c8 = piece % (D / 8);
-      *reinterpret_cast<uint4*>(&Ks[buf][row * KLD + c8 * 8]) = kbuf[i];
+      *reinterpret_cast<u32x4_t*>(&Ks[buf][row * KLD + c8 * 8]) = kbuf[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -341,14 +351,20 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void a
     load_idx(0, kidx);
     gather(kidx);
     stash(0);
-    if (nchunks > 1) load_idx(1, kidx);
   }
+  // Q rows, the first chunk and its indices are complete here: the loop then
+  // carries only its own loads, whose waits sit at their first use
+  __builtin_amdgcn_s_waitcnt(0);
+  if (nchunks > 1) load_idx(1, kidx);
   __syncthreads();
   for (int kc = 0; kc < nchunks; ++kc) {
     const int buf = kc & 1;
     if (kc + 1 < nchunks) {
       gather(kidx);                                // rows of chunk kc+1
-      if (kc + 2 < nchunks) load_idx(kc + 2, kidx);   // indices of chunk kc+2 (kidx is free again)
+      // indices of chunk kc+2 (kidx is free again); issued unconditionally
+      // (clamped to the last chunk) so the wait before the stash below counts
+      // exactly these loads
+      load_idx(min(kc + 2, nchunks - 1), kidx);
     }
     if (active) {
       f32x16_t s[2][2];   // [query tile][key subtile]
@@ -410,8 +426,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void a
             for (int i = 0; i < 4; ++i) {
               const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][st][half * 8 + 2 * i], cs, -mc[t]));
               const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][st][half * 8 + 2 * i + 1], cs, -mc[t]));
-              lsum[t] += p0 + p1;
               pk[i] = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+              lsum[t] = __builtin_amdgcn_fdot2_f32_bf16(pk[i], ones, lsum[t], false);
             }
             bp[t] = *reinterpret_cast<bf16x8_t*>(pk);
           }
@@ -464,8 +480,8 @@ __global__ __launch_bounds__(ATT_BM) void attend_f32_kernel(AttArgs a, const int
                                                             const float* __restrict__ qr, const float* __restrict__ kr,
                                                             const float* __restrict__ vv, float* __restrict__ out) {
   if (status[1]) return;
-  const int item = blockIdx.x;
-  if (item >= status[0]) return;
+  const int item = att_item(status[0]);
+  if (item < 0) return;
   const int cid = work[2 * item], chunk = work[2 * item + 1];
   const int bh = cid / a.Cq, c = cid % a.Cq;
   const int32_t* qo = q_off + (size_t)bh * (a.Cq + 1);
@@ -500,13 +516,13 @@ hipError_t launch_attend(const Geo& g, const scope_plan_t& plan, const void* qr,
   a.Cq = g.Cq;
   a.scale = (float)(1.0 / sqrt((double)g.d));
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
+  if (plan.work_capacity == 0) return hipSuccess;
   const unsigned grid = (unsigned)plan.work_capacity;
-  if (grid == 0) return hipSuccess;
 #define SCOPE_ATT_ARGS a, plan.work, plan.status, plan.perm_q, plan.q_off, plan.counts_r, plan.sel_off, plan.sel_idx
   if (g.bf16) {
     if (g.d == 64)
-      attend_bf16_x2_kernel<64><<<grid, 128, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
-                                                     (const uint16_t*)v, (uint16_t*)out);
+      attend_bf16_pair_kernel<64, 4><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
+                                                          (const uint16_t*)v, (uint16_t*)out);
     else
       attend_bf16_kernel<128><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
                                                    (const uint16_t*)v, (uint16_t*)out);

@@ -95,7 +95,8 @@ static scope_status validate(const scope_params* p) {
 }
 
 static int64_t work_cap(const Geo& g) {
-  return (int64_t)g.BH * (g.Cq + (g.N + ATT_BM - 1) / ATT_BM);
+  const int bm = att_chunk(g);
+  return (int64_t)g.BH * (g.Cq + (g.N + bm - 1) / bm);
 }
 
 static scope_status check_plan_core(const scope_plan_t* pl) {

@@ -547,7 +547,7 @@ __global__ __launch_bounds__(NT) void final_select_kernel(SelArgs a, const doubl
 // Attention work list: one item per (cluster, 128-query chunk), cluster-major
 // in (head, cluster) order; one workgroup.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void worklist_kernel(int BH, int Cq, const int32_t* __restrict__ q_off,
+__global__ __launch_bounds__(1024) void worklist_kernel(int BH, int Cq, int chunk, const int32_t* __restrict__ q_off,
                                                         const int32_t* __restrict__ cr, int32_t* __restrict__ work,
                                                         int64_t cap, int32_t* __restrict__ status) {
   __shared__ int64_t tmp[17];
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(int BH, int Cq, const in
     if (i < total) {
       const int bh = (int)(i / Cq), c = (int)(i % Cq);
       const int n = q_off[(size_t)bh * (Cq + 1) + c + 1] - q_off[(size_t)bh * (Cq + 1) + c];
-      items = (cr[i] > 0 && n > 0) ? (n + ATT_BM - 1) / ATT_BM : 0;
+      items = (cr[i] > 0 && n > 0) ? (n + chunk - 1) / chunk : 0;
     }
     int64_t tot;
     int64_t pos = base + block_incl_scan<int64_t, 1024>(items, tmp, &tot) - items;
@@ -620,7 +620,7 @@ hipError_t launch_final_select(const Geo& g, const scope_params& p, const Worksp
 }
 
 hipError_t launch_worklist(const Geo& g, const scope_plan_t& plan, hipStream_t s) {
-  worklist_kernel<<<1, 1024, 0, s>>>(g.BH, g.Cq, plan.q_off, plan.counts_r, plan.work, plan.work_capacity,
+  worklist_kernel<<<1, 1024, 0, s>>>(g.BH, g.Cq, att_chunk(g), plan.q_off, plan.counts_r, plan.work, plan.work_capacity,
                                       plan.status);
   return hipGetLastError();
 }
