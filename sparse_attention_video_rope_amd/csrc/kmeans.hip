@@ -696,87 +696,105 @@ __global__ __launch_bounds__(1024) void sort_kernel(Geo g, const int32_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Lloyd update: one wave per (cluster, clustering, head) sums its members'
-// rows (in the order of the stable sort), divides by the count in fp64,
-// rounds to fp32, and refreshes the bf16 copy and its squared norm.
-// lpr lanes share a member row (8 channels each); the 64/lpr row slots of a
-// wave take members slot, slot + 64/lpr, ...; slots are combined with fixed
-// lane exchanges.  Sums are exact for bf16 data, so the order is immaterial
-// there and fixed everywhere.
+// Lloyd update, in two passes that replace a sort by label:
+//  accum_kernel: one workgroup per (point range, channel slice, clustering,
+//    head) streams its points in index order and adds every channel value, in
+//    fp64, to an LDS table sums[label][channel] (lanes = channels, 64/SW points
+//    per instruction, so no two lanes of one instruction share an address
+//    unless two points share a label); slice 0 also counts the points per
+//    label.  The table is written out as one partial per workgroup.
+//  finalize_kernel: one wave per centroid adds the partials in a fixed order,
+//    divides by the count, rounds to fp32 (an empty cluster keeps its
+//    centroid), and refreshes the bf16 copy and its squared norm.
+// bf16 values are exactly representable in fp64 and their sums over at most
+// 2^18 points stay exact for data of ordinary range, so the LDS atomic order
+// does not change the result: the mean equals exact sum / n rounded once.
 // ---------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ void load8(const T* __restrict__ x, bool vec, int nvalid, double* o);
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* __restrict__ x, bool vec, int nvalid, double* o) {
-  uint32_t w[4];
-  if (vec) {
-    const uint4 u = *reinterpret_cast<const uint4*>(x);
-    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
-  } else {
+constexpr int ACC_NT = 512;
+
+template <typename T, int SW>
+__global__ __launch_bounds__(ACC_NT) void accum_kernel(const T* __restrict__ qr, const T* __restrict__ kr, Geo g,
+                                                       const int32_t* __restrict__ labels, double* __restrict__ psum,
+                                                       int32_t* __restrict__ pcnt, int nslices, int parts) {
+  const int part = blockIdx.x, bh = blockIdx.z;
+  // blockIdx.y enumerates the (clustering, slice) pairs
+  int m = 0, sl = blockIdx.y;
+  while (m < 3 && sl >= (g.dm[m] + SW - 1) / SW) { sl -= (g.dm[m] + SW - 1) / SW; ++m; }
+  const int N = g.N, d = g.d, dm = g.dm[m], C = g.C[m];
+  const int s0 = sl * SW, sw = min(SW, dm - s0);
+  if (sw <= 0) return;
+  extern __shared__ __align__(16) unsigned char acc_smem[];
+  double* S = reinterpret_cast<double*>(acc_smem);                         // [C][SW]
+  int32_t* cnt = reinterpret_cast<int32_t*>(acc_smem + (size_t)C * SW * 8);  // [C]
+  // the wave index is uniform; readfirstlane lets the compiler keep wave-level values in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < C * SW; i += ACC_NT) S[i] = 0.0;
+  for (int i = tid; i < C; i += ACC_NT) cnt[i] = 0;
+  __syncthreads();
+
+  const int per = (N + parts - 1) / parts;
+  const int p0 = min(N, part * per), p1 = min(N, p0 + per);
+  const int32_t* lab = labels + ((size_t)bh * 4 + m) * N;
+  const T* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + g.off[m] + s0;
+  // A wave takes 64 points at a time.  Instruction k covers the G points
+  // k + j*ST (j = lane / SW), which lie ST tokens apart and so rarely share a
+  // label (an LDS address).  Loads use clamped addresses and adds are
+  // unconditional, so the loop has no branches.
+  constexpr int G = 64 / SW, ST = SW;
+  const int ch = lane % SW, sub = lane / SW;
+  const bool chv = ch < sw;
+  const int chc = min(ch, sw - 1);
+  int c0 = p0 + wv * 64;
+  int Lnext = lab[min(c0 + lane, N - 1)];
+  for (; c0 < p1; c0 += ACC_NT) {
+    const int pl = c0 + lane;
+    const int L = min(max(Lnext, 0), C - 1);
+    const int np = min(64, p1 - c0);
+    float v[ST];   // exact copies of the stored values (bf16 or fp32)
+    const char* xc = reinterpret_cast<const char*>(X + (size_t)c0 * d);   // uniform base, 32-bit byte offsets
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = 2 * j < nvalid ? reinterpret_cast<const uint32_t*>(x)[j] : 0u;
+    for (int k = 0; k < ST; ++k)
+      v[k] = Elem<T>::ldf(reinterpret_cast<const T*>(xc + (uint32_t)((min(k + sub * ST, np - 1) * d + chc) * sizeof(T))));
+    // labels of the next chunk, in flight during this chunk's adds
+    Lnext = lab[min(c0 + ACC_NT + lane, N - 1)];
+    if (sl == 0 && pl < p1) atomicAdd(&cnt[L], 1);
+#pragma unroll
+    for (int k = 0; k < ST; ++k) {
+      const int q = k + sub * ST;
+      const int lk = __shfl(L, q, 64);
+      // lanes without a point add -0.0, which leaves every sum unchanged
+      atomicAdd(&S[lk * SW + ch], (chv && q < np) ? (double)v[k] : -0.0);
+    }
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    o[2 * j] = 2 * j < nvalid ? (double)__uint_as_float(w[j] << 16) : 0.0;
-    o[2 * j + 1] = 2 * j + 1 < nvalid ? (double)__uint_as_float(w[j] & 0xFFFF0000u) : 0.0;
+  __syncthreads();
+  double* out = psum + ((((size_t)bh * 4 + m) * nslices + sl) * parts + part) * (size_t)g.Cmax * SW;
+  for (int i = tid; i < C * SW; i += ACC_NT) out[i] = S[i];
+  if (sl == 0) {
+    int32_t* oc = pcnt + (((size_t)bh * 4 + m) * parts + part) * g.Cmax;
+    for (int i = tid; i < C; i += ACC_NT) oc[i] = cnt[i];
   }
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float* __restrict__ x, bool vec, int nvalid, double* o) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = j < nvalid ? (double)x[j] : 0.0;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void segsum_kernel(const T* __restrict__ qr, const T* __restrict__ kr, Geo g,
-                                                     const int32_t* __restrict__ perm,
-                                                     const int32_t* __restrict__ off, float* __restrict__ qcent,
-                                                     float* __restrict__ kcent, uint16_t* __restrict__ cbf,
-                                                     float* __restrict__ cnorm) {
+__global__ __launch_bounds__(256) void finalize_kernel(Geo g, const double* __restrict__ psum,
+                                                       const int32_t* __restrict__ pcnt, int SW, int nslices,
+                                                       int parts, float* __restrict__ qcent, float* __restrict__ kcent,
+                                                       uint16_t* __restrict__ cbf, float* __restrict__ cnorm) {
   const int m = blockIdx.y, bh = blockIdx.z;
   const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (c >= g.C[m]) return;
-  const int N = g.N, d = g.d, dm = g.dm[m], doff = g.off[m];
-  const int lane = threadIdx.x & 63;
-  int lpr = 1;
-  while (lpr * 8 < dm) lpr <<= 1;
-  const int sub = lane & (lpr - 1), slot = lane / lpr, nslot = 64 / lpr;
-  const int32_t* of = off + ((size_t)bh * 4 + m) * (g.Cmax + 1);
-  const int a = of[c], cnt = of[c + 1] - a;
-  float* row = m == 0 ? qcent + ((size_t)bh * g.Cq + c) * d : kcent + ((size_t)bh * g.Cm + c) * d + doff;
-  const int nvalid = min(8, dm - sub * 8);
-  const bool vec = sizeof(T) == 2 && ((doff * 2) % 16 == 0) && ((d * 2) % 16 == 0) && nvalid == 8;
-  if (cnt > 0) {
-    const int32_t* pm = perm + ((size_t)bh * 4 + m) * N + a;
-    const T* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + doff + sub * 8;
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (nvalid > 0) {
-      for (int k0 = slot; k0 < cnt; k0 += 4 * nslot) {
-        double v[4][8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int k = k0 + u * nslot;
-          if (k < cnt) load8<T>(X + (size_t)pm[k] * d, vec, nvalid, v[u]);
-          else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[u][j] = 0.0;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j] += v[u][j];
-      }
+  const int d = g.d, dm = g.dm[m], lane = threadIdx.x & 63;
+  int n = 0;
+  const int32_t* pc = pcnt + ((size_t)bh * 4 + m) * parts * g.Cmax + c;
+  for (int q = 0; q < parts; ++q) n += pc[(size_t)q * g.Cmax];
+  float* row = m == 0 ? qcent + ((size_t)bh * g.Cq + c) * d : kcent + ((size_t)bh * g.Cm + c) * d + g.off[m];
+  if (n > 0) {
+    for (int ch = lane; ch < dm; ch += 64) {
+      const int sl = ch / SW, j = ch % SW;
+      const double* ps = psum + (((size_t)bh * 4 + m) * nslices + sl) * parts * (size_t)g.Cmax * SW + (size_t)c * SW + j;
+      double sum = 0.0;
+      for (int q = 0; q < parts; ++q) sum += ps[(size_t)q * g.Cmax * SW];
+      row[ch] = (float)(sum / (double)n);
     }
-    // combine the row slots holding the same channels (lanes lpr, 2 lpr, ... apart)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      for (int o = lpr; o < 64; o <<= 1) acc[j] += __shfl_xor(acc[j], o, 64);
-    if (slot == 0)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < nvalid) row[sub * 8 + j] = (float)(acc[j] / (double)cnt);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -870,22 +888,25 @@ hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Wor
   return hipGetLastError();
 }
 
-hipError_t launch_sort(const Geo& g, const Workspace& w, hipStream_t s) {
-  sort_kernel<<<dim3(4, g.BH), 1024, 0, s>>>(g, w.labels, 0, w.perm, (int64_t)4 * g.N, g.N, w.off,
-                                             (int64_t)4 * (g.Cmax + 1), g.Cmax + 1);
-  return hipGetLastError();
-}
-
 hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Workspace& w, hipStream_t s) {
-  hipError_t e = launch_sort(g, w, s);
-  if (e != hipSuccess) return e;
-  dim3 grid((g.Cmax + 3) / 4, 4, g.BH);
-  if (g.bf16)
-    segsum_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.perm, w.off,
-                                                 w.qcent, w.kcent, w.cbf, w.cnorm);
-  else
-    segsum_kernel<float><<<grid, 256, 0, s>>>((const float*)qr, (const float*)kr, g, w.perm, w.off, w.qcent,
-                                              w.kcent, w.cbf, w.cnorm);
+  const int SW = acc_sw(g), ns = acc_slices(g), parts = acc_parts(g);
+  int ypairs = 0;
+  for (int m = 0; m < 4; ++m) ypairs += (g.dm[m] + SW - 1) / SW;
+  const size_t lds = (size_t)g.Cmax * SW * 8 + (size_t)g.Cmax * 4;
+  dim3 grid(parts, ypairs, g.BH);
+  auto go = [&](auto kern, const auto* q, const auto* k) {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    kern<<<grid, ACC_NT, lds, s>>>(q, k, g, w.labels, w.psum, w.pcnt, ns, parts);
+  };
+  const uint16_t *qb = (const uint16_t*)qr, *kb = (const uint16_t*)kr;
+  const float *qf = (const float*)qr, *kf = (const float*)kr;
+  if (g.bf16) {
+    if (SW == 32) go(accum_kernel<uint16_t, 32>, qb, kb); else go(accum_kernel<uint16_t, 16>, qb, kb);
+  } else {
+    if (SW == 32) go(accum_kernel<float, 32>, qf, kf); else go(accum_kernel<float, 16>, qf, kf);
+  }
+  finalize_kernel<<<dim3((g.Cmax + 3) / 4, 4, g.BH), 256, 0, s>>>(g, w.psum, w.pcnt, SW, ns, parts, w.qcent, w.kcent,
+                                                                  w.cbf, w.cnorm);
   return hipGetLastError();
 }
 

@@ -55,8 +55,8 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
   w.cbf = (uint16_t*)take(2 * BH * 4 * g.CmaxPad * g.DPmax);
   w.cnorm = (float*)take(4 * BH * 4 * g.CmaxPad);
   w.labels = (int32_t*)take(4 * BH * 4 * N);
-  w.perm = (int32_t*)take(4 * BH * 4 * N);
-  w.off = (int32_t*)take(4 * BH * 4 * (g.Cmax + 1));
+  w.psum = (double*)take(8 * BH * 4 * (size_t)acc_slices(g) * acc_parts(g) * g.Cmax * acc_sw(g));
+  w.pcnt = (int32_t*)take(4 * BH * 4 * (size_t)acc_parts(g) * g.Cmax);
   w.codes = (uint16_t*)take(8 * BH * N);
   w.qlab = (int32_t*)take(4 * BH * N);
   w.lut = (double*)take(8 * BH * g.Cq * 3 * g.Cm);

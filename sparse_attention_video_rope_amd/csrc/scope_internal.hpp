@@ -49,8 +49,8 @@ struct Workspace {
   uint16_t* cbf;                // [BH][4][CmaxPad][DPmax] bf16 centroids, zero padded
   float* cnorm;                 // [BH][4][CmaxPad] ||bf16 centroid||^2 (FLT_MAX on padding)
   int32_t* labels;              // [BH][4][N]
-  int32_t* perm;                // [BH][4][N] points sorted by label (stable)
-  int32_t* off;                 // [BH][4][Cmax+1] cluster offsets into perm
+  double* psum;                 // [BH][4][acc_slices][acc_parts][Cmax][acc_sw] partial centroid sums
+  int32_t* pcnt;                // [BH][4][acc_parts][Cmax] partial cluster sizes
   uint16_t* codes;              // [BH][N][4]
   int32_t* qlab;                // [BH][N] (final query labels)
   double* lut;                  // [BH][Cq][3][Cm]
@@ -61,6 +61,16 @@ struct Workspace {
 // Queries per attention work item: the bf16 head-dim-64 kernel runs 4 waves of
 // 64 queries; the bf16 head-dim-128 and fp32 kernels run 128.
 inline int att_chunk(const Geo& g) { return (g.bf16 && g.d == 64) ? 256 : ATT_BM; }
+// Lloyd update layout: channel slices of acc_sw channels, acc_parts point
+// ranges per (head, clustering).  Slices are 32 channels wide unless the
+// per-cluster sums of that width would not fit in LDS.
+inline int acc_sw(const Geo& g) { return g.Cmax <= 600 ? 32 : 16; }
+inline int acc_slices(const Geo& g) { return (g.d + acc_sw(g) - 1) / acc_sw(g); }
+inline int acc_parts(const Geo& g) {
+  const int p = (g.N + 4095) / 4096;
+  return p < 1 ? 1 : (p > 8 ? 8 : p);
+}
+
 Geo make_geo(const scope_params& p);
 // Lays the workspace out from `base` (nullptr: only computes .bytes).
 Workspace carve(const Geo& g, const scope_plan_t* plan, char* base);
