@@ -35,9 +35,10 @@ def hipcc() -> str:
     return exe
 
 
-# per-file additions: the attention kernels never see NaN (finite inputs, masked
-# logits are -inf), so max() needs no NaN quieting of the MFMA results
-FILE_FLAGS = {"attend.hip": ["-fno-honor-nans"]}
+# per-file additions: the attention and k-means kernels never see NaN (finite
+# inputs; masked logits are -inf), so min() / max() need no NaN quieting of the
+# MFMA results
+FILE_FLAGS = {"attend.hip": ["-fno-honor-nans"], "kmeans.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -18,6 +18,8 @@ namespace scope {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int CENTRE_MARK = 1 << 30;   // `nearest` bit: the point is a chosen centre
 
@@ -442,162 +444,6 @@ __global__ __launch_bounds__(256) void centroid_kernel(Geo g, const float* __res
   }
 }
 
-// ---------------------------------------------------------------------------
-// Assignment, bf16: MFMA filter + fp64 refinement.
-// Each wave takes 64 points as two 32-column tiles; the WG's 256 points share
-// the clustering's centroids in LDS.  v_mfma_f32_32x32x16_bf16 gives
-// dot(x, mu~_c) for 32 centroids x 32 points; dhat_c = ||mu~_c||^2 - 2 dot.
-// If the two smallest dhat of a point lie within the worst-case rounding
-// window of each other, the wave re-decides that point with exact fp64
-// distances (about 0.1-0.3% of the points on the synthetic workloads).
-// ---------------------------------------------------------------------------
-constexpr int ASG_PTS = 256;
-
-__global__ __launch_bounds__(256) void assign_bf16_kernel(const uint16_t* __restrict__ qr,
-                                                          const uint16_t* __restrict__ kr, Geo g,
-                                                          const uint16_t* __restrict__ cbf,
-                                                          const float* __restrict__ cnorm,
-                                                          int32_t* __restrict__ labels) {
-  const int m = blockIdx.y, bh = blockIdx.z;
-  const int N = g.N, d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m], Cpad = g.Cpad[m], dpad = g.dpad[m];
-  const int KB = dpad / 16, ldc = dpad + 8;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  uint16_t* sc = reinterpret_cast<uint16_t*>(smem_raw);
-  float* scn = reinterpret_cast<float*>(smem_raw + (size_t)Cpad * ldc * 2);
-  __shared__ float red[8];
-  __shared__ double xsh[4][128];   // one exact-refinement row per wave
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hi = lane >> 5, col = lane & 31;
-  const uint16_t* gc = cbf + ((size_t)bh * 4 + m) * g.CmaxPad * g.DPmax;
-  for (int idx = tid; idx < Cpad * (dpad / 8); idx += 256) {
-    const int r = idx / (dpad / 8), c8 = idx % (dpad / 8);
-    *reinterpret_cast<uint4*>(sc + r * ldc + c8 * 8) =
-        *reinterpret_cast<const uint4*>(gc + (size_t)r * g.DPmax + c8 * 8);
-  }
-  const float* gcn = cnorm + ((size_t)bh * 4 + m) * g.CmaxPad;
-  float mx = 0.f;
-  for (int idx = tid; idx < Cpad; idx += 256) {
-    const float v = gcn[idx];
-    scn[idx] = v;
-    if (idx < C) mx = fmaxf(mx, v);
-  }
-  mx = block_max<float, 256>(mx, red);   // also orders the LDS fills above
-  const float M = sqrtf(mx) * 1.0001f;
-
-  // point operands: tile t, k-block kb -> 8 bf16 channels kb*16 + hi*8 + 0..7.
-  // The points are staged through LDS in two halves of 128 (waves 0-1, then
-  // waves 2-3) with coalesced 4-byte channel-pair loads.
-  const uint16_t* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + off;
-  uint32_t* pt = reinterpret_cast<uint32_t*>(smem_raw + (size_t)Cpad * ldc * 2 + (size_t)Cpad * 4);
-  const int pld2 = (dpad + 8) / 2;   // point tile row stride in channel pairs
-  bf16x8_t b[2][8];
-  float xn2[2] = {0.f, 0.f};
-  int pts[2];
-  for (int half = 0; half < 2; ++half) {
-    const int p0 = blockIdx.x * ASG_PTS + half * 128;
-    for (int idx = tid; idx < 128 * (dpad / 2); idx += 256) {
-      const int r = idx / (dpad / 2), pr = idx % (dpad / 2), p = p0 + r;
-      pt[r * pld2 + pr] = (p < N && 2 * pr < dm) ? *reinterpret_cast<const uint32_t*>(X + (size_t)p * d + 2 * pr) : 0u;
-    }
-    __syncthreads();
-    if ((wv >> 1) == half) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r = (wv & 1) * 64 + t * 32 + col;
-        pts[t] = p0 + r;
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-          uint4 u = make_uint4(0, 0, 0, 0);
-          if (kb < KB) u = *reinterpret_cast<const uint4*>(pt + r * pld2 + kb * 8 + hi * 4);
-          b[t][kb] = *reinterpret_cast<bf16x8_t*>(&u);
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float f0 = __uint_as_float(w[j] << 16), f1 = __uint_as_float(w[j] & 0xFFFF0000u);
-            xn2[t] += f0 * f0 + f1 * f1;
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  float best[2] = {FLT_MAX, FLT_MAX}, second[2] = {FLT_MAX, FLT_MAX};
-  int bi[2] = {0, 0};
-  for (int cb = 0; cb < Cpad / 32; ++cb) {
-    f32x16_t acc0 = {}, acc1 = {};
-    const uint16_t* arow = sc + (cb * 32 + col) * ldc + hi * 8;
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      if (kb < KB) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + kb * 16);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[0][kb], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[1][kb], acc1, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int c = cb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-      const float cn = scn[c];
-      const float d0 = fmaf(-2.f, acc0[v], cn), d1 = fmaf(-2.f, acc1[v], cn);
-      if (d0 < best[0]) { second[0] = best[0]; best[0] = d0; bi[0] = c; }
-      else if (d0 < second[0]) second[0] = d0;
-      if (d1 < best[1]) { second[1] = best[1]; best[1] = d1; bi[1] = c; }
-      else if (d1 < second[1]) second[1] = d1;
-    }
-  }
-  const float gamma = (float)(dpad + 16) * 0x1p-23f;
-  int32_t* lab = labels + ((size_t)bh * 4 + m) * N;
-  double* xs = xsh[wv];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    // merge the two half-waves holding the same point
-    const float ob = __shfl_xor(best[t], 32), os = __shfl_xor(second[t], 32);
-    const int oi = __shfl_xor(bi[t], 32);
-    float bb, ss;
-    int ii;
-    if (best[t] < ob || (best[t] == ob && bi[t] < oi)) { bb = best[t]; ii = bi[t]; ss = fminf(second[t], ob); }
-    else { bb = ob; ii = oi; ss = fminf(os, best[t]); }
-    const float xn = sqrtf(xn2[t] + __shfl_xor(xn2[t], 32)) * 1.0001f;
-    const float eps = gamma * 2.f * xn * M + 0x1p-22f * (M * M + 2.f * xn * M);
-    const int p = pts[t];
-    if (hi == 0 && p < N) lab[p] = ii;
-    // near ties: the whole wave re-decides each such point with exact fp64
-    // distances to the bf16 centroids in LDS (difference form, ties to the lowest c)
-    uint64_t amb = __ballot(hi == 0 && p < N && ss - bb <= 4.f * eps);
-    while (amb) {
-      const int L = __ffsll((unsigned long long)amb) - 1;
-      amb &= amb - 1;
-      const int pp = __shfl(p, L);
-      for (int ch = lane; ch < dm; ch += 64) xs[ch] = (double)bf16_to_f32(X[(size_t)pp * d + ch]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      double bd = __builtin_inf();
-      int bc = 0x7FFFFFFF;
-      for (int c = lane; c < C; c += 64) {
-        const uint16_t* row = sc + c * ldc;
-        double acc = 0.0;
-        for (int ch = 0; ch < dm; ++ch) {
-          const double df = xs[ch] - (double)bf16_to_f32(row[ch]);
-          acc = fma(df, df, acc);
-        }
-        if (acc < bd) { bd = acc; bc = c; }
-      }
-#pragma unroll
-      for (int o2 = 32; o2 >= 1; o2 >>= 1) {
-        const double od = __shfl_xor(bd, o2);
-        const int oc = __shfl_xor(bc, o2);
-        if (od < bd || (od == bd && oc < bc)) { bd = od; bc = oc; }
-      }
-      if (lane == 0) lab[pp] = bc;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-  }
-}
-
 // Assignment, fp32 storage: exact fp64 distances to the fp32 centroids.
 __global__ __launch_bounds__(256) void assign_exact_f32_kernel(const float* __restrict__ qr, const float* __restrict__ kr,
                                                                Geo g, const float* __restrict__ qcent,
@@ -834,6 +680,202 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
   if (i < n) p[i] = v;
 }
 
+// ---------------------------------------------------------------------------
+// Lloyd assignment, bf16 data: persistent workgroups per (clustering, head),
+// each wave taking 64-point tiles (two 32-point MFMA column tiles).
+// The centroids sit in LDS as -2*mu (exact in bf16), so MFMA output + ||mu||^2
+// is ||x - mu||^2 - ||x||^2.  Each lane holds 16 candidates (centroid rows) of
+// one point per 32-centroid block; their element number 0..15 is written into
+// the low 4 mantissa bits, so min3 / med3 give the block's best and second best
+// together with the position of the best, and the block of the running best is
+// kept apart.
+// Error of a candidate value against the exact distance (up to the common
+// ||x||^2), M = max ||mu||: accumulation of the dpad products
+// <= dpad 2^-24 * 2 |x| M; rounding of ||mu||^2 and of the sum
+// <= 2^-23 (M^2 + 2 |x| M); the packed bits move a value v by < 2^-19 |v|.
+// EPS covers twice the first two; the packing is charged on the two values
+// compared.  A point whose best two candidates lie within that window is
+// re-decided with exact fp64 distances (ties to the lowest index), so the
+// labels equal the fp64 argmin.
+// ---------------------------------------------------------------------------
+constexpr int ASG_NT = 256;
+
+__device__ __forceinline__ float pack_pos(float x, int v) {
+  return __uint_as_float((__float_as_uint(x) & ~0xFu) | (uint32_t)v);
+}
+
+// 8 bf16 channels c0 .. c0+7 of a row (channels >= dm read as zero; dm even)
+__device__ __forceinline__ bf16x8_t load_row8(const uint16_t* __restrict__ row, int c0, int dm, bool vec16) {
+  u32x4_t u = {0u, 0u, 0u, 0u};
+  if (vec16 && c0 + 8 <= dm) {
+    u = *reinterpret_cast<const u32x4_t*>(row + c0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (c0 + 2 * j < dm) u[j] = *reinterpret_cast<const uint32_t*>(row + c0 + 2 * j);
+  }
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+template <int KB>
+__device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int N, int d, int dm, int C, int Cpad,
+                                             bool vec16, const uint16_t* __restrict__ sc, int ldc,
+                                             const float* __restrict__ scn, float M, double* __restrict__ xs,
+                                             int32_t* __restrict__ lab, int gw, int gstride) {
+  const int lane = threadIdx.x & 63, hi = lane >> 5, col = lane & 31;
+  const int ncb = Cpad / 32;
+  const float gamma = (float)(KB * 16 + 16) * 0x1p-23f;
+  const int ntiles = (N + 63) / 64;
+  for (int tile = gw; tile < ntiles; tile += gstride) {
+    bf16x8_t b[2][KB];
+    float xn2[2] = {0.f, 0.f};
+    int pts[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      pts[t] = tile * 64 + t * 32 + col;
+      const uint16_t* row = X + (size_t)min(pts[t], N - 1) * d;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        b[t][kb] = load_row8(row, kb * 16 + hi * 8, dm, vec16);
+        const u32x4_t u = __builtin_bit_cast(u32x4_t, b[t][kb]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, u[j]);
+          xn2[t] = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, xn2[t], false);
+        }
+      }
+    }
+    float best[2] = {FLT_MAX, FLT_MAX}, second[2] = {FLT_MAX, FLT_MAX};
+    int bcb[2] = {0, 0};
+    for (int cb = 0; cb < ncb; ++cb) {
+      f32x16_t cn;   // ||mu||^2 of rows cb*32 + 8*(v/4) + 4*hi + v%4
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 q = *reinterpret_cast<const float4*>(scn + cb * 32 + 8 * g4 + 4 * hi);
+        cn[4 * g4] = q.x; cn[4 * g4 + 1] = q.y; cn[4 * g4 + 2] = q.z; cn[4 * g4 + 3] = q.w;
+      }
+      const uint16_t* arow = sc + (cb * 32 + col) * ldc + hi * 8;
+      f32x16_t acc[2];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + kb * 16);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[t][kb], kb == 0 ? f32x16_t{} : acc[t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float kb1 = FLT_MAX, ks1 = FLT_MAX;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float x = pack_pos(acc[t][v] + cn[v], v), y = pack_pos(acc[t][v + 1] + cn[v + 1], v + 1);
+          ks1 = fminf(ks1, __builtin_amdgcn_fmed3f(kb1, x, y));
+          kb1 = fminf(kb1, fminf(x, y));
+        }
+        second[t] = fminf(fminf(second[t], ks1), fmaxf(best[t], kb1));
+        if (kb1 < best[t]) { best[t] = kb1; bcb[t] = cb; }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int v = (int)(__float_as_uint(best[t]) & 0xFu);
+      const int idx = bcb[t] * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+      // merge the two half-waves holding the same point
+      const float ob = __shfl_xor(best[t], 32), os = __shfl_xor(second[t], 32);
+      const int oi = __shfl_xor(idx, 32);
+      const bool mine = best[t] < ob || (best[t] == ob && idx < oi);
+      const int ii = mine ? idx : oi;
+      const float bb = fminf(best[t], ob);
+      const float ss = fminf(fminf(second[t], os), fmaxf(best[t], ob));
+      const float xn = sqrtf(xn2[t] + __shfl_xor(xn2[t], 32)) * 1.0001f;
+      const float eps = gamma * 2.f * xn * M + 0x1p-22f * (M * M + 2.f * xn * M);
+      const float window = 4.f * eps + 0x1p-18f * (fabsf(bb) + fabsf(ss));
+      const int p = pts[t];
+      if (hi == 0 && p < N) lab[p] = ii;
+      uint64_t amb = __ballot(hi == 0 && p < N && ss - bb <= window);
+      while (amb) {
+        const int L = __ffsll((unsigned long long)amb) - 1;
+        amb &= amb - 1;
+        const int pp = __shfl(p, L);
+        for (int ch = lane; ch < dm; ch += 64) xs[ch] = (double)bf16_to_f32(X[(size_t)pp * d + ch]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        double bd = __builtin_inf();
+        int bc = 0x7FFFFFFF;
+        for (int c = lane; c < C; c += 64) {
+          const uint16_t* row = sc + c * ldc;
+          double accd = 0.0;
+          for (int ch = 0; ch < dm; ++ch) {
+            // LDS holds -2 mu; mu = -0.5 * that, exactly
+            const double df = xs[ch] + 0.5 * (double)bf16_to_f32(row[ch]);
+            accd = fma(df, df, accd);
+          }
+          if (accd < bd) { bd = accd; bc = c; }
+        }
+#pragma unroll
+        for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+          const double od = __shfl_xor(bd, o2);
+          const int oc = __shfl_xor(bc, o2);
+          if (od < bd || (od == bd && oc < bc)) { bd = od; bc = oc; }
+        }
+        if (lane == 0) lab[pp] = bc;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(ASG_NT) void assign2_kernel(const uint16_t* __restrict__ qr,
+                                                         const uint16_t* __restrict__ kr, Geo g,
+                                                         const uint16_t* __restrict__ cbf,
+                                                         const float* __restrict__ cnorm,
+                                                         int32_t* __restrict__ labels) {
+  const int m = blockIdx.y, bh = blockIdx.z;
+  const int N = g.N, d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m], Cpad = g.Cpad[m], dpad = g.dpad[m];
+  const int ldc = dpad + 8;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  uint16_t* sc = reinterpret_cast<uint16_t*>(smem_raw);                               // [Cpad][ldc] -2 mu
+  float* scn = reinterpret_cast<float*>(smem_raw + (size_t)Cpad * ldc * 2);           // [Cpad] ||mu||^2
+  double* xsh = reinterpret_cast<double*>(smem_raw + (size_t)Cpad * ldc * 2 + (size_t)Cpad * 4);   // [4][128]
+  __shared__ float red[8];
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint16_t* gc = cbf + ((size_t)bh * 4 + m) * g.CmaxPad * g.DPmax;
+  for (int idx = tid; idx < Cpad * (dpad / 2); idx += ASG_NT) {
+    const int r = idx / (dpad / 2), c2 = idx % (dpad / 2);
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(gc + (size_t)r * g.DPmax + 2 * c2);
+    const float f0 = -2.f * __uint_as_float(u << 16), f1 = -2.f * __uint_as_float(u & 0xFFFF0000u);
+    // x -2 is exact in bf16: the fp32 products keep 8 significant bits
+    *reinterpret_cast<uint32_t*>(sc + r * ldc + 2 * c2) = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+  }
+  const float* gcn = cnorm + ((size_t)bh * 4 + m) * g.CmaxPad;
+  float mx = 0.f;
+  for (int idx = tid; idx < Cpad; idx += ASG_NT) {
+    const float v = gcn[idx];
+    scn[idx] = v;
+    if (idx < C) mx = fmaxf(mx, v);
+  }
+  mx = block_max<float, ASG_NT>(mx, red);   // also orders the LDS fills above
+  const float M = sqrtf(mx) * 1.0001f;
+  const uint16_t* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + off;
+  const bool vec16 = ((off * 2) % 16 == 0) && ((d * 2) % 16 == 0);
+  int32_t* lab = labels + ((size_t)bh * 4 + m) * N;
+  const int gw = blockIdx.x * (ASG_NT / 64) + wv, gstride = gridDim.x * (ASG_NT / 64);
+  double* xs = xsh + wv * 128;
+  switch (dpad / 16) {
+    case 1: assign_tiles<1>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
+    case 2: assign_tiles<2>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
+    case 3: assign_tiles<3>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
+    case 4: assign_tiles<4>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
+    case 5: assign_tiles<5>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
+    case 6: assign_tiles<6>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
+    case 7: assign_tiles<7>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
+    default: assign_tiles<8>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
+  }
+}
+
 // ---- launchers --------------------------------------------------------------
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {
@@ -873,14 +915,16 @@ hipError_t launch_prep(const Geo& g, const Workspace& w, hipStream_t s) {
 hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Workspace& w, int iter,
                          hipStream_t s) {
   if (g.bf16) {
-    int maxpad = 0;
-    for (int m = 0; m < 4; ++m)
-      maxpad = max(maxpad, g.Cpad[m] * (g.dpad[m] + 8) * 2 + g.Cpad[m] * 4 + 128 * (g.dpad[m] + 8) * 2);
-    dim3 grid((g.N + ASG_PTS - 1) / ASG_PTS, 4, g.BH);
-    if (maxpad > 64 * 1024)
-      (void)hipFuncSetAttribute((const void*)assign_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, maxpad);
-    assign_bf16_kernel<<<grid, 256, maxpad, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm,
-                                                w.labels);
+    int lds = 0;
+    for (int m = 0; m < 4; ++m) lds = max(lds, g.Cpad[m] * (g.dpad[m] + 8) * 2 + g.Cpad[m] * 4 + 4 * 128 * 8);
+    // about 2048 workgroups in all, at most one wave per 64-point tile
+    const int ntiles = (g.N + 63) / 64;
+    int parts = (2048 + 4 * g.BH - 1) / (4 * g.BH);
+    parts = max(1, min(parts, (ntiles + 3) / 4));
+    dim3 grid(parts, 4, g.BH);
+    if (lds > 64 * 1024)
+      (void)hipFuncSetAttribute((const void*)assign2_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    assign2_kernel<<<grid, ASG_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, w.labels);
   } else {
     dim3 grid((g.N + 255) / 256, 4, g.BH);
     assign_exact_f32_kernel<<<grid, 256, 0, s>>>((const float*)qr, (const float*)kr, g, w.qcent, w.kcent, w.labels);
