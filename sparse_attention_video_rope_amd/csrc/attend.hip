@@ -37,218 +37,30 @@ struct AttArgs {
   float scale;        // 1 / sqrt(d)
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a, const int32_t* __restrict__ work,
-                                                          const int32_t* __restrict__ status,
-                                                          const int32_t* __restrict__ perm_q,
-                                                          const int32_t* __restrict__ q_off,
-                                                          const int32_t* __restrict__ cr,
-                                                          const int64_t* __restrict__ sel_off,
-                                                          const int32_t* __restrict__ sel_idx,
-                                                          const uint16_t* __restrict__ qr,
-                                                          const uint16_t* __restrict__ kr,
-                                                          const uint16_t* __restrict__ vv,
-                                                          uint16_t* __restrict__ out) {
-  constexpr int BN = 64;                 // keys per chunk
-  constexpr int KLD = D + 8;             // K tile row stride (elements)
-  constexpr int VLD = BN + 4;            // V^T tile row stride (elements, 8-byte aligned rows)
-  constexpr int KPT = BN * D / 8 / 256;  // K 16-byte pieces per thread
-  constexpr int VPT = (BN / 2) * (D / 8) / 256;   // V key-pair pieces per thread
-  constexpr float RESCALE_LOG2 = 8.f;    // lazy rescale: p stays below 2^8
-  __shared__ __align__(16) uint16_t Ks[2][BN * KLD];
-  __shared__ __align__(16) uint16_t Vt[2][D * VLD];
-
-  if (status[1]) return;
-  const int item = att_item(status[0]);
-  if (item < 0) return;
-  const int cid = work[2 * item], chunk = work[2 * item + 1];
-  const int bh = cid / a.Cq, c = cid % a.Cq;
-  const int32_t* qo = q_off + (size_t)bh * (a.Cq + 1);
-  const int q0 = qo[c] + chunk * ATT_BM;
-  const int nq = min(ATT_BM, qo[c + 1] - q0);
-  const int r = cr[cid];
-  const int32_t* keys = sel_idx + sel_off[cid];
-  const size_t hb = (size_t)bh * a.N;
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, col = lane & 31, hi = lane >> 5;
-  const bool active = wv * 32 < nq;
-  const int qi = wv * 32 + col;
-  const bool qvalid = qi < nq;
-  const int tok = qvalid ? min(max(perm_q[hb + q0 + qi], 0), a.N - 1) : 0;
-
-  bf16x8_t qb[D / 16];
-  {
-    const uint16_t* qrow = qr + (hb + tok) * D + hi * 8;
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-      uint4 u = qvalid ? *reinterpret_cast<const uint4*>(qrow + kb * 16) : make_uint4(0, 0, 0, 0);
-      qb[kb] = *reinterpret_cast<bf16x8_t*>(&u);
-    }
-  }
-  f32x16_t o[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) o[t] = f32x16_t{};
-  float mref = -__builtin_inff(), lsum = 0.f;   // running max (raw logit units) used for the exponent
-  const float cs = a.scale_log2;
-
-  const int nchunks = (r + BN - 1) / BN;
-  // key indices come from the plan; clamp so a malformed plan cannot read out of bounds
-  auto key_at = [&](int i) -> size_t { const int j = keys[i]; return (size_t)min(max(j, 0), a.N - 1); };
-  uint4 kbuf[KPT], vb0[VPT], vb1[VPT];
-  auto gather = [&](int kc) {
-    const int nk = min(BN, r - kc * BN);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int piece = tid + i * 256;
-      const int row = piece / (D / 8), c8 = piece % (D / 8);
-      kbuf[i] = row < nk ? *reinterpret_cast<const uint4*>(kr + (hb + key_at(kc * BN + row)) * D + c8 * 8)
-                         : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      // V: one thread per (key pair, channel octet); the pair becomes 8 packed dwords of V^T
-      const int piece = tid + i * 256;
-      const int kp = piece % (BN / 2), oc = piece / (BN / 2);
-      const int r0 = 2 * kp;
-      vb0[i] = r0 < nk ? *reinterpret_cast<const uint4*>(vv + (hb + key_at(kc * BN + r0)) * D + oc * 8)
-                       : make_uint4(0, 0, 0, 0);
-      vb1[i] = r0 + 1 < nk ? *reinterpret_cast<const uint4*>(vv + (hb + key_at(kc * BN + r0 + 1)) * D + oc * 8)
-                           : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int piece = tid + i * 256;
-      const int row = piece / (D / 8), c8 = piece % (D / 8);
-      *reinterpret_cast<uint4*>(&Ks[buf][row * KLD + c8 * 8]) = kbuf[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int piece = tid + i * 256;
-      const int kp = piece % (BN / 2), oc = piece / (BN / 2);
-      const uint32_t w0[4] = {vb0[i].x, vb0[i].y, vb0[i].z, vb0[i].w};
-      const uint32_t w1[4] = {vb1[i].x, vb1[i].y, vb1[i].z, vb1[i].w};
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&Vt[buf][(oc * 8) * VLD + 2 * kp]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dst[(2 * j) * (VLD / 2)] = __builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u);      // channel 2j
-        dst[(2 * j + 1) * (VLD / 2)] = __builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u);  // channel 2j+1
-      }
-    }
-  };
-
-  if (nchunks > 0) { gather(0); stash(0); }
-  __syncthreads();
-  for (int kc = 0; kc < nchunks; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nchunks) gather(kc + 1);
-    if (active) {
-      f32x16_t s[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const uint16_t* arow = &Ks[buf][(st * 32 + col) * KLD + hi * 8];
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(arow), qb[0],
-                                                        f32x16_t{}, 0, 0, 0);
-#pragma unroll
-        for (int kb = 1; kb < D / 16; ++kb) {
-          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(arow + kb * 16);
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[kb], s[st], 0, 0, 0);
-        }
-      }
-      const int kleft = r - kc * BN;
-      if (kleft < BN) {
-        // partial last chunk: keys past the end get -inf
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (st * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kleft) s[st][v] = -__builtin_inff();
-      }
-      float mloc = -__builtin_inff();
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) mloc = fmaxf(mloc, fmaxf(s[st][v], s[st][v + 1]));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      // lazy rescale: move the reference max only when the new max exceeds it by 2^8
-      const bool grow = (mloc - mref) * cs > RESCALE_LOG2;
-      if (__ballot(grow)) {
-        const float mnew = grow ? mloc : mref;
-        const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * cs);
-        lsum *= alpha;
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
-        mref = mnew;
-      }
-      const float mc = mref * cs;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x2_t pk[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][half * 8 + 2 * i], cs, -mc));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][half * 8 + 2 * i + 1], cs, -mc));
-            lsum += p0 + p1;
-            pk[i] = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
-          }
-          const bf16x8_t bp = *reinterpret_cast<bf16x8_t*>(pk);
-          const int base = st * 32 + half * 16 + 4 * hi;
-#pragma unroll
-          for (int t = 0; t < D / 32; ++t) {
-            const uint16_t* vrow = &Vt[buf][(t * 32 + col) * VLD + base];
-            uint2 av[2];
-            av[0] = *reinterpret_cast<const uint2*>(vrow);
-            av[1] = *reinterpret_cast<const uint2*>(vrow + 8);
-            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<bf16x8_t*>(av), bp, o[t], 0, 0, 0);
-          }
-        }
-      }
-    }
-    if (kc + 1 < nchunks) stash(buf ^ 1);
-    __syncthreads();
-  }
-  if (!qvalid) return;
-  const float ltot = lsum + __shfl_xor(lsum, 32);
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  uint16_t* orow = out + (hb + tok) * D;
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      bf16x2_t e[2];
-      e[0] = __builtin_convertvector((f32x2_t){o[t][g4 * 4] * inv, o[t][g4 * 4 + 1] * inv}, bf16x2_t);
-      e[1] = __builtin_convertvector((f32x2_t){o[t][g4 * 4 + 2] * inv, o[t][g4 * 4 + 3] * inv}, bf16x2_t);
-      *reinterpret_cast<uint2*>(orow + t * 32 + 8 * g4 + 4 * hi) = *reinterpret_cast<uint2*>(e);
-    }
-  }
-}
-
-// bf16 path with two 32-query column tiles per wave (NW waves, 64*NW queries
-// per workgroup): every K / V^T operand read from LDS feeds two MFMAs, and the
+// bf16 path with TT 32-query column tiles per wave (NW waves, 32*TT*NW queries
+// per workgroup): every K / V^T operand read from LDS feeds TT MFMAs, and the
 // key indices of chunk kc+2 are loaded while chunk kc is computed.  Gathers
 // are unconditional: indices past r_c repeat the last selected key (those
 // logits are masked to -inf), so no lane needs a branch or a zero fill.  The
 // row sum is taken over the bf16-rounded probabilities that feed the P V
 // product (dot2 with (1, 1)), so the normalisation matches the weights used.
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attend_bf16_pair_kernel(
+template <int D, int NW, int TT, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) void attend_bf16_tiles_kernel(
     AttArgs a, const int32_t* __restrict__ work, const int32_t* __restrict__ status,
     const int32_t* __restrict__ perm_q, const int32_t* __restrict__ q_off, const int32_t* __restrict__ cr,
     const int64_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, const uint16_t* __restrict__ qr,
     const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vv, uint16_t* __restrict__ out) {
   constexpr int NTH = 64 * NW;
-  constexpr int BM = 64 * NW;
+  constexpr int BM = 32 * TT * NW;
+  static_assert(BM == ATT_BM, "queries per workgroup must equal the work-list chunk");
   constexpr int BN = 64;
   constexpr int KLD = D + 8;
   constexpr int VLD = BN + 4;
   constexpr int KPT = BN * D / 8 / NTH;            // K 16-byte pieces per thread
-  constexpr int VPT = (BN / 2) * (D / 8) / NTH;    // V key-pair pieces per thread
-  static_assert(KPT * NTH == BN * D / 8 && VPT * NTH == (BN / 2) * (D / 8), "gather split");
+  constexpr int VPIECES = (BN / 2) * (D / 8);       // V key-pair pieces per chunk
+  constexpr int VPT = (VPIECES + NTH - 1) / NTH;     // per thread (the last round may be partial)
+  static_assert(KPT * NTH == BN * D / 8, "gather split");
+  static_assert(VPIECES % 64 == 0, "V pieces per wave");
   constexpr int NIDX = KPT + 2 * VPT;              // key indices per thread per chunk
   constexpr float RESCALE_LOG2 = 8.f;
   __shared__ __align__(16) uint16_t Ks[2][BN * KLD];
@@ -269,13 +81,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const char* vbase = reinterpret_cast<const char*>(vv + hb * D);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, col = lane & 31, hi = lane >> 5;
-  const bool active = wv * 64 < nq;
-  int tok[2];
-  bool qvalid[2];
-  bf16x8_t qb[2][D / 16];
+  const bool active = wv * 32 * TT < nq;
+  int tok[TT];
+  bool qvalid[TT];
+  bf16x8_t qb[TT][D / 16];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int qi = wv * 64 + t * 32 + col;
+  for (int t = 0; t < TT; ++t) {
+    const int qi = wv * 32 * TT + t * 32 + col;
     qvalid[t] = qi < nq;
     tok[t] = qvalid[t] ? min(max(perm_q[hb + q0 + qi], 0), a.N - 1) : 0;
     const uint16_t* qrow = qr + (hb + tok[t]) * D + hi * 8;
@@ -285,12 +97,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       qb[t][kb] = *reinterpret_cast<bf16x8_t*>(&u);
     }
   }
-  f32x16_t o[2][D / 32];
+  f32x16_t o[TT][D / 32];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < TT; ++t)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) o[t][dt] = f32x16_t{};
-  float mref[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.f, 0.f};
+  float mref[TT], lsum[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) { mref[t] = -__builtin_inff(); lsum[t] = 0.f; }
   const float cs = a.scale_log2;
   const int nchunks = (r + BN - 1) / BN;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -298,7 +112,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // rows this thread gathers: K pieces i -> row (tid + i*NTH) / (D/8); V pairs i -> rows 2kp, 2kp+1
   auto row_of = [&](int i) -> int {
     if (i < KPT) return (tid + i * NTH) / (D / 8);
-    const int j = (i - KPT) >> 1, piece = tid + j * NTH;
+    const int j = (i - KPT) >> 1, piece = min(tid + j * NTH, VPIECES - 1);
     return 2 * (piece % (BN / 2)) + ((i - KPT) & 1);
   };
   // Raw key indices of a chunk, loaded one chunk ahead of their gather and left
@@ -320,7 +134,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int oc = (tid + i * NTH) / (BN / 2);
+      const int oc = min(tid + i * NTH, VPIECES - 1) / (BN / 2);
       vb0[i] = *reinterpret_cast<const u32x4_t*>(vbase + row_off(ix[KPT + 2 * i]) + oc * 16);
       vb1[i] = *reinterpret_cast<const u32x4_t*>(vbase + row_off(ix[KPT + 2 * i + 1]) + oc * 16);
     }
@@ -335,6 +149,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int piece = tid + i * NTH;
+      if (VPIECES % NTH != 0 && piece >= VPIECES) break;   // wave-uniform
       const int kp = piece % (BN / 2), oc = piece / (BN / 2);
       const uint32_t w0[4] = {vb0[i].x, vb0[i].y, vb0[i].z, vb0[i].w};
       const uint32_t w1[4] = {vb1[i].x, vb1[i].y, vb1[i].z, vb1[i].w};
@@ -367,7 +182,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       load_idx(min(kc + 2, nchunks - 1), kidx);
     }
     if (active) {
-      f32x16_t s[2][2];   // [query tile][key subtile]
+      f32x16_t s[TT][2];   // [query tile][key subtile]
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const uint16_t* arow = &Ks[buf][(st * 32 + col) * KLD + hi * 8];
@@ -375,7 +190,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int kb = 0; kb < D / 16; ++kb) ak[kb] = *reinterpret_cast<const bf16x8_t*>(arow + kb * 16);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < TT; ++t) {
           s[t][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], qb[t][0], f32x16_t{}, 0, 0, 0);
 #pragma unroll
           for (int kb = 1; kb < D / 16; ++kb)
@@ -385,16 +200,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       const int kleft = r - kc * BN;
       if (kleft < BN) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < TT; ++t)
 #pragma unroll
           for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
               if (st * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kleft) s[t][st][v] = -__builtin_inff();
       }
-      float mc[2];
+      float mc[TT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < TT; ++t) {
         float mloc = -__builtin_inff();
 #pragma unroll
         for (int st = 0; st < 2; ++st)
@@ -418,9 +233,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          bf16x8_t bp[2];
+          bf16x8_t bp[TT];
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int t = 0; t < TT; ++t) {
             bf16x2_t pk[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -440,7 +255,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
             av[1] = *reinterpret_cast<const uint2*>(vrow + 8);
             const bf16x8_t avv = *reinterpret_cast<bf16x8_t*>(av);
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < TT; ++t)
               o[t][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avv, bp[t], o[t][dt], 0, 0, 0);
           }
         }
@@ -450,7 +265,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     __syncthreads();
   }
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TT; ++t) {
     const float ltot = lsum[t] + __shfl_xor(lsum[t], 32);
     if (!qvalid[t]) continue;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
@@ -520,12 +335,15 @@ hipError_t launch_attend(const Geo& g, const scope_plan_t& plan, const void* qr,
   const unsigned grid = (unsigned)plan.work_capacity;
 #define SCOPE_ATT_ARGS a, plan.work, plan.status, plan.perm_q, plan.q_off, plan.counts_r, plan.sel_off, plan.sel_idx
   if (g.bf16) {
+    // 4 waves x 32 queries; head dim 64 fits 128 VGPRs (4 waves per SIMD)
     if (g.d == 64)
-      attend_bf16_pair_kernel<64, 4><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
-                                                          (const uint16_t*)v, (uint16_t*)out);
+      attend_bf16_tiles_kernel<64, 4, 1, 4><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr,
+                                                                 (const uint16_t*)kr, (const uint16_t*)v,
+                                                                 (uint16_t*)out);
     else
-      attend_bf16_kernel<128><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
-                                                   (const uint16_t*)v, (uint16_t*)out);
+      attend_bf16_tiles_kernel<128, 4, 1, 2><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr,
+                                                                  (const uint16_t*)kr, (const uint16_t*)v,
+                                                                  (uint16_t*)out);
   } else {
     if (g.d == 64)
       attend_f32_kernel<64><<<grid, ATT_BM, 0, s>>>(SCOPE_ATT_ARGS, (const float*)qr, (const float*)kr,

@@ -9,7 +9,7 @@
 
 namespace scope {
 
-constexpr int ATT_BM = 128;     // queries per attention work item (4 waves x 32, or the fp32 kernel)
+constexpr int ATT_BM = 128;     // queries per attention work item (4 waves x 32)
 constexpr int SEL_NB = 2048;    // histogram bins per level in the selection kernels
 constexpr int SEL_CAP = 2048;   // boundary candidates sorted in LDS
 constexpr int MAX_C = 1024;     // largest Cq / Cm supported
@@ -58,9 +58,8 @@ struct Workspace {
   size_t bytes;
 };
 
-// Queries per attention work item: the bf16 head-dim-64 kernel runs 4 waves of
-// 64 queries; the bf16 head-dim-128 and fp32 kernels run 128.
-inline int att_chunk(const Geo& g) { return (g.bf16 && g.d == 64) ? 256 : ATT_BM; }
+// Queries per attention work item (every kernel: 128).
+inline int att_chunk(const Geo&) { return ATT_BM; }
 // Lloyd update layout: channel slices of acc_sw channels, acc_parts point
 // ranges per (head, clustering).  Slices are 32 channels wide unless the
 // per-cluster sums of that width would not fit in LDS.

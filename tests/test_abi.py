@@ -64,8 +64,8 @@ def test_invalid_parameters(kw, code):
 def test_workspace_size_and_capacities():
     p = good()
     ws, sel, work = sav.sizes(p)
-    # work items: BH * (Cq + ceil(N / chunk)); chunk 256 queries for bf16 head dim 64, else 128
-    assert ws > 0 and sel == 2 * 8 * 256 and work == 2 * (8 + 1)
+    # work items: BH * (Cq + ceil(N / 128))
+    assert ws > 0 and sel == 2 * 8 * 256 and work == 2 * (8 + 2)
     assert sav.sizes(good(dtype="f32"))[2] == 2 * (8 + 2)
     assert sav.sizes(good(d=128, split=(44, 42, 42)))[2] == 2 * (8 + 2)
     # monotone in the token count
