@@ -415,6 +415,253 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
 }
 
 // ---------------------------------------------------------------------------
+// k-means++ seeding with the point state in registers (N <= SR_NT * SR_PMAX).
+// Same draw rule as seed_kernel (index-order running sum of D^2).
+// Thread t owns the P consecutive points t P .. t P + P - 1, so (thread, slot)
+// is the index order.  Per draw:
+//   1. a block scan of the per-thread D^2 sums finds the crossing thread,
+//      which walks its own slots to the point;
+//   2. the centre row is staged in LDS; 3. its distances to the earlier
+//      centres are computed by all waves (lanes = channels);
+//   4. the Elkan test (||c_s - a||^2 >= 4 D^2 means no change) leaves the
+//      points whose distance is needed; a block scan of the per-thread counts
+//      orders them into one list, all threads compute the distances (lpr lanes
+//      per row, 8 row loads in flight per lane), and the owners apply them.
+// ---------------------------------------------------------------------------
+constexpr int SR_NT = 512;
+constexpr int SR_PMAX = 36;          // points per thread held in registers
+constexpr int SR_LIST = 4096;        // list entries per compute round
+constexpr int SR_CACHE_BYTES = 48 * 1024;
+
+// squared distance over 8 channels c0 .. c0+7 of a row (channels >= dm count 0)
+template <typename T>
+__device__ __forceinline__ double sqdist8(const T* __restrict__ row, const double* __restrict__ c, int c0, int dm) {
+  double acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (c0 + j < dm) {
+      const double df = Elem<T>::ld(row + c0 + j) - c[c0 + j];
+      acc = fma(df, df, acc);
+    }
+  }
+  return acc;
+}
+__device__ __forceinline__ double sqdist8v(u32x4_t u, const double* __restrict__ c) {
+  double acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double d0 = (double)__uint_as_float(u[j] << 16) - c[2 * j];
+    const double d1 = (double)__uint_as_float(u[j] & 0xFFFF0000u) - c[2 * j + 1];
+    acc = fma(d0, d0, acc);
+    acc = fma(d1, d1, acc);
+  }
+  return acc;
+}
+
+template <typename T, int PM>
+__global__ __launch_bounds__(SR_NT) void seedr_kernel(const T* __restrict__ qr, const T* __restrict__ kr, Geo g,
+                                                      int32_t* __restrict__ seeds, float* __restrict__ qcent,
+                                                      float* __restrict__ kcent) {
+  const int m = blockIdx.y, bh = blockIdx.x;
+  const int N = g.N, d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m];
+  const T* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + off;
+  int32_t* sd = seeds + ((size_t)bh * 4 + m) * g.Cmax;
+
+  __shared__ double cvec[128];
+  __shared__ double cc[MAX_C];
+  __shared__ int32_t chosen[MAX_C];
+  __shared__ double dtmp[SR_NT / 64 + 1];
+  __shared__ int32_t itmp[SR_NT / 64 + 1];
+  __shared__ int32_t sh_ci, sh_lo, sh_hi;
+  extern __shared__ __align__(16) unsigned char seedr_smem[];
+  int32_t* list = reinterpret_cast<int32_t*>(seedr_smem);                                // [SR_LIST]
+  double* ldist = reinterpret_cast<double*>(seedr_smem + SR_LIST * 4);                    // [SR_LIST]
+  T* cache = reinterpret_cast<T*>(seedr_smem + SR_LIST * 12);                             // [C][cld]
+  const int cld = dm + 2;
+  const bool cached = (size_t)C * cld * sizeof(T) <= SR_CACHE_BYTES;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = (N + SR_NT - 1) / SR_NT;          // slots per thread (<= PM)
+  // 16-byte row pieces: bf16 rows 16-byte aligned and the range a multiple of 8 channels
+  const bool vecrow = sizeof(T) == 2 && ((off * 2) % 16 == 0) && ((d * 2) % 16 == 0) && (dm % 8 == 0);
+  int lpr = 1;
+  while (lpr * 8 < dm) lpr <<= 1;
+  const uint64_t stream = ((uint64_t)bh * 4 + m) << 20;
+
+  double d2[PM];
+  // nearest centre of slot k (bits 0..14) | 0x8000 if the point is a chosen centre; two ids per word
+  uint32_t nrw[(PM + 1) / 2];
+#pragma unroll
+  for (int k = 0; k < PM; ++k) d2[k] = 0.0;
+#pragma unroll
+  for (int k = 0; k < (PM + 1) / 2; ++k) nrw[k] = NR_MARK | (NR_MARK << 16);
+  auto nr_get = [&](int k) -> uint32_t { return (nrw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu; };
+  auto nr_set = [&](int k, uint32_t v) {
+    nrw[k >> 1] = (nrw[k >> 1] & ~(0xFFFFu << (16 * (k & 1)))) | (v << (16 * (k & 1)));
+  };
+  const int p0 = tid * P;
+  auto valid = [&](int k) { return k < P && p0 + k < N; };
+
+  int ci = 0;
+  for (int s = 0; s < C; ++s) {
+    // ---- 1. centre s -------------------------------------------------------------
+    if (s == 0) {
+      const uint64_t k0 = splitmix64(g.seed, stream) >> 11;
+      const uint64_t lo = k0 * (uint64_t)N, hi = __umul64hi(k0, (uint64_t)N);
+      ci = (int)((hi << 11) | (lo >> 53));
+    } else {
+      double loc = 0.0;
+#pragma unroll
+      for (int k = 0; k < PM; ++k) loc += valid(k) ? d2[k] : 0.0;
+      double total;
+      const double incl = block_incl_scan<double, SR_NT>(loc, dtmp, &total);
+      const uint64_t ku = splitmix64(g.seed, stream + (uint64_t)s) >> 11;
+      const double target = ((double)ku * 0x1p-53) * total;
+      const int mode = total > 0.0 ? 0 : 2;   // 0 draw, 1 rounding at the end, 2 all zero
+      if (tid == 0) { sh_ci = -1; sh_lo = 0x7FFFFFFF; sh_hi = -1; }
+      __syncthreads();
+      if (mode == 0) {
+        const double excl = incl - loc;
+        if (excl <= target && incl > target) {   // exactly one thread, unless rounding left no crossing
+          double run = excl;
+          int pick = -1;
+#pragma unroll
+          for (int k = 0; k < PM; ++k) {
+            if (pick < 0 && valid(k)) { run += d2[k]; if (run > target) pick = k; }
+          }
+          if (pick < 0) {   // rounding inside the thread: its last slot with weight
+#pragma unroll
+            for (int k = 0; k < PM; ++k) if (valid(k) && d2[k] > 0.0) pick = k;
+          }
+          sh_ci = p0 + max(pick, 0);
+        }
+      } else {
+        int low = 0x7FFFFFFF;
+#pragma unroll
+        for (int k = PM - 1; k >= 0; --k) if (valid(k) && !(nr_get(k) & NR_MARK)) low = p0 + k;
+        if (low != 0x7FFFFFFF) atomicMin(&sh_lo, low);
+      }
+      __syncthreads();
+      if (mode == 0 && sh_ci < 0) {
+        // no crossing (u * total rounded up to total): the last point with D^2 > 0
+        int best = -1;
+#pragma unroll
+        for (int k = 0; k < PM; ++k) if (valid(k) && d2[k] > 0.0) best = p0 + k;
+        if (best >= 0) atomicMax(&sh_hi, best);
+        __syncthreads();
+        ci = sh_hi;
+      } else {
+        ci = mode == 0 ? sh_ci : sh_lo;
+      }
+      if (ci < 0 || ci >= N) ci = 0;
+    }
+    // ---- 2. centre row ---------------------------------------------------------------
+    if (tid == 0) { chosen[s] = ci; sd[s] = ci; }
+    if (tid < dm) {
+      const T xv = X[(size_t)ci * d + tid];
+      cvec[tid] = Elem<T>::ld(&xv);
+      if (cached) cache[(size_t)s * cld + tid] = xv;
+    }
+    __syncthreads();
+    // ---- 3. distances to the earlier centres (one centre per wave step, lanes = channels)
+    for (int a = wv; a < s; a += SR_NT / 64) {
+      double t = 0.0;
+      for (int ch = lane; ch < dm; ch += 64) {
+        const double xa = cached ? Elem<T>::ld(cache + (size_t)a * cld + ch) : Elem<T>::ld(X + (size_t)chosen[a] * d + ch);
+        const double df = xa - cvec[ch];
+        t = fma(df, df, t);
+      }
+      t = wave_sum_dpp(t);
+      if (lane == 0) cc[a] = t;
+    }
+    __syncthreads();
+    // ---- 4. points whose D^2 may change ------------------------------------------------
+    static_assert(PM <= 64, "one need bit per slot");
+    uint64_t need = 0;
+#pragma unroll
+    for (int k = 0; k < PM; ++k) {
+      const bool nd = valid(k) && (s == 0 || !(cc[nr_get(k) & NR_ID] * (1.0 - 1e-9) >= 4.0 * d2[k]));
+      need |= (uint64_t)nd << k;
+    }
+    const int cnt = __popcll(need);
+    int K;
+    const int o_t = block_incl_scan<int, SR_NT>(cnt, itmp, &K) - cnt;   // first list position of this thread
+    for (int base = 0; base < K; base += SR_LIST) {
+      if (o_t + cnt > base && o_t < base + SR_LIST) {
+#pragma unroll
+        for (int k = 0; k < PM; ++k) {
+          if ((need >> k) & 1ull) {
+            const int pos = o_t + __popcll(need & ((1ull << k) - 1ull));
+            if (pos >= base && pos < base + SR_LIST) list[pos - base] = p0 + k;
+          }
+        }
+      }
+      __syncthreads();
+      const int nl = min(SR_LIST, K - base);
+      {
+        const int sub = tid & (lpr - 1), slot = tid / lpr, nslot = SR_NT / lpr;
+        const bool lv = sub * 8 < dm;
+        const int c0 = lv ? sub * 8 : 0;
+        for (int e0 = slot; e0 < nl; e0 += 8 * nslot) {
+          double acc[8];
+          if (vecrow) {
+            u32x4_t b[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int e = min(e0 + u * nslot, nl - 1);
+              b[u] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(X) + (size_t)list[e] * d + c0);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u] = sqdist8v(b[u], cvec + c0);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int e = min(e0 + u * nslot, nl - 1);
+              acc[u] = sqdist8<T>(X + (size_t)list[e] * d, cvec, c0, dm);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const double a2 = group_sum_dpp(lv ? acc[u] : 0.0, lpr);
+            const int e = e0 + u * nslot;
+            if (sub == 0 && e < nl) ldist[e] = a2;
+          }
+        }
+      }
+      __syncthreads();
+      if (o_t + cnt > base && o_t < base + SR_LIST) {
+#pragma unroll
+        for (int k = 0; k < PM; ++k) {
+          if ((need >> k) & 1ull) {
+            const int pos = o_t + __popcll(need & ((1ull << k) - 1ull));
+            if (pos >= base && pos < base + SR_LIST) {
+              const double dist = ldist[pos - base];
+              if (s == 0 || dist < d2[k]) {
+                d2[k] = dist;
+                nr_set(k, s == 0 ? 0u : ((uint32_t)s | (nr_get(k) & NR_MARK)));
+              }
+            }
+          }
+        }
+      }
+      if (base + SR_LIST < K) __syncthreads();   // the list is rewritten in the next round
+    }
+    // the chosen point is a centre
+    if (ci >= p0 && ci < p0 + P) {
+#pragma unroll
+      for (int k = 0; k < PM; ++k) if (p0 + k == ci) nr_set(k, nr_get(k) | NR_MARK);
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < C * dm; idx += SR_NT) {
+    const int c = idx / dm, ch = idx % dm;
+    const float val = Elem<T>::ldf(X + (size_t)chosen[c] * d + ch);
+    if (m == 0) qcent[((size_t)bh * g.Cq + c) * d + ch] = val;
+    else kcent[((size_t)bh * g.Cm + c) * d + off + ch] = val;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // bf16 copies of the fp32 centroids (zero padded to [Cpad][dpad]) and their
 // squared norms (FLT_MAX on padding rows, so padding never wins).
 // ---------------------------------------------------------------------------
@@ -891,14 +1138,30 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
     const size_t b = (size_t)g.C[m] * (g.dm[m] + 2) * sizeof(T);
     if (b <= (size_t)SEED_CACHE_BYTES && b > cache) cache = b;
   }
+  const int P = (g.N + SR_NT - 1) / SR_NT;
+  if (P <= SR_PMAX) {
+    size_t rcache = 0;
+    for (int m = 0; m < 4; ++m) {
+      const size_t b = (size_t)g.C[m] * (g.dm[m] + 2) * sizeof(T);
+      if (b <= (size_t)SR_CACHE_BYTES && b > rcache) rcache = b;
+    }
+    const size_t rlds = (size_t)SR_LIST * 12 + rcache;
+    auto gor = [&](auto kern) {
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rlds);
+      kern<<<grid, SR_NT, rlds, s>>>(qr, kr, g, w.seeds, w.qcent, w.kcent);
+    };
+    if (P <= 8) gor(seedr_kernel<T, 8>);
+    else if (P <= 16) gor(seedr_kernel<T, 16>);
+    else if (P <= 24) gor(seedr_kernel<T, 24>);
+    else gor(seedr_kernel<T, SR_PMAX>);
+    return;
+  }
   const size_t lds = (size_t)SEED_NW * SEED_LIST * 12 + cache;
-  const bool resident = (g.N + SEED_NT - 1) / SEED_NT <= SEED_RG;
   auto go = [&](auto kern) {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     kern<<<grid, SEED_NT, lds, s>>>(qr, kr, g, w.d2, (uint16_t*)w.nearest, w.seeds, w.qcent, w.kcent);
   };
-  if (resident) go(seed_kernel<T, true>);
-  else go(seed_kernel<T, false>);
+  go(seed_kernel<T, false>);
 }
 
 hipError_t launch_seed(const Geo& g, const void* qr, const void* kr, const Workspace& w, hipStream_t s) {
