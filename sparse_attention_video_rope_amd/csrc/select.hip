@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void lut_kernel(Geo g, const float* __restrict
 // ---------------------------------------------------------------------------
 // Shared machinery of the selection kernels
 // ---------------------------------------------------------------------------
-constexpr int NT = 256;
+constexpr int NT = 512;
 constexpr int BPT = SEL_NB / NT;      // histogram bins per thread in a walk
 
 struct SelArgs {
@@ -77,6 +77,18 @@ __device__ __forceinline__ double bin_x(const Sel& S, double s) { return (S.smax
 __device__ __forceinline__ int bin1_of(double x) { return min(max((int)x, 0), SEL_NB - 1); }
 __device__ __forceinline__ int bin2_of(double x, int b1) {
   return min(max((int)((x - (double)b1) * SEL_NB), 0), SEL_NB - 1);
+}
+
+// f(j, codes[j]) for the keys j = threadIdx.x + k NT, four code loads in flight
+template <typename F>
+__device__ __forceinline__ void each_key(const Sel& S, F&& f) {
+  const int N = S.N;
+  int j = threadIdx.x;
+  for (; j + 3 * NT < N; j += 4 * NT) {
+    const ushort4 z0 = S.codes[j], z1 = S.codes[j + NT], z2 = S.codes[j + 2 * NT], z3 = S.codes[j + 3 * NT];
+    f(j, z0); f(j + NT, z1); f(j + 2 * NT, z2); f(j + 3 * NT, z3);
+  }
+  for (; j < N; j += NT) f(j, S.codes[j]);
 }
 
 struct SelSmem {
@@ -147,32 +159,42 @@ struct Boundary {
   int count;
 };
 
-__device__ Boundary find_boundary(const Sel& S, const SelSmem& sm, bool by_mass, uint64_t tgt) {
+// by_mass with rho > 0: the target is ceil(rho * total mass), the total (returned
+// in *zmass) taken from the level-1 histogram (integer sums, exact).
+__device__ Boundary find_boundary(const Sel& S, const SelSmem& sm, bool by_mass, uint64_t tgt, double rho = 0.0,
+                                  uint64_t* zmass = nullptr) {
   const int tid = threadIdx.x, N = S.N;
   // ---- level 1 ------------------------------------------------------------
   for (int b = tid; b < SEL_NB; b += NT) { sm.hc[b] = 0; sm.hm[b] = 0; }
   __syncthreads();
-  for (int j = tid; j < N; j += NT) {
-    const ushort4 z = S.codes[j];
+  each_key(S, [&](int, ushort4 z) {
     const int b1 = bin1_of(bin_x(S, logit(S, z)));
     atomicAdd(&sm.hc[b1], 1);
     if (by_mass) atomicAdd((unsigned long long*)&sm.hm[b1], (unsigned long long)weight_fx(S, z));
-  }
+  });
   __syncthreads();
+  if (by_mass && rho > 0.0) {
+    uint64_t zl = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) zl += sm.hm[tid * BPT + i];
+    const uint64_t z = block_sum<uint64_t, NT>(zl, sm.u64tmp);
+    tgt = (uint64_t)ceil(rho * (double)z);
+    tgt = tgt > z ? z : (tgt < 1 ? 1 : tgt);
+    if (zmass) *zmass = z;
+  }
   uint64_t bm;
   int64_t bc;
   const int B1 = hist_walk(sm, by_mass, tgt, 0, 0, &bm, &bc);
   // ---- level 2 ------------------------------------------------------------
   for (int b = tid; b < SEL_NB; b += NT) { sm.hc[b] = 0; sm.hm[b] = 0; }
   __syncthreads();
-  for (int j = tid; j < N; j += NT) {
-    const ushort4 z = S.codes[j];
+  each_key(S, [&](int, ushort4 z) {
     const double x = bin_x(S, logit(S, z));
-    if (bin1_of(x) != B1) continue;
+    if (bin1_of(x) != B1) return;
     const int b2 = bin2_of(x, B1);
     atomicAdd(&sm.hc[b2], 1);
     if (by_mass) atomicAdd((unsigned long long*)&sm.hm[b2], (unsigned long long)weight_fx(S, z));
-  }
+  });
   __syncthreads();
   const int B2 = hist_walk(sm, by_mass, tgt, bm, bc, &bm, &bc);
   const int ncand = sm.hc[B2];
@@ -181,16 +203,15 @@ __device__ Boundary find_boundary(const Sel& S, const SelSmem& sm, bool by_mass,
     // ---- exact resolution: sort the boundary bin by (s desc, j asc) --------
     if (tid == 0) sm.misc[1] = 0;
     __syncthreads();
-    for (int j = tid; j < N; j += NT) {
-      const ushort4 z = S.codes[j];
+    each_key(S, [&](int j, ushort4 z) {
       const double s = logit(S, z);
       const double x = bin_x(S, s);
-      if (bin1_of(x) != B1 || bin2_of(x, B1) != B2) continue;
+      if (bin1_of(x) != B1 || bin2_of(x, B1) != B2) return;
       const int k = atomicAdd(&sm.misc[1], 1);
       sm.cs[k] = s;
       sm.cj[k] = j;
       sm.cw[k] = by_mass ? weight_fx(S, z) : 0;
-    }
+    });
     __syncthreads();
     int P2 = 1;
     while (P2 < ncand) P2 <<= 1;
@@ -329,11 +350,11 @@ __device__ void setup_cluster(Sel& S, const SelArgs& a, const double* lutrow, co
   S.inv_sqrt_d = a.inv_sqrt_d;
   S.fx = a.fx_scale;
   double smax = -__builtin_inf(), smin = __builtin_inf();
-  for (int j = tid; j < a.N; j += NT) {
-    const double s = logit(S, codes[j]);
+  each_key(S, [&](int, ushort4 z) {
+    const double s = logit(S, z);
     smax = fmax(smax, s);
     smin = fmin(smin, s);
-  }
+  });
   S.smax = block_max<double, NT>(smax, sm.dtmp);
   const double lo = block_min<double, NT>(smin, sm.dtmp);
   S.scale1 = S.smax > lo ? (double)SEL_NB / (S.smax - lo) : 0.0;
@@ -403,11 +424,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(SelArgs a, const double* __res
     st.zfx = 0;
   } else {
     uint64_t z = 0;
-    for (int j = tid; j < a.N; j += NT) z += weight_fx(S, S.codes[j]);
-    z = block_sum<uint64_t, NT>(z, sm.u64tmp);
-    uint64_t tgt = (uint64_t)ceil(a.rho * (double)z);
-    tgt = tgt > z ? z : (tgt < 1 ? 1 : tgt);
-    const Boundary b = find_boundary(S, sm, true, tgt);
+    const Boundary b = find_boundary(S, sm, true, 0, a.rho, &z);
     t = b.count;
     st.all = t >= a.N;
     st.tau = b.tau;
