@@ -119,9 +119,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   // untouched until then: vmcnt retires loads in order, so any arithmetic on
   // them here would make the wave wait for the row gathers issued before them.
   int kidx[NIDX];
+  const char* keyb = reinterpret_cast<const char*>(keys);   // uniform base, 32-bit byte offsets
   auto load_idx = [&](int kc, int* dst) {
 #pragma unroll
-    for (int i = 0; i < NIDX; ++i) dst[i] = keys[min(kc * BN + row_of(i), r - 1)];
+    for (int i = 0; i < NIDX; ++i)
+      dst[i] = *reinterpret_cast<const int*>(keyb + (uint32_t)min(kc * BN + row_of(i), r - 1) * 4u);
   };
   // byte offset of a gathered row inside the head (index clamped to [0, N))
   auto row_off = [&](int j) -> uint32_t { return (uint32_t)min(max(j, 0), a.N - 1) * (uint32_t)(D * 2); };
@@ -130,13 +132,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c8 = (tid + i * NTH) % (D / 8);
-      kbuf[i] = *reinterpret_cast<const u32x4_t*>(kbase + row_off(ix[i]) + c8 * 16);
+      kbuf[i] = *reinterpret_cast<const u32x4_t*>(kbase + (row_off(ix[i]) + (uint32_t)(c8 * 16)));
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int oc = min(tid + i * NTH, VPIECES - 1) / (BN / 2);
-      vb0[i] = *reinterpret_cast<const u32x4_t*>(vbase + row_off(ix[KPT + 2 * i]) + oc * 16);
-      vb1[i] = *reinterpret_cast<const u32x4_t*>(vbase + row_off(ix[KPT + 2 * i + 1]) + oc * 16);
+      vb0[i] = *reinterpret_cast<const u32x4_t*>(vbase + (row_off(ix[KPT + 2 * i]) + (uint32_t)(oc * 16)));
+      vb1[i] = *reinterpret_cast<const u32x4_t*>(vbase + (row_off(ix[KPT + 2 * i + 1]) + (uint32_t)(oc * 16)));
     }
   };
   auto stash = [&](int buf) {
@@ -210,11 +212,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
       float mc[TT];
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
-        float mloc = -__builtin_inff();
+        // max3 chain over the 32 logits of this lane
+        float mloc = fmaxf(s[t][0][0], s[t][0][1]);
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int v = 0; v < 16; v += 2) mloc = fmaxf(mloc, fmaxf(s[t][st][v], s[t][st][v + 1]));
+        for (int e = 2; e < 32; e += 2)
+          mloc = fmaxf(fmaxf(mloc, s[t][e >> 4][e & 15]), s[t][e >> 4][(e + 1) & 15]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
         const bool grow = (mloc - mref[t]) * cs > RESCALE_LOG2;
         if (__ballot(grow)) {
