@@ -662,6 +662,253 @@ __global__ __launch_bounds__(SR_NT) void seedr_kernel(const T* __restrict__ qr, 
 }
 
 // ---------------------------------------------------------------------------
+// k-means++ seeding for bf16 data with the point state in LDS (1024 threads).
+// Same draw rule as seed_kernel.  Thread t owns the P consecutive points
+// t P .. t P + P - 1 ((thread, slot) is the index order).  The exact fp64 D^2
+// of every point lives in global memory; LDS holds an fp32 copy for the
+// pruning test (with a margin that covers its rounding), the 16-bit nearest
+// centre ids, and each thread's exact D^2 sum.  Per draw: a block scan of the
+// per-thread sums finds the crossing thread, which reads its exact values to
+// find the point; the centre's distances to the earlier centres are computed
+// by all waves; the points the Elkan test keeps are listed in index order (a
+// scan of per-thread counts) and all threads compute their exact distances;
+// the thread that computes a distance applies it: it replaces the exact D^2
+// (global) when smaller, refreshes the LDS copies and adds the exact
+// difference to the owner's sum (fp64 LDS atomics; sums of bf16-derived D^2
+// are exact, so their order does not matter).
+// ---------------------------------------------------------------------------
+constexpr int SL_NT = 1024;
+constexpr int SL_LIST = 4096;
+constexpr int SL_LDS_LIMIT = 160 * 1024;
+
+struct SeedLLayout {
+  size_t d2s, nrs, list, tsum, cc, chosen, cache, bytes;
+  bool cached;
+};
+__host__ __device__ inline SeedLLayout seedl_layout(int N, int C, int dm) {
+  SeedLLayout L;
+  const int P = (N + SL_NT - 1) / SL_NT;
+  size_t o = 0;
+  auto take = [&](size_t b) { const size_t r = o; o += (b + 15) & ~(size_t)15; return r; };
+  L.d2s = take((size_t)4 * SL_NT * P);
+  L.nrs = take((size_t)2 * SL_NT * P);
+  L.list = take((size_t)4 * (SL_LIST + 1));
+  L.tsum = take((size_t)8 * SL_NT);
+  L.cc = take((size_t)8 * C);
+  L.chosen = take((size_t)4 * C);
+  const size_t base = o;
+  L.cache = take((size_t)2 * C * (dm + 2));
+  L.cached = o <= (size_t)SL_LDS_LIMIT - 2048;   // room left for the static LDS
+  if (!L.cached) o = base;
+  L.bytes = o;
+  return L;
+}
+
+__global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
+                                                      Geo g, double* __restrict__ d2all, int32_t* __restrict__ seeds,
+                                                      float* __restrict__ qcent, float* __restrict__ kcent) {
+  const int m = blockIdx.y, bh = blockIdx.x;
+  const int N = g.N, d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m];
+  const uint16_t* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + off;
+  double* D2g = d2all + ((size_t)bh * 4 + m) * N;
+  int32_t* sd = seeds + ((size_t)bh * 4 + m) * g.Cmax;
+  const SeedLLayout L = seedl_layout(N, C, dm);
+  extern __shared__ __align__(16) unsigned char seedl_smem[];
+  float* d2s = reinterpret_cast<float*>(seedl_smem + L.d2s);           // [P][NT] slot-major
+  uint16_t* nrs = reinterpret_cast<uint16_t*>(seedl_smem + L.nrs);     // [P][NT]
+  int32_t* list = reinterpret_cast<int32_t*>(seedl_smem + L.list);     // [SL_LIST + 1]
+  double* tsum = reinterpret_cast<double*>(seedl_smem + L.tsum);       // [NT]
+  double* cc = reinterpret_cast<double*>(seedl_smem + L.cc);           // [C]
+  int32_t* chosen = reinterpret_cast<int32_t*>(seedl_smem + L.chosen); // [C]
+  uint16_t* cache = reinterpret_cast<uint16_t*>(seedl_smem + L.cache); // [C][cld]
+  __shared__ double cvec[128];
+  __shared__ double dtmp[SL_NT / 64 + 1];
+  __shared__ int32_t itmp[SL_NT / 64 + 1];
+  __shared__ int32_t sh_ci, sh_lo, sh_hi;
+  const int cld = dm + 2;
+  const bool cached = L.cached;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = (N + SL_NT - 1) / SL_NT;
+  const int p0 = tid * P;
+  const bool vecrow = ((off * 2) % 16 == 0) && ((d * 2) % 16 == 0) && (dm % 8 == 0);
+  int lpr = 1;
+  while (lpr * 8 < dm) lpr <<= 1;
+  const uint64_t stream = ((uint64_t)bh * 4 + m) << 20;
+
+  for (int i = tid; i < SL_NT * P; i += SL_NT) { d2s[i] = 0.f; nrs[i] = (uint16_t)NR_MARK; }
+  tsum[tid] = 0.0;
+  __syncthreads();
+
+  int ci = 0;
+  for (int s = 0; s < C; ++s) {
+    // ---- 1. centre s -------------------------------------------------------------
+    if (s == 0) {
+      const uint64_t k0 = splitmix64(g.seed, stream) >> 11;
+      const uint64_t lo = k0 * (uint64_t)N, hi = __umul64hi(k0, (uint64_t)N);
+      ci = (int)((hi << 11) | (lo >> 53));
+    } else {
+      const double loc = tsum[tid];
+      double total;
+      const double incl = block_incl_scan<double, SL_NT>(loc, dtmp, &total);
+      const uint64_t ku = splitmix64(g.seed, stream + (uint64_t)s) >> 11;
+      const double target = ((double)ku * 0x1p-53) * total;
+      if (tid == 0) { sh_ci = -1; sh_lo = 0x7FFFFFFF; sh_hi = -1; }
+      __syncthreads();
+      if (total > 0.0) {
+        const double excl = incl - loc;
+        // the crossing thread's wave reads its P exact values (one per lane) and scans them
+        const uint64_t cross = __ballot(excl <= target && incl > target);
+        if (cross) {
+          const int L = __ffsll((unsigned long long)cross) - 1;
+          const double ex = __shfl(excl, L);
+          const int q0 = (wv * 64 + L) * P;
+          const int p = q0 + lane;
+          const double v = (lane < P && p < N) ? D2g[p] : 0.0;
+          const double inc = ex + wave_incl_scan(v);
+          const uint64_t hit = __ballot(lane < P && p < N && inc > target);
+          const uint64_t pos = __ballot(v > 0.0);
+          const int k = hit ? __ffsll((unsigned long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+          if (lane == 0) sh_ci = q0 + k;
+        }
+        __syncthreads();
+        if (sh_ci < 0) {
+          // no crossing (u * total rounded up to total): the last point with D^2 > 0
+          int best = -1;
+          for (int k = 0; k < P; ++k) { const int p = p0 + k; if (p < N && D2g[p] > 0.0) best = p; }
+          if (best >= 0) atomicMax(&sh_hi, best);
+          __syncthreads();
+          ci = sh_hi;
+        } else {
+          ci = sh_ci;
+        }
+      } else {
+        // every point coincides with a centre: the lowest index not chosen yet
+        int low = 0x7FFFFFFF;
+        for (int k = P - 1; k >= 0; --k) {
+          const int p = p0 + k;
+          if (p < N && !(nrs[k * SL_NT + tid] & NR_MARK)) low = p;
+        }
+        if (low != 0x7FFFFFFF) atomicMin(&sh_lo, low);
+        __syncthreads();
+        ci = sh_lo;
+      }
+      if (ci < 0 || ci >= N) ci = 0;
+    }
+    // ---- 2. centre row ---------------------------------------------------------------
+    if (tid == 0) { chosen[s] = ci; sd[s] = ci; }
+    if (tid < dm) {
+      const uint16_t xv = X[(size_t)ci * d + tid];
+      cvec[tid] = (double)bf16_to_f32(xv);
+      if (cached) cache[(size_t)s * cld + tid] = xv;
+    }
+    __syncthreads();
+    // ---- 3. distances to the earlier centres (lanes = channels) -------------------------
+    for (int a = wv; a < s; a += SL_NT / 64) {
+      double t = 0.0;
+      for (int ch = lane; ch < dm; ch += 64) {
+        const double xa = (double)bf16_to_f32(cached ? cache[(size_t)a * cld + ch] : X[(size_t)chosen[a] * d + ch]);
+        const double df = xa - cvec[ch];
+        t = fma(df, df, t);
+      }
+      t = wave_sum_dpp(t);
+      if (lane == 0) cc[a] = t;
+    }
+    __syncthreads();
+    // ---- 4. points whose D^2 may change ------------------------------------------------
+    // the fp32 copy is within 2^-24 of the exact D^2; the margin keeps the test exact
+    uint32_t need = 0;
+    for (int k0 = 0; k0 < P; k0 += 8) {
+      // eight slots at a time: their LDS reads issue together
+      uint32_t nv[8];
+      float dv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = min(k0 + u, P - 1);
+        nv[u] = nrs[k * SL_NT + tid];
+        dv[u] = d2s[k * SL_NT + tid];
+      }
+      double ca[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ca[u] = s > 0 ? cc[nv[u] & NR_ID] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u;
+        const bool ok = k < P && p0 + k < N;
+        const bool nd = ok && (s == 0 || !(ca[u] * (1.0 - 1e-9) >= 4.0 * (double)dv[u] * (1.0 + 1e-6)));
+        need |= (uint32_t)nd << min(k, 31);
+      }
+    }
+    const int cnt = __popc(need);
+    int K;
+    const int o_t = block_incl_scan<int, SL_NT>(cnt, itmp, &K) - cnt;
+    for (int base = 0; base < K; base += SL_LIST) {
+      if (o_t + cnt > base && o_t < base + SL_LIST) {
+        int pos = o_t;
+        for (int k = 0; k < P; ++k) {
+          if ((need >> k) & 1u) {
+            if (pos >= base && pos < base + SL_LIST) list[pos - base] = p0 + k;
+            ++pos;
+          }
+        }
+      }
+      __syncthreads();
+      const int nl = min(SL_LIST, K - base);
+      {
+        const int sub = tid & (lpr - 1), slot = tid / lpr, nslot = SL_NT / lpr;
+        const bool lv = sub * 8 < dm;
+        const int c0 = lv ? sub * 8 : 0;
+        for (int e0 = slot; e0 < nl; e0 += 8 * nslot) {
+          double acc[8];
+          int pp[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) pp[u] = list[min(e0 + u * nslot, nl - 1)];
+          if (vecrow) {
+            u32x4_t b[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              b[u] = *reinterpret_cast<const u32x4_t*>(X + (size_t)pp[u] * d + c0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u] = sqdist8v(b[u], cvec + c0);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u] = sqdist8<uint16_t>(X + (size_t)pp[u] * d, cvec, c0, dm);
+          }
+          double old[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) old[u] = (sub == 0 && s > 0) ? D2g[pp[u]] : 0.0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const double dist = group_sum_dpp(lv ? acc[u] : 0.0, lpr);
+            const int e = e0 + u * nslot;
+            if (sub == 0 && e < nl && (s == 0 || dist < old[u])) {
+              const int p = pp[u];
+              const int t = p / P, k = p - t * P;
+              D2g[p] = dist;
+              d2s[k * SL_NT + t] = (float)dist;
+              nrs[k * SL_NT + t] = s == 0 ? (uint16_t)0 : (uint16_t)(s | (nrs[k * SL_NT + t] & NR_MARK));
+              atomicAdd(&tsum[t], dist - old[u]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      const int t = ci / P, k = ci - t * P;
+      nrs[k * SL_NT + t] |= (uint16_t)NR_MARK;
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < C * dm; idx += SL_NT) {
+    const int c = idx / dm, ch = idx % dm;
+    const float val = bf16_to_f32(X[(size_t)chosen[c] * d + ch]);
+    if (m == 0) qcent[((size_t)bh * g.Cq + c) * d + ch] = val;
+    else kcent[((size_t)bh * g.Cm + c) * d + off + ch] = val;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // bf16 copies of the fp32 centroids (zero padded to [Cpad][dpad]) and their
 // squared norms (FLT_MAX on padding rows, so padding never wins).
 // ---------------------------------------------------------------------------
@@ -1137,6 +1384,21 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
   for (int m = 0; m < 4; ++m) {
     const size_t b = (size_t)g.C[m] * (g.dm[m] + 2) * sizeof(T);
     if (b <= (size_t)SEED_CACHE_BYTES && b > cache) cache = b;
+  }
+  if (sizeof(T) == 2) {
+    size_t need = 0;
+    bool fits = (g.N + SL_NT - 1) / SL_NT <= 32;
+    for (int m = 0; m < 4; ++m) {
+      const SeedLLayout L = seedl_layout(g.N, g.C[m], g.dm[m]);
+      need = L.bytes > need ? L.bytes : need;
+    }
+    fits = fits && need + 2048 <= (size_t)SL_LDS_LIMIT;
+    if (fits) {
+      (void)hipFuncSetAttribute((const void*)seedl_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)need);
+      seedl_kernel<<<grid, SL_NT, need, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.d2, w.seeds, w.qcent,
+                                            w.kcent);
+      return;
+    }
   }
   const int P = (g.N + SR_NT - 1) / SR_NT;
   if (P <= SR_PMAX) {
