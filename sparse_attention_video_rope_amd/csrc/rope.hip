@@ -48,20 +48,23 @@ template <> struct Vec8<float> {
 };
 
 // One thread rotates 8 consecutive channels (4 pairs) of one token of Q or K.
+// Grid: x over the tokens x (d/8) chunks of one head, y over heads, z over Q / K, so
+// all index arithmetic is 32-bit (d/8 is 8 or 16: a shift).
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    T* __restrict__ qo, T* __restrict__ ko,
                                                    const double2* __restrict__ tab, RopeArgs a) {
-  const int64_t per = (int64_t)a.BH * a.N * (a.d / 8);
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= 2 * per) return;
-  const int sel = gid >= per;
-  const int64_t r = gid - sel * per;
-  const int chunk = (int)(r % (a.d / 8));
-  const int64_t row = r / (a.d / 8);
-  const int n = (int)(row % a.N);
-  const int pos[3] = {n / (a.Hg * a.Wg), (n / a.Wg) % a.Hg, n % a.Wg};
-  const int64_t base = row * a.d + chunk * 8;
+  const int cshift = a.d == 128 ? 4 : 3;
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;   // token * (d/8) + chunk
+  if (r >= (a.N << cshift)) return;
+  const int sel = blockIdx.z, bh = blockIdx.y;
+  const int chunk = r & ((1 << cshift) - 1);
+  const int n = r >> cshift;
+  const int hw = a.Hg * a.Wg;
+  const int t = n / hw, rem = n - t * hw;
+  const int hh = rem / a.Wg, ww = rem - hh * a.Wg;
+  const int pos[3] = {t, hh, ww};
+  const size_t base = ((size_t)bh * a.N + n) * a.d + chunk * 8;
   Vec8<T> x;
   x.load((sel ? k : q) + base);
 #pragma unroll
@@ -93,8 +96,7 @@ hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const
   a.off1 = g.off[2]; a.off2 = g.off[3];
   a.dm[0] = g.dm[1]; a.dm[1] = g.dm[2]; a.dm[2] = g.dm[3];
   a.toff[0] = 0; a.toff[1] = n0; a.toff[2] = n0 + n1;
-  const int64_t threads = 2 * (int64_t)g.BH * g.N * (g.d / 8);
-  const int blocks = (int)((threads + 255) / 256);
+  const dim3 blocks((unsigned)((g.N * (g.d / 8) + 255) / 256), (unsigned)g.BH, 2);
   if (g.bf16)
     rope_kernel<uint16_t><<<blocks, 256, 0, s>>>((const uint16_t*)q, (const uint16_t*)k, (uint16_t*)qo,
                                                  (uint16_t*)ko, w.rope_tab, a);

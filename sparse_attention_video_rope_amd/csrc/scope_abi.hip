@@ -61,6 +61,7 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
   w.qlab = (int32_t*)take(4 * BH * N);
   w.lut = (double*)take(8 * BH * g.Cq * 3 * g.Cm);
   w.csel = (ClusterSel*)take(sizeof(ClusterSel) * BH * g.Cq);
+  w.htot = (int64_t*)take(8 * BH);
   w.bytes = o;
   if (plan) {
     if (plan->seeds) w.seeds = plan->seeds;
@@ -175,7 +176,7 @@ scope_status scope_plan(const scope_params* p, const void* q, const void* k, voi
   STEP(launch_perm(g, w, plan->perm_q, plan->q_off, stream));
   STEP(launch_lut(g, w, stream));
   STEP(launch_topp(g, *p, w, plan->counts_t, plan->counts_b, stream));
-  STEP(launch_khead(g, *plan, stream));
+  STEP(launch_khead(g, *plan, w, stream));
   STEP(launch_final_select(g, *p, w, *plan, stream));
   STEP(launch_worklist(g, *plan, stream));
 #undef STEP

@@ -55,6 +55,7 @@ struct Workspace {
   int32_t* qlab;                // [BH][N] (final query labels)
   double* lut;                  // [BH][Cq][3][Cm]
   ClusterSel* csel;             // [BH][Cq]
+  int64_t* htot;                // [BH] per-head total of r_c, then the head's offset in sel_idx
   size_t bytes;
 };
 
@@ -88,7 +89,7 @@ hipError_t launch_perm(const Geo& g, const Workspace& w, int32_t* perm_q, int32_
 hipError_t launch_lut(const Geo& g, const Workspace& w, hipStream_t s);
 hipError_t launch_topp(const Geo& g, const scope_params& p, const Workspace& w, int32_t* ct, int32_t* cb,
                        hipStream_t s);
-hipError_t launch_khead(const Geo& g, const scope_plan_t& plan, hipStream_t s);
+hipError_t launch_khead(const Geo& g, const scope_plan_t& plan, const Workspace& w, hipStream_t s);
 hipError_t launch_final_select(const Geo& g, const scope_params& p, const Workspace& w,
                                const scope_plan_t& plan, hipStream_t s);
 hipError_t launch_worklist(const Geo& g, const scope_plan_t& plan, hipStream_t s);

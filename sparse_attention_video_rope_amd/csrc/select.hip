@@ -441,46 +441,74 @@ __global__ __launch_bounds__(NT) void topp_kernel(SelArgs a, const double* __res
 }
 
 // ---------------------------------------------------------------------------
-// Stage 5b: k_head (Eq. 9), r_c (Eq. 10) and the CSR offsets; one workgroup.
+// Stage 5b: k_head (Eq. 9), r_c (Eq. 10) and the CSR offsets.
+// khead_kernel (one workgroup per head) writes k_head, r_c, the head-local
+// prefix of r_c into sel_off and the head total; seloff_scan_kernel turns the
+// head totals into head offsets (and flags a capacity overflow);
+// seloff_add_kernel adds them to sel_off.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void khead_kernel(int BH, int Cq, int N, const int32_t* __restrict__ q_off,
-                                                     const int32_t* __restrict__ cb, int32_t* __restrict__ cr,
-                                                     int32_t* __restrict__ khead, int64_t* __restrict__ sel_off,
-                                                     int64_t capacity, int32_t* __restrict__ status) {
+constexpr int KH_NT = 256;
+
+__global__ __launch_bounds__(KH_NT) void khead_kernel(int Cq, int N, const int32_t* __restrict__ q_off,
+                                                      const int32_t* __restrict__ cb, int32_t* __restrict__ cr,
+                                                      int32_t* __restrict__ khead, int64_t* __restrict__ sel_off,
+                                                      int64_t* __restrict__ htot) {
+  __shared__ int64_t tmp[KH_NT / 64 + 1];
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  const int32_t* qo = q_off + (size_t)bh * (Cq + 1);
+  int64_t num = 0, den = 0;
+  for (int c = tid; c < Cq; c += KH_NT) {
+    const int64_t n = qo[c + 1] - qo[c];
+    num += n * cb[(size_t)bh * Cq + c];
+    den += n;
+  }
+  num = block_sum<int64_t, KH_NT>(num, tmp);
+  den = block_sum<int64_t, KH_NT>(den, tmp);
+  const int64_t kh = den > 0 ? (num + den - 1) / den : 0;
+  if (tid == 0) khead[bh] = (int32_t)kh;
+  int64_t base = 0;
+  for (int c0 = 0; c0 < Cq; c0 += KH_NT) {
+    const int c = c0 + tid;
+    int64_t r = 0;
+    if (c < Cq) {
+      const int64_t n = qo[c + 1] - qo[c];
+      const int64_t b = cb[(size_t)bh * Cq + c];
+      r = n > 0 ? (b > kh ? b : kh) : 0;
+      if (r > N) r = N;
+      cr[(size_t)bh * Cq + c] = (int32_t)r;
+    }
+    int64_t tot;
+    const int64_t inc = block_incl_scan<int64_t, KH_NT>(r, tmp, &tot);
+    if (c < Cq) sel_off[(size_t)bh * Cq + c] = base + inc - r;
+    base += tot;
+  }
+  if (tid == 0) htot[bh] = base;
+}
+
+__global__ __launch_bounds__(1024) void seloff_scan_kernel(int BH, int Cq, int64_t* __restrict__ htot,
+                                                           int64_t* __restrict__ sel_off, int64_t capacity,
+                                                           int32_t* __restrict__ status) {
   __shared__ int64_t tmp[17];
   const int tid = threadIdx.x;
   int64_t base = 0;
-  for (int bh = 0; bh < BH; ++bh) {
-    int64_t num = 0, den = 0;
-    for (int c = tid; c < Cq; c += 1024) {
-      const int64_t n = q_off[(size_t)bh * (Cq + 1) + c + 1] - q_off[(size_t)bh * (Cq + 1) + c];
-      num += n * cb[(size_t)bh * Cq + c];
-      den += n;
-    }
-    num = block_sum<int64_t, 1024>(num, tmp);
-    den = block_sum<int64_t, 1024>(den, tmp);
-    const int64_t kh = den > 0 ? (num + den - 1) / den : 0;
-    if (tid == 0) khead[bh] = (int32_t)kh;
-    for (int c0 = 0; c0 < Cq; c0 += 1024) {
-      const int c = c0 + tid;
-      int64_t r = 0;
-      if (c < Cq) {
-        const int64_t n = q_off[(size_t)bh * (Cq + 1) + c + 1] - q_off[(size_t)bh * (Cq + 1) + c];
-        const int64_t b = cb[(size_t)bh * Cq + c];
-        r = n > 0 ? (b > kh ? b : kh) : 0;
-        if (r > N) r = N;
-        cr[(size_t)bh * Cq + c] = (int32_t)r;
-      }
-      int64_t tot;
-      const int64_t inc = block_incl_scan<int64_t, 1024>(r, tmp, &tot);
-      if (c < Cq) sel_off[(size_t)bh * Cq + c] = base + inc - r;
-      base += tot;
-    }
+  for (int h0 = 0; h0 < BH; h0 += 1024) {
+    const int h = h0 + tid;
+    const int64_t v = h < BH ? htot[h] : 0;
+    int64_t tot;
+    const int64_t inc = block_incl_scan<int64_t, 1024>(v, tmp, &tot);
+    if (h < BH) htot[h] = base + inc - v;   // offset of head h
+    base += tot;
   }
   if (tid == 0) {
     sel_off[(size_t)BH * Cq] = base;
     status[1] = base > capacity ? 1 : 0;
   }
+}
+
+__global__ __launch_bounds__(256) void seloff_add_kernel(int Cq, const int64_t* __restrict__ htot,
+                                                         int64_t* __restrict__ sel_off) {
+  const int c = blockIdx.x * 256 + threadIdx.x, bh = blockIdx.y;
+  if (c < Cq) sel_off[(size_t)bh * Cq + c] += htot[bh];
 }
 
 // ---------------------------------------------------------------------------
@@ -621,9 +649,11 @@ hipError_t launch_topp(const Geo& g, const scope_params& p, const Workspace& w, 
   return hipGetLastError();
 }
 
-hipError_t launch_khead(const Geo& g, const scope_plan_t& plan, hipStream_t s) {
-  khead_kernel<<<1, 1024, 0, s>>>(g.BH, g.Cq, g.N, plan.q_off, plan.counts_b, plan.counts_r, plan.k_head,
-                                  plan.sel_off, plan.sel_capacity, plan.status);
+hipError_t launch_khead(const Geo& g, const scope_plan_t& plan, const Workspace& w, hipStream_t s) {
+  khead_kernel<<<g.BH, KH_NT, 0, s>>>(g.Cq, g.N, plan.q_off, plan.counts_b, plan.counts_r, plan.k_head, plan.sel_off,
+                                      w.htot);
+  seloff_scan_kernel<<<1, 1024, 0, s>>>(g.BH, g.Cq, w.htot, plan.sel_off, plan.sel_capacity, plan.status);
+  seloff_add_kernel<<<dim3((g.Cq + 255) / 256, g.BH), 256, 0, s>>>(g.Cq, w.htot, plan.sel_off);
   return hipGetLastError();
 }
 
