@@ -678,7 +678,15 @@ __global__ __launch_bounds__(SR_NT) void seedr_kernel(const T* __restrict__ qr, 
 // are exact, so their order does not matter).
 // ---------------------------------------------------------------------------
 constexpr int SL_NT = 1024;
+
+// x >= 0 rounded to fp32 towards +infinity (for a non-negative finite float
+// the next float up has the bit pattern plus one)
+__device__ __forceinline__ float f32_up(double x) {
+  const float f = (float)x;
+  return (double)f < x ? __uint_as_float(__float_as_uint(f) + 1u) : f;
+}
 constexpr int SL_LIST = 4096;
+constexpr int SL_U = 8;          // rows in flight per lane group in the distance phase
 constexpr int SL_LDS_LIMIT = 160 * 1024;
 
 struct SeedLLayout {
@@ -704,6 +712,9 @@ __host__ __device__ inline SeedLLayout seedl_layout(int N, int C, int dm) {
   return L;
 }
 
+// VEC: every clustering reads its rows as aligned 16-byte pieces (offsets and
+// widths are multiples of 8 channels); the host checks this.
+template <bool VEC>
 __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
                                                       Geo g, double* __restrict__ d2all, int32_t* __restrict__ seeds,
                                                       float* __restrict__ qcent, float* __restrict__ kcent) {
@@ -728,20 +739,28 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
   const int cld = dm + 2;
   const bool cached = L.cached;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int P = (N + SL_NT - 1) / SL_NT;
-  const int p0 = tid * P;
-  const bool vecrow = ((off * 2) % 16 == 0) && ((d * 2) % 16 == 0) && (dm % 8 == 0);
   int lpr = 1;
   while (lpr * 8 < dm) lpr <<= 1;
   const uint64_t stream = ((uint64_t)bh * 4 + m) << 20;
 
-  for (int i = tid; i < SL_NT * P; i += SL_NT) { d2s[i] = 0.f; nrs[i] = (uint16_t)NR_MARK; }
-  tsum[tid] = 0.0;
+  for (int i = threadIdx.x; i < SL_NT * P; i += SL_NT) { d2s[i] = 0.f; nrs[i] = (uint16_t)NR_MARK; }
+  tsum[threadIdx.x] = 0.0;
   __syncthreads();
 
   int ci = 0;
   for (int s = 0; s < C; ++s) {
+    // the thread index is made opaque once per draw, so that values derived
+    // from it are recomputed here instead of being kept live (and spilled)
+    // across the whole loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int p0 = tid * P;
+    // bit k: point p0 + k exists
+    const int nk = max(0, min(P, N - p0));
+    const uint32_t vmask = nk >= 32 ? 0xFFFFFFFFu : ((1u << nk) - 1u);
     // ---- 1. centre s -------------------------------------------------------------
     if (s == 0) {
       const uint64_t k0 = splitmix64(g.seed, stream) >> 11;
@@ -750,7 +769,7 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
     } else {
       const double loc = tsum[tid];
       double total;
-      const double incl = block_incl_scan<double, SL_NT>(loc, dtmp, &total);
+      const double incl = block_incl_scan_dpp<double, SL_NT>(loc, dtmp, &total);
       const uint64_t ku = splitmix64(g.seed, stream + (uint64_t)s) >> 11;
       const double target = ((double)ku * 0x1p-53) * total;
       if (tid == 0) { sh_ci = -1; sh_lo = 0x7FFFFFFF; sh_hi = -1; }
@@ -765,7 +784,7 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
           const int q0 = (wv * 64 + L) * P;
           const int p = q0 + lane;
           const double v = (lane < P && p < N) ? D2g[p] : 0.0;
-          const double inc = ex + wave_incl_scan(v);
+          const double inc = ex + wave_incl_scan_dpp(v);
           const uint64_t hit = __ballot(lane < P && p < N && inc > target);
           const uint64_t pos = __ballot(v > 0.0);
           const int k = hit ? __ffsll((unsigned long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
@@ -816,41 +835,39 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
     }
     __syncthreads();
     // ---- 4. points whose D^2 may change ------------------------------------------------
-    // the fp32 copy is within 2^-24 of the exact D^2; the margin keeps the test exact
-    uint32_t need = 0;
-    for (int k0 = 0; k0 < P; k0 += 8) {
-      // eight slots at a time: their LDS reads issue together
-      uint32_t nv[8];
-      float dv[8];
+    // the fp32 copy is the exact D^2 rounded up, so skipping when the
+    // centre-to-centre distance is at least 4.000008 x that copy is exact
+    uint32_t need = vmask;
+    if (s > 0) {
+      need = 0;
+      for (int k0 = 0; k0 < P; k0 += 8) {
+        // eight slots at a time: their LDS reads issue together
+        uint32_t nv[8];
+        float dv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = min(k0 + u, P - 1);
-        nv[u] = nrs[k * SL_NT + tid];
-        dv[u] = d2s[k * SL_NT + tid];
+        for (int u = 0; u < 8; ++u) {
+          const int k = min(k0 + u, P - 1);
+          nv[u] = nrs[k * SL_NT + tid];
+          dv[u] = d2s[k * SL_NT + tid];
+        }
+        double ca[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ca[u] = cc[nv[u] & NR_ID];
+        uint32_t bits = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) bits |= (uint32_t)!(ca[u] >= 4.000008 * (double)dv[u]) << u;
+        need |= bits << k0;
       }
-      double ca[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) ca[u] = s > 0 ? cc[nv[u] & NR_ID] : 0.0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + u;
-        const bool ok = k < P && p0 + k < N;
-        const bool nd = ok && (s == 0 || !(ca[u] * (1.0 - 1e-9) >= 4.0 * (double)dv[u] * (1.0 + 1e-6)));
-        need |= (uint32_t)nd << min(k, 31);
-      }
+      need &= vmask;
     }
     const int cnt = __popc(need);
     int K;
-    const int o_t = block_incl_scan<int, SL_NT>(cnt, itmp, &K) - cnt;
+    const int o_t = block_incl_scan_dpp<int, SL_NT>(cnt, itmp, &K) - cnt;
     for (int base = 0; base < K; base += SL_LIST) {
       if (o_t + cnt > base && o_t < base + SL_LIST) {
         int pos = o_t;
-        for (int k = 0; k < P; ++k) {
-          if ((need >> k) & 1u) {
-            if (pos >= base && pos < base + SL_LIST) list[pos - base] = p0 + k;
-            ++pos;
-          }
-        }
+        for (uint32_t mm = need; mm != 0u; mm &= mm - 1u, ++pos)
+          if (pos >= base && pos < base + SL_LIST) list[pos - base] = p0 + __ffs(mm) - 1;
       }
       __syncthreads();
       const int nl = min(SL_LIST, K - base);
@@ -858,34 +875,39 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
         const int sub = tid & (lpr - 1), slot = tid / lpr, nslot = SL_NT / lpr;
         const bool lv = sub * 8 < dm;
         const int c0 = lv ? sub * 8 : 0;
-        for (int e0 = slot; e0 < nl; e0 += 8 * nslot) {
-          double acc[8];
-          int pp[8];
+        for (int e0 = slot; e0 < nl; e0 += SL_U * nslot) {
+          double acc[SL_U];
+          int pp[SL_U];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) pp[u] = list[min(e0 + u * nslot, nl - 1)];
-          if (vecrow) {
-            u32x4_t b[8];
+          for (int u = 0; u < SL_U; ++u) pp[u] = list[min(e0 + u * nslot, nl - 1)];
+          if constexpr (VEC) {
+            // 32-bit byte offsets from the uniform row base (N d <= 2^25)
+            const char* Xb = reinterpret_cast<const char*>(X);
+            u32x4_t b[SL_U];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-              b[u] = *reinterpret_cast<const u32x4_t*>(X + (size_t)pp[u] * d + c0);
+            for (int u = 0; u < SL_U; ++u)
+              b[u] = *reinterpret_cast<const u32x4_t*>(Xb + ((uint32_t)pp[u] * (uint32_t)(2 * d) + (uint32_t)(2 * c0)));
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc[u] = sqdist8v(b[u], cvec + c0);
+            for (int u = 0; u < SL_U; ++u) acc[u] = sqdist8v(b[u], cvec + c0);
           } else {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc[u] = sqdist8<uint16_t>(X + (size_t)pp[u] * d, cvec, c0, dm);
+            for (int u = 0; u < SL_U; ++u) acc[u] = sqdist8<uint16_t>(X + (size_t)pp[u] * d, cvec, c0, dm);
           }
-          double old[8];
+          double old[SL_U];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) old[u] = (sub == 0 && s > 0) ? D2g[pp[u]] : 0.0;
+          for (int u = 0; u < SL_U; ++u)
+            old[u] = (sub == 0 && s > 0)
+                         ? *reinterpret_cast<const double*>(reinterpret_cast<const char*>(D2g) + (uint32_t)pp[u] * 8u)
+                         : 0.0;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
+          for (int u = 0; u < SL_U; ++u) {
             const double dist = group_sum_dpp(lv ? acc[u] : 0.0, lpr);
             const int e = e0 + u * nslot;
             if (sub == 0 && e < nl && (s == 0 || dist < old[u])) {
               const int p = pp[u];
               const int t = p / P, k = p - t * P;
               D2g[p] = dist;
-              d2s[k * SL_NT + t] = (float)dist;
+              d2s[k * SL_NT + t] = f32_up(dist);
               nrs[k * SL_NT + t] = s == 0 ? (uint16_t)0 : (uint16_t)(s | (nrs[k * SL_NT + t] & NR_MARK));
               atomicAdd(&tsum[t], dist - old[u]);
             }
@@ -900,7 +922,7 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
     }
     __syncthreads();
   }
-  for (int idx = tid; idx < C * dm; idx += SL_NT) {
+  for (int idx = threadIdx.x; idx < C * dm; idx += SL_NT) {
     const int c = idx / dm, ch = idx % dm;
     const float val = bf16_to_f32(X[(size_t)chosen[c] * d + ch]);
     if (m == 0) qcent[((size_t)bh * g.Cq + c) * d + ch] = val;
@@ -1394,9 +1416,16 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
     }
     fits = fits && need + 2048 <= (size_t)SL_LDS_LIMIT;
     if (fits) {
-      (void)hipFuncSetAttribute((const void*)seedl_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)need);
-      seedl_kernel<<<grid, SL_NT, need, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.d2, w.seeds, w.qcent,
-                                            w.kcent);
+      bool vec = g.d % 8 == 0;
+      for (int m = 0; m < 4; ++m) vec = vec && g.off[m] % 8 == 0 && g.dm[m] % 8 == 0;
+      const void* fn = vec ? (const void*)seedl_kernel<true> : (const void*)seedl_kernel<false>;
+      (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)need);
+      if (vec)
+        seedl_kernel<true><<<grid, SL_NT, need, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.d2, w.seeds,
+                                                     w.qcent, w.kcent);
+      else
+        seedl_kernel<false><<<grid, SL_NT, need, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.d2, w.seeds,
+                                                      w.qcent, w.kcent);
       return;
     }
   }

@@ -112,6 +112,64 @@ __device__ __forceinline__ T wave_incl_scan(T v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves only (no
+// LDS, no lane-address registers): a Hillis-Steele scan inside each 16-lane
+// row (row_shr 1, 2, 4, 8), then row 0's total is added to row 1 and row 2's
+// to row 3 (row_bcast:15), then lane 31's running total to rows 2 and 3
+// (row_bcast:31).  The addition order differs from wave_incl_scan, so use it
+// for integers or for fp64 values whose partial sums are exact.  All 64 lanes
+// must be active.
+template <int CTRL, int RM>
+__device__ __forceinline__ int dpp_row_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, RM, 0xF, false);
+}
+template <int CTRL, int RM>
+__device__ __forceinline__ double dpp_row_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, RM, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, RM, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += dpp_row_i32<0x111, 0xF>(v);
+  v += dpp_row_i32<0x112, 0xF>(v);
+  v += dpp_row_i32<0x114, 0xF>(v);
+  v += dpp_row_i32<0x118, 0xF>(v);
+  v += dpp_row_i32<0x142, 0xA>(v);
+  v += dpp_row_i32<0x143, 0xC>(v);
+  return v;
+}
+__device__ __forceinline__ double wave_incl_scan_dpp(double v) {
+  v += dpp_row_f64<0x111, 0xF>(v);
+  v += dpp_row_f64<0x112, 0xF>(v);
+  v += dpp_row_f64<0x114, 0xF>(v);
+  v += dpp_row_f64<0x118, 0xF>(v);
+  v += dpp_row_f64<0x142, 0xA>(v);
+  v += dpp_row_f64<0x143, 0xC>(v);
+  return v;
+}
+
+// Block-wide inclusive scan built on wave_incl_scan_dpp (same caveat on the
+// order); `tmp` holds NT/64 + 1 values.  All threads must call.
+template <typename T, int NT>
+__device__ __forceinline__ T block_incl_scan_dpp(T v, T* tmp, T* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  T inc = wave_incl_scan_dpp(v);
+  if (lane == 63) tmp[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    T x = lane < NW ? tmp[lane] : T(0);
+    T xs = wave_incl_scan_dpp(x);
+    if (lane < NW) tmp[lane] = xs - x;   // exclusive wave offsets
+    if (lane == NW - 1) tmp[NW] = xs;
+  }
+  __syncthreads();
+  T r = inc + tmp[w];
+  if (total) *total = tmp[NW];
+  __syncthreads();
+  return r;
+}
+
 // Block-wide inclusive scan; `tmp` holds one T per wave.  All threads must call.
 template <typename T, int NT>
 __device__ __forceinline__ T block_incl_scan(T v, T* tmp, T* total) {
