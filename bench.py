@@ -223,7 +223,7 @@ def main():
         "attend_tflops": round(achieved, 2),
         "density": round(density, 4),
         "k_head": {"min": int(kh.min()), "mean": float(kh.mean()), "max": int(kh.max())},
-        "roofline": {"kernel": "attend_bf16_tiles_kernel" if w.dtype == "bf16" else "attend_f32_kernel",
+        "roofline": {"kernel": "attend_bf16_lds_kernel" if w.dtype == "bf16" else "attend_f32_kernel",
                      "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "wall_s": round(wall, 3),
