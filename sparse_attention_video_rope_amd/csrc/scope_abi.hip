@@ -62,6 +62,7 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
   w.lut = (double*)take(8 * BH * g.Cq * 3 * g.Cm);
   w.csel = (ClusterSel*)take(sizeof(ClusterSel) * BH * g.Cq);
   w.htot = (int64_t*)take(8 * BH);
+  w.hist1 = (int32_t*)take(4 * BH * g.Cq * (size_t)SEL_NB);
   w.bytes = o;
   if (plan) {
     if (plan->seeds) w.seeds = plan->seeds;

@@ -56,6 +56,7 @@ struct Workspace {
   double* lut;                  // [BH][Cq][3][Cm]
   ClusterSel* csel;             // [BH][Cq]
   int64_t* htot;                // [BH] per-head total of r_c, then the head's offset in sel_idx
+  int32_t* hist1;               // [BH][Cq][SEL_NB] level-1 key counts of the Top-p pass (reused by the final selection)
   size_t bytes;
 };
 

@@ -159,20 +159,76 @@ struct Boundary {
   int count;
 };
 
+// Exact resolution of a boundary bin holding at most 64 keys (candidates already
+// in sm.cs / cj / cw, n of them) by one wave: a bitonic sort across the lanes
+// by (s desc, j asc), then the first position whose running weight reaches
+// tgt (mass) or position tgt - before_count - 1 (count).
+__device__ Boundary resolve_small_bin(const SelSmem& sm, int n, bool by_mass, uint64_t tgt, uint64_t bm, int64_t bc) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    double s = tid < n ? sm.cs[tid] : -__builtin_inf();
+    int j = tid < n ? sm.cj[tid] : 0x7FFFFFFF - tid;   // distinct sentinels after every key
+    uint64_t w = tid < n ? sm.cw[tid] : 0;
+    for (int size = 2; size <= 64; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const double so = __shfl_xor(s, stride);
+        const int jo = __shfl_xor(j, stride);
+        const uint64_t wo = __shfl_xor(w, stride);
+        const bool other_first = so > s || (so == s && jo < j);
+        const bool lower = (tid & stride) == 0, asc = (tid & size) == 0;
+        if (lower == asc ? other_first : !other_first) { s = so; j = jo; w = wo; }
+      }
+    }
+    int kb;
+    if (by_mass) {
+      const uint64_t run = bm + wave_incl_scan(w);
+      const uint64_t hit = __ballot(tid < n && run >= tgt);
+      kb = hit ? __ffsll((unsigned long long)hit) - 1 : n - 1;
+    } else {
+      kb = min(max((int)((int64_t)tgt - bc - 1), 0), n - 1);
+    }
+    const double tau = __shfl(s, kb);
+    const uint64_t same = __ballot(s == tau);
+    const int k0 = __ffsll((unsigned long long)same) - 1;
+    if (tid == 0) {
+      sm.dtmp[0] = tau;
+      sm.misc[4] = kb - k0 + 1;
+      sm.misc[5] = (int)bc + kb + 1;
+    }
+  }
+  __syncthreads();
+  Boundary r;
+  r.tau = sm.dtmp[0];
+  r.m = sm.misc[4];
+  r.count = sm.misc[5];
+  __syncthreads();
+  return r;
+}
+
 // by_mass with rho > 0: the target is ceil(rho * total mass), the total (returned
 // in *zmass) taken from the level-1 histogram (integer sums, exact).
+// pre_hc: level-1 key counts of the same bins, computed earlier (count mode
+// only; replaces the level-1 pass).  save_hc: where to store the level-1 counts.
 __device__ Boundary find_boundary(const Sel& S, const SelSmem& sm, bool by_mass, uint64_t tgt, double rho = 0.0,
-                                  uint64_t* zmass = nullptr) {
+                                  uint64_t* zmass = nullptr, const int32_t* pre_hc = nullptr,
+                                  int32_t* save_hc = nullptr) {
   const int tid = threadIdx.x, N = S.N;
   // ---- level 1 ------------------------------------------------------------
-  for (int b = tid; b < SEL_NB; b += NT) { sm.hc[b] = 0; sm.hm[b] = 0; }
-  __syncthreads();
-  each_key(S, [&](int, ushort4 z) {
-    const int b1 = bin1_of(bin_x(S, logit(S, z)));
-    atomicAdd(&sm.hc[b1], 1);
-    if (by_mass) atomicAdd((unsigned long long*)&sm.hm[b1], (unsigned long long)weight_fx(S, z));
-  });
-  __syncthreads();
+  if (pre_hc) {
+    for (int b = tid; b < SEL_NB; b += NT) { sm.hc[b] = pre_hc[b]; sm.hm[b] = 0; }
+    __syncthreads();
+  } else {
+    for (int b = tid; b < SEL_NB; b += NT) { sm.hc[b] = 0; sm.hm[b] = 0; }
+    __syncthreads();
+    each_key(S, [&](int, ushort4 z) {
+      const int b1 = bin1_of(bin_x(S, logit(S, z)));
+      atomicAdd(&sm.hc[b1], 1);
+      if (by_mass) atomicAdd((unsigned long long*)&sm.hm[b1], (unsigned long long)weight_fx(S, z));
+    });
+    __syncthreads();
+    if (save_hc)
+      for (int b = tid; b < SEL_NB; b += NT) save_hc[b] = sm.hc[b];
+  }
   if (by_mass && rho > 0.0) {
     uint64_t zl = 0;
 #pragma unroll
@@ -185,6 +241,22 @@ __device__ Boundary find_boundary(const Sel& S, const SelSmem& sm, bool by_mass,
   uint64_t bm;
   int64_t bc;
   const int B1 = hist_walk(sm, by_mass, tgt, 0, 0, &bm, &bc);
+  const int n1 = sm.hc[B1];
+  if (n1 > 0 && n1 <= 64) {
+    // ---- few keys in the boundary bin: sort them directly ----------------
+    if (tid == 0) sm.misc[1] = 0;
+    __syncthreads();
+    each_key(S, [&](int j, ushort4 z) {
+      const double s = logit(S, z);
+      if (bin1_of(bin_x(S, s)) != B1) return;
+      const int k = atomicAdd(&sm.misc[1], 1);
+      sm.cs[k] = s;
+      sm.cj[k] = j;
+      sm.cw[k] = by_mass ? weight_fx(S, z) : 0;
+    });
+    __syncthreads();
+    return resolve_small_bin(sm, n1, by_mass, tgt, bm, bc);
+  }
   // ---- level 2 ------------------------------------------------------------
   for (int b = tid; b < SEL_NB; b += NT) { sm.hc[b] = 0; sm.hm[b] = 0; }
   __syncthreads();
@@ -401,7 +473,8 @@ static size_t sel_smem_bytes(int Cm) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NT) void topp_kernel(SelArgs a, const double* __restrict__ lut,
                                                   const ushort4* __restrict__ codes, ClusterSel* __restrict__ csel,
-                                                  int32_t* __restrict__ ct, int32_t* __restrict__ cb) {
+                                                  int32_t* __restrict__ ct, int32_t* __restrict__ cb,
+                                                  int32_t* __restrict__ hist1) {
   const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   double *Pl, *El;
@@ -424,7 +497,8 @@ __global__ __launch_bounds__(NT) void topp_kernel(SelArgs a, const double* __res
     st.zfx = 0;
   } else {
     uint64_t z = 0;
-    const Boundary b = find_boundary(S, sm, true, 0, a.rho, &z);
+    const Boundary b = find_boundary(S, sm, true, 0, a.rho, &z, nullptr,
+                                     hist1 + ((size_t)bh * a.Cq + c) * SEL_NB);
     t = b.count;
     st.all = t >= a.N;
     st.tau = b.tau;
@@ -521,7 +595,8 @@ __global__ __launch_bounds__(NT) void final_select_kernel(SelArgs a, const doubl
                                                           const int32_t* __restrict__ cr,
                                                           const int64_t* __restrict__ sel_off,
                                                           int32_t* __restrict__ sel_idx,
-                                                          const int32_t* __restrict__ status) {
+                                                          const int32_t* __restrict__ status,
+                                                          const int32_t* __restrict__ hist1) {
   const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const size_t ci = (size_t)bh * a.Cq + c;
   const int r = cr[ci];
@@ -552,7 +627,8 @@ __global__ __launch_bounds__(NT) void final_select_kernel(SelArgs a, const doubl
     tau = st.tau;
     m = st.m;
   } else {
-    const Boundary b = find_boundary(S, sm, false, (uint64_t)r);
+    // same bins as the Top-p pass (smax, scale1 from csel): its level-1 counts are reused
+    const Boundary b = find_boundary(S, sm, false, (uint64_t)r, 0.0, nullptr, hist1 + ci * SEL_NB);
     tau = b.tau;
     m = b.m;
   }
@@ -645,7 +721,8 @@ hipError_t launch_topp(const Geo& g, const scope_params& p, const Workspace& w, 
                        hipStream_t s) {
   const size_t lds = sel_smem_bytes(g.Cm);
   allow_big_lds((const void*)topp_kernel, lds);
-  topp_kernel<<<dim3(g.Cq, g.BH), NT, lds, s>>>(sel_args(g, p), w.lut, (const ushort4*)w.codes, w.csel, ct, cb);
+  topp_kernel<<<dim3(g.Cq, g.BH), NT, lds, s>>>(sel_args(g, p), w.lut, (const ushort4*)w.codes, w.csel, ct, cb,
+                                                 w.hist1);
   return hipGetLastError();
 }
 
@@ -662,7 +739,8 @@ hipError_t launch_final_select(const Geo& g, const scope_params& p, const Worksp
   const size_t lds = sel_smem_bytes(g.Cm);
   allow_big_lds((const void*)final_select_kernel, lds);
   final_select_kernel<<<dim3(g.Cq, g.BH), NT, lds, s>>>(sel_args(g, p), w.lut, (const ushort4*)w.codes, w.csel,
-                                                        plan.counts_r, plan.sel_off, plan.sel_idx, plan.status);
+                                                        plan.counts_r, plan.sel_off, plan.sel_idx, plan.status,
+                                                        w.hist1);
   return hipGetLastError();
 }
 
