@@ -665,12 +665,14 @@ __global__ __launch_bounds__(SR_NT) void seedr_kernel(const T* __restrict__ qr, 
 // k-means++ seeding for bf16 data with the point state in LDS (1024 threads).
 // Same draw rule as seed_kernel.  Thread t owns the P consecutive points
 // t P .. t P + P - 1 ((thread, slot) is the index order).  The exact fp64 D^2
-// of every point lives in global memory; LDS holds an fp32 copy for the
-// pruning test (with a margin that covers its rounding), the 16-bit nearest
-// centre ids, and each thread's exact D^2 sum.  Per draw: a block scan of the
-// per-thread sums finds the crossing thread, which reads its exact values to
-// find the point; the centre's distances to the earlier centres are computed
-// by all waves; the points the Elkan test keeps are listed in index order (a
+// of every point lives in global memory; LDS holds, per point, one 32-bit word
+// with D^2 rounded up to bf16 (high half) and ||x|| rounded to bf16 (low half)
+// for the pruning tests, the 16-bit nearest centre ids, and each thread's exact
+// D^2 sum.  Per draw: a block scan of the per-thread sums finds the crossing
+// thread, which reads its exact values to find the point; the centre's
+// distances to the earlier centres are computed by all waves; the points that
+// neither the Elkan test (||c_s - a||^2 >= 4 D^2, a the nearest centre) nor the
+// norm test ((||x|| - ||c_s||)^2 >= D^2) rules out are listed in index order (a
 // scan of per-thread counts) and all threads compute their exact distances;
 // the thread that computes a distance applies it: it replaces the exact D^2
 // (global) when smaller, refreshes the LDS copies and adds the exact
@@ -684,6 +686,36 @@ constexpr int SL_NT = 1024;
 __device__ __forceinline__ float f32_up(double x) {
   const float f = (float)x;
   return (double)f < x ? __uint_as_float(__float_as_uint(f) + 1u) : f;
+}
+// bf16 bits of x >= 0 rounded up (an upper bound of x)
+__device__ __forceinline__ uint32_t bf16_up_bits(double x) {
+  const uint32_t b = __float_as_uint(f32_up(x));
+  return (b >> 16) + ((b & 0xFFFFu) != 0u);
+}
+// bf16 bits of x >= 0 rounded to nearest (ties to even)
+__device__ __forceinline__ uint32_t bf16_rn_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+// squared norm of a 16-byte bf16 row piece, fp32 (only rounded to bf16 later)
+__device__ __forceinline__ float sqnorm8v(u32x4_t u) {
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // through a scalar: this compiler turns a bit_cast of the vector element
+    // u[j] itself into a cast of u[0]
+    const uint32_t wj = u[j];
+    const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, wj);
+    a = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, a, false);
+  }
+  return a;
+}
+__device__ __forceinline__ float sqnorm8(const uint16_t* __restrict__ row, int c0, int dm) {
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (c0 + j < dm) { const float x = bf16_to_f32(row[c0 + j]); a = fmaf(x, x, a); }
+  return a;
 }
 constexpr int SL_LIST = 4096;
 constexpr int SL_U = 8;          // rows in flight per lane group in the distance phase
@@ -725,7 +757,7 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
   int32_t* sd = seeds + ((size_t)bh * 4 + m) * g.Cmax;
   const SeedLLayout L = seedl_layout(N, C, dm);
   extern __shared__ __align__(16) unsigned char seedl_smem[];
-  float* d2s = reinterpret_cast<float*>(seedl_smem + L.d2s);           // [P][NT] slot-major
+  uint32_t* d2s = reinterpret_cast<uint32_t*>(seedl_smem + L.d2s);     // [P][NT] slot-major: D^2 up | norm
   uint16_t* nrs = reinterpret_cast<uint16_t*>(seedl_smem + L.nrs);     // [P][NT]
   int32_t* list = reinterpret_cast<int32_t*>(seedl_smem + L.list);     // [SL_LIST + 1]
   double* tsum = reinterpret_cast<double*>(seedl_smem + L.tsum);       // [NT]
@@ -745,7 +777,7 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
   while (lpr * 8 < dm) lpr <<= 1;
   const uint64_t stream = ((uint64_t)bh * 4 + m) << 20;
 
-  for (int i = threadIdx.x; i < SL_NT * P; i += SL_NT) { d2s[i] = 0.f; nrs[i] = (uint16_t)NR_MARK; }
+  for (int i = threadIdx.x; i < SL_NT * P; i += SL_NT) { d2s[i] = 0u; nrs[i] = (uint16_t)NR_MARK; }
   tsum[threadIdx.x] = 0.0;
   __syncthreads();
 
@@ -835,27 +867,38 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
     }
     __syncthreads();
     // ---- 4. points whose D^2 may change ------------------------------------------------
-    // the fp32 copy is the exact D^2 rounded up, so skipping when the
-    // centre-to-centre distance is at least 4.000008 x that copy is exact
+    // dv (the high half) is the exact D^2 rounded up, so both tests only skip
+    // points whose distance cannot drop:
+    //   Elkan: ||c_s - a||^2 >= 4 dv (the factor 4.000004 covers the product's
+    //     rounding);
+    //   norm: | ||x|| - ||c_s|| | >= |xb - cb| - 2^-7 (xb + cb) =: g, with xb, cb
+    //     the bf16 norms (relative error <= 2^-9 each, plus fp32 rounding), so
+    //     g > 0 and g^2 >= 1.0001 dv imply ||x - c_s||^2 >= D^2.
     uint32_t need = vmask;
     if (s > 0) {
+      const uint32_t cw = d2s[(ci - (ci / P) * P) * SL_NT + ci / P];
+      const float cb = __uint_as_float(cw << 16);
       need = 0;
       for (int k0 = 0; k0 < P; k0 += 8) {
         // eight slots at a time: their LDS reads issue together
-        uint32_t nv[8];
-        float dv[8];
+        uint32_t nv[8], wv8[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int k = min(k0 + u, P - 1);
           nv[u] = nrs[k * SL_NT + tid];
-          dv[u] = d2s[k * SL_NT + tid];
+          wv8[u] = d2s[k * SL_NT + tid];
         }
         double ca[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) ca[u] = cc[nv[u] & NR_ID];
         uint32_t bits = 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) bits |= (uint32_t)!(ca[u] >= 4.000008 * (double)dv[u]) << u;
+        for (int u = 0; u < 8; ++u) {
+          const float dv = __uint_as_float(wv8[u] & 0xFFFF0000u), xb = __uint_as_float(wv8[u] << 16);
+          const float gap = fabsf(xb - cb) - 0x1p-7f * (xb + cb);
+          const bool skip = ca[u] >= 4.000004 * (double)dv || (gap > 0.f && gap * gap >= dv * 1.0001f);
+          bits |= (uint32_t)!skip << u;
+        }
         need |= bits << k0;
       }
       need &= vmask;
@@ -877,6 +920,7 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
         const int c0 = lv ? sub * 8 : 0;
         for (int e0 = slot; e0 < nl; e0 += SL_U * nslot) {
           double acc[SL_U];
+          float xx[SL_U];   // squared norms (first draw only)
           int pp[SL_U];
 #pragma unroll
           for (int u = 0; u < SL_U; ++u) pp[u] = list[min(e0 + u * nslot, nl - 1)];
@@ -889,9 +933,17 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
               b[u] = *reinterpret_cast<const u32x4_t*>(Xb + ((uint32_t)pp[u] * (uint32_t)(2 * d) + (uint32_t)(2 * c0)));
 #pragma unroll
             for (int u = 0; u < SL_U; ++u) acc[u] = sqdist8v(b[u], cvec + c0);
+            if (s == 0) {
+#pragma unroll
+              for (int u = 0; u < SL_U; ++u) xx[u] = lv ? sqnorm8v(b[u]) : 0.f;
+            }
           } else {
 #pragma unroll
             for (int u = 0; u < SL_U; ++u) acc[u] = sqdist8<uint16_t>(X + (size_t)pp[u] * d, cvec, c0, dm);
+            if (s == 0) {
+#pragma unroll
+              for (int u = 0; u < SL_U; ++u) xx[u] = lv ? sqnorm8(X + (size_t)pp[u] * d, c0, dm) : 0.f;
+            }
           }
           double old[SL_U];
 #pragma unroll
@@ -902,13 +954,16 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
 #pragma unroll
           for (int u = 0; u < SL_U; ++u) {
             const double dist = group_sum_dpp(lv ? acc[u] : 0.0, lpr);
+            // norm of the row (first draw): fp32 partial sums, rounded to bf16
+            const float xn = s == 0 ? sqrtf((float)group_sum_dpp((double)xx[u], lpr)) : 0.f;
             const int e = e0 + u * nslot;
             if (sub == 0 && e < nl && (s == 0 || dist < old[u])) {
               const int p = pp[u];
               const int t = p / P, k = p - t * P;
+              const int li = k * SL_NT + t;
               D2g[p] = dist;
-              d2s[k * SL_NT + t] = f32_up(dist);
-              nrs[k * SL_NT + t] = s == 0 ? (uint16_t)0 : (uint16_t)(s | (nrs[k * SL_NT + t] & NR_MARK));
+              d2s[li] = (bf16_up_bits(dist) << 16) | (s == 0 ? bf16_rn_bits(xn) : (d2s[li] & 0xFFFFu));
+              nrs[li] = s == 0 ? (uint16_t)0 : (uint16_t)(s | (nrs[li] & NR_MARK));
               atomicAdd(&tsum[t], dist - old[u]);
             }
           }
@@ -1256,7 +1311,10 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
         const u32x4_t u = __builtin_bit_cast(u32x4_t, b[t][kb]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, u[j]);
+          // through a scalar: a bit_cast of the vector element u[j] itself is
+          // compiled as a cast of u[0]
+          const uint32_t wj = u[j];
+          const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, wj);
           xn2[t] = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, xn2[t], false);
         }
       }

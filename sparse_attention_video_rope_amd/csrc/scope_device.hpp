@@ -66,6 +66,17 @@ __device__ __forceinline__ T wave_min(T v) {
   return v;
 }
 
+// The DPP builtins are not convergent operations for the compiler, so a DPP
+// reduction whose result is only used inside a branch may be sunk into that
+// branch, where the disabled lanes read as 0.  Every DPP helper below ends by
+// passing its result through an empty volatile asm, which keeps the whole
+// reduction where the helper is called.
+template <typename T>
+__device__ __forceinline__ T dpp_pin(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // DPP lane move of an fp64 value (both 32-bit halves; lanes outside the pattern read 0).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
@@ -83,6 +94,7 @@ __device__ __forceinline__ double wave_sum_dpp(double v) {
   v += dpp_f64<0x4E>(v);    // quad_perm [2,3,0,1]
   v += dpp_f64<0x141>(v);   // row_half_mirror
   v += dpp_f64<0x140>(v);   // row_mirror
+  v = dpp_pin(v);
   auto rl = [&](int l) {
     return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
                             __builtin_amdgcn_readlane(__double2loint(v), l));
@@ -97,7 +109,7 @@ __device__ __forceinline__ double group_sum_dpp(double v, int n) {
   if (n >= 4) v += dpp_f64<0x4E>(v);    // xor 2
   if (n >= 8) v += dpp_f64<0x141>(v);   // i <-> 7-i within 8
   if (n >= 16) v += dpp_f64<0x140>(v);  // i <-> 15-i within 16
-  return v;
+  return dpp_pin(v);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave (fixed order).
@@ -136,7 +148,7 @@ __device__ __forceinline__ int wave_incl_scan_dpp(int v) {
   v += dpp_row_i32<0x118, 0xF>(v);
   v += dpp_row_i32<0x142, 0xA>(v);
   v += dpp_row_i32<0x143, 0xC>(v);
-  return v;
+  return dpp_pin(v);
 }
 __device__ __forceinline__ double wave_incl_scan_dpp(double v) {
   v += dpp_row_f64<0x111, 0xF>(v);
@@ -145,7 +157,7 @@ __device__ __forceinline__ double wave_incl_scan_dpp(double v) {
   v += dpp_row_f64<0x118, 0xF>(v);
   v += dpp_row_f64<0x142, 0xA>(v);
   v += dpp_row_f64<0x143, 0xC>(v);
-  return v;
+  return dpp_pin(v);
 }
 
 // Block-wide inclusive scan built on wave_incl_scan_dpp (same caveat on the
