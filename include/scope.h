@@ -104,6 +104,12 @@ typedef struct {
   uint16_t* k_codes;     /* [B*H][N][4] (z^T, z^H, z^W, 0) key subspace codes */
   int32_t* seeds;        /* [B*H][4][max(Cq,Cm)] k-means++ centre indices (Q, T, H, W) */
   double* lut;           /* [B*H][Cq][3][Cm] lookup tables P^m[c][z] (fp64) */
+  float* k_norm_max;     /* [B*H] optional: an upper bound of ||k'_j|| over the keys of each head,
+                            written by scope_plan.  scope_attend uses it to bound the logits of a
+                            query (|<q', k'>| <= ||q'|| ||k'||) and then drops the running maximum
+                            of the online softmax when that bound is tight enough; NULL: the
+                            maximum is always tracked.  It must belong to the k_rope that is
+                            passed to scope_attend (scope_plan_finalize does not write it). */
 } scope_plan_t;
 
 /* Sizes for a parameter set: workspace bytes for scope_plan, the worst-case

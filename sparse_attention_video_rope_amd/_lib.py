@@ -49,7 +49,7 @@ class PlanStruct(ctypes.Structure):
                 ("counts_r", c_void_p), ("k_head", c_void_p), ("sel_off", c_void_p), ("sel_idx", c_void_p),
                 ("sel_capacity", c_int64), ("work", c_void_p), ("work_capacity", c_int64), ("status", c_void_p),
                 ("q_centroids", c_void_p), ("k_centroids", c_void_p), ("q_labels", c_void_p),
-                ("k_codes", c_void_p), ("seeds", c_void_p), ("lut", c_void_p)]
+                ("k_codes", c_void_p), ("seeds", c_void_p), ("lut", c_void_p), ("k_norm_max", c_void_p)]
 
 
 _lib = None
@@ -114,7 +114,8 @@ def _ptr(t) -> Optional[int]:
 class Plan:
     """Caller-owned device buffers of one plan (torch tensors) plus the C struct."""
 
-    def __init__(self, p: Params, device="cuda", debug: bool = True, sel_capacity: Optional[int] = None):
+    def __init__(self, p: Params, device="cuda", debug: bool = True, sel_capacity: Optional[int] = None,
+                 norm_bound: bool = True):
         import torch
         ws, sel_worst, work_cap = sizes(p)
         BH, N, Cq, Cm, d = p.BH, p.N, p.Cq, p.Cm, p.d
@@ -131,6 +132,8 @@ class Plan:
         self.sel_idx = torch.empty(max(cap, 1), **i32)
         self.work = torch.empty(2 * max(work_cap, 1), **i32)
         self.status = torch.zeros(4, **i32)
+        # per-head bound of ||k'|| (lets scope_attend drop the running softmax maximum); None: not provided
+        self.k_norm_max = torch.zeros(BH, dtype=torch.float32, device=device) if norm_bound else None
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
         self.debug = debug
         if debug:
@@ -144,7 +147,7 @@ class Plan:
             self.q_centroids = self.k_centroids = self.q_labels = self.k_codes = self.seeds = self.lut = None
         s = PlanStruct()
         for name in ("perm_q", "q_off", "counts_t", "counts_b", "counts_r", "k_head", "sel_off", "sel_idx", "work",
-                     "status", "q_centroids", "k_centroids", "q_labels", "k_codes", "seeds", "lut"):
+                     "status", "q_centroids", "k_centroids", "q_labels", "k_codes", "seeds", "lut", "k_norm_max"):
             setattr(s, name, _ptr(getattr(self, name)))
         s.sel_capacity = cap
         s.work_capacity = work_cap

@@ -73,8 +73,9 @@ template <int D, int WPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void attend_bf16_lds_kernel(
     AttArgs a, const int32_t* __restrict__ work, const int32_t* __restrict__ status,
     const int32_t* __restrict__ perm_q, const int32_t* __restrict__ q_off, const int32_t* __restrict__ cr,
-    const int64_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, const uint16_t* __restrict__ qr,
-    const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vv, uint16_t* __restrict__ out) {
+    const int64_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, const float* __restrict__ knm,
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vv,
+    uint16_t* __restrict__ out) {
   constexpr int NW = 4;
   constexpr int BM = 32 * NW;
   static_assert(BM == ATT_BM, "queries per workgroup must equal the work-list chunk");
@@ -127,6 +128,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const float cs = a.scale_log2;
   const int nchunks = (r + BN - 1) / BN;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // upper bound of this query's logits <q', k'_j> (before the 1/sqrt(d) scale):
+  // ||q'|| (fp32 sum of exact bf16 squares) times the head's key-norm bound,
+  // with a factor 1 + 2^-12 for the roundings; negative when there is no bound
+  float bound = -1.f;
+  {
+    float qn2 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      const u32x4_t u = __builtin_bit_cast(u32x4_t, qb[kb]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t wj = u[j];   // through a scalar (a bit_cast of u[j] compiles as u[0])
+        const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, wj);
+        qn2 = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, qn2, false);
+      }
+    }
+    qn2 += __shfl_xor(qn2, 32);
+    const float kb_ = knm ? knm[bh] : -1.f;
+    if (kb_ > 0.f) bound = sqrtf(qn2) * kb_ * (1.f + 0x1p-12f);
+  }
 
   auto kswz = [](int j) { return D == 64 ? (j >> 1) & 7 : j & (PR - 1); };
   auto vswz = [](int j) { return (D / 32) * (j & 3); };
@@ -172,6 +193,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
   }
 
+  // fixed (wave-uniform): the softmax reference mref is final, no running
+  // maximum is kept; see the switch after the first chunk below
+  bool fixed = false;
   auto step = [&](int kc, lds_u16* Kc, lds_u16* Vc, lds_u16* Kn, lds_u16* Vn) {
     if (kc + 1 < nchunks) {
       gather(Kn, Vn);                              // rows of chunk kc+1
@@ -196,20 +220,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           for (int v = 0; v < 16; ++v)
             if (st * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kleft) s[st][v] = -__builtin_inff();
       }
-      float mloc = fmaxf(s[0][0], s[0][1]);
+      if (!fixed) {
+        float mloc = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-      for (int e = 2; e < 32; e += 2) mloc = fmaxf(fmaxf(mloc, s[e >> 4][e & 15]), s[e >> 4][(e + 1) & 15]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const bool grow_m = (mloc - mref) * cs > RESCALE_LOG2;
-      if (__ballot(grow_m)) {
-        const float mnew = grow_m ? mloc : mref;
-        const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * cs);
-        lsum *= alpha;
+        for (int e = 2; e < 32; e += 2) mloc = fmaxf(fmaxf(mloc, s[e >> 4][e & 15]), s[e >> 4][(e + 1) & 15]);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const bool grow_m = (mloc - mref) * cs > RESCALE_LOG2;
+        if (__ballot(grow_m)) {
+          const float mnew = grow_m ? mloc : mref;
+          const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * cs);
+          lsum *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+          for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
-        mref = mnew;
+            for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+          mref = mnew;
+        }
       }
       const float mc = mref * cs;
 #pragma unroll
@@ -255,8 +281,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   // path, so the loop starts with no loads outstanding
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // After the first chunk mref is its maximum m0 <= max_j s_j <= bound.  If
+  // (bound - m0) cs <= 124 for every query of the wave, the reference becomes
+  // mref = max(m0, bound - 60 / cs) for the rest of the item: every later
+  // weight is exp2((s - mref) cs) <= 2^60 (no overflow), and the largest one
+  // is >= 2^-64 (the fp32 / bf16 exponent range keeps every weight that is
+  // not negligible next to it), so the chunk maximum is no longer needed.
+  auto decide = [&]() {
+    if (nchunks < 2 || !active) return;
+    const bool ok = !qvalid || (bound >= mref && (bound - mref) * cs <= 124.f);
+    // the decision is wave-uniform; it is handed over in a VGPR the compiler
+    // cannot see through, so the branches on it compile as exec-masked
+    // regions that update O in place (as a uniform branch, the accumulators
+    // were copied between register sets on every chunk)
+    int fv = __ballot(!ok) == 0 ? 1 : 0;
+    asm volatile("" : "+v"(fv));
+    fixed = fv != 0;
+    if (fixed) {
+      const float mnew = qvalid ? fmaxf(mref, bound - 60.f / cs) : mref;
+      const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * cs);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+      mref = mnew;
+    }
+  };
   for (int kc = 0; kc < nchunks; kc += 2) {
     step(kc, K0, V0, K1, V1);
+    if (kc == 0) decide();
     if (kc + 1 < nchunks) step(kc + 1, K1, V1, K0, V0);
   }
   const float ltot = lsum + __shfl_xor(lsum, 32);
@@ -284,6 +338,7 @@ __global__ __launch_bounds__(ATT_BM) void attend_f32_kernel(AttArgs a, const int
                                                             const int32_t* __restrict__ cr,
                                                             const int64_t* __restrict__ sel_off,
                                                             const int32_t* __restrict__ sel_idx,
+                                                            const float* __restrict__ /*knm: unused*/,
                                                             const float* __restrict__ qr, const float* __restrict__ kr,
                                                             const float* __restrict__ vv, float* __restrict__ out) {
   if (status[1]) return;
@@ -325,11 +380,12 @@ hipError_t launch_attend(const Geo& g, const scope_plan_t& plan, const void* qr,
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   if (plan.work_capacity == 0) return hipSuccess;
   const unsigned grid = (unsigned)plan.work_capacity;
-#define SCOPE_ATT_ARGS a, plan.work, plan.status, plan.perm_q, plan.q_off, plan.counts_r, plan.sel_off, plan.sel_idx
+#define SCOPE_ATT_ARGS \
+  a, plan.work, plan.status, plan.perm_q, plan.q_off, plan.counts_r, plan.sel_off, plan.sel_idx, plan.k_norm_max
   if (g.bf16) {
-    // 4 waves x 32 queries; head dim 64 fits 128 VGPRs (4 waves per SIMD)
+    // 4 waves x 32 queries; 3 (d = 64) or 2 (d = 128) waves per SIMD
     if (g.d == 64)
-      attend_bf16_lds_kernel<64, 4><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
+      attend_bf16_lds_kernel<64, 3><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
                                                          (const uint16_t*)v, (uint16_t*)out);
     else
       attend_bf16_lds_kernel<128, 2><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,

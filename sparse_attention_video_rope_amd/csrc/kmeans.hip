@@ -10,6 +10,7 @@
 // the fp64 arithmetic below is order-independent; the MFMA assignment is a
 // filter whose near-ties are re-decided with exact fp64 distances.
 #include <float.h>
+#include <type_traits>
 
 #include "scope_device.hpp"
 #include "scope_internal.hpp"
@@ -1402,6 +1403,9 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
   }
 }
 
+// KBMAX: the largest dpad / 16 of the launch; the kernel's register budget is
+// that of its widest instantiated tile loop, so narrow heads get a narrow kernel.
+template <int KBMAX>
 __global__ __launch_bounds__(ASG_NT) void assign2_kernel(const uint16_t* __restrict__ qr,
                                                          const uint16_t* __restrict__ kr, Geo g,
                                                          const uint16_t* __restrict__ cbf,
@@ -1438,16 +1442,20 @@ __global__ __launch_bounds__(ASG_NT) void assign2_kernel(const uint16_t* __restr
   int32_t* lab = labels + ((size_t)bh * 4 + m) * N;
   const int gw = blockIdx.x * (ASG_NT / 64) + wv, gstride = gridDim.x * (ASG_NT / 64);
   double* xs = xsh + wv * 128;
-  switch (dpad / 16) {
-    case 1: assign_tiles<1>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
-    case 2: assign_tiles<2>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
-    case 3: assign_tiles<3>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
-    case 4: assign_tiles<4>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
-    case 5: assign_tiles<5>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
-    case 6: assign_tiles<6>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
-    case 7: assign_tiles<7>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
-    default: assign_tiles<8>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride); break;
-  }
+  const int kbn = dpad / 16;
+  auto run = [&](auto kb) {
+    constexpr int KB = decltype(kb)::value;
+    if constexpr (KB <= KBMAX)
+      if (kbn == KB) assign_tiles<KB>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride);
+  };
+  run(std::integral_constant<int, 1>{});
+  run(std::integral_constant<int, 2>{});
+  run(std::integral_constant<int, 3>{});
+  run(std::integral_constant<int, 4>{});
+  run(std::integral_constant<int, 5>{});
+  run(std::integral_constant<int, 6>{});
+  run(std::integral_constant<int, 7>{});
+  run(std::integral_constant<int, 8>{});
 }
 
 // ---- launchers --------------------------------------------------------------
@@ -1534,9 +1542,15 @@ hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Wor
     int parts = (2048 + 4 * g.BH - 1) / (4 * g.BH);
     parts = max(1, min(parts, (ntiles + 3) / 4));
     dim3 grid(parts, 4, g.BH);
-    if (lds > 64 * 1024)
-      (void)hipFuncSetAttribute((const void*)assign2_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    assign2_kernel<<<grid, ASG_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, w.labels);
+    int kbmax = 1;
+    for (int m = 0; m < 4; ++m) kbmax = max(kbmax, g.dpad[m] / 16);
+    auto go = [&](auto kern) {
+      if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      kern<<<grid, ASG_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, w.labels);
+    };
+    if (kbmax <= 2) go(assign2_kernel<2>);
+    else if (kbmax <= 4) go(assign2_kernel<4>);
+    else go(assign2_kernel<8>);
   } else {
     dim3 grid((g.N + 255) / 256, 4, g.BH);
     assign_exact_f32_kernel<<<grid, 256, 0, s>>>((const float*)qr, (const float*)kr, g, w.qcent, w.kcent, w.labels);

@@ -49,14 +49,21 @@ template <> struct Vec8<float> {
 
 // One thread rotates 8 consecutive channels (4 pairs) of one token of Q or K.
 // Grid: x over the tokens x (d/8) chunks of one head, y over heads, z over Q / K, so
-// all index arithmetic is 32-bit (d/8 is 8 or 16: a shift).
+// all index arithmetic is 32-bit (d/8 is 8 or 16: a shift).  For K, knm (if set)
+// receives an upper bound of the head's largest ||k'|| over the stored
+// (rounded) rows: the fp32 norm times 1 + 2^-12 (which covers the rounding of
+// the fp32 sum and the square root), as float bits via atomicMax (zeroed
+// beforehand; non-negative floats order like their bits).
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    T* __restrict__ qo, T* __restrict__ ko,
-                                                   const double2* __restrict__ tab, RopeArgs a) {
+                                                   const double2* __restrict__ tab, RopeArgs a,
+                                                   uint32_t* __restrict__ knm) {
+  __shared__ float red[256 / 64];
   const int cshift = a.d == 128 ? 4 : 3;
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;   // token * (d/8) + chunk
-  if (r >= (a.N << cshift)) return;
+  const int r0 = blockIdx.x * blockDim.x + threadIdx.x;   // token * (d/8) + chunk
+  const bool valid = r0 < (a.N << cshift);
+  const int r = valid ? r0 : 0;
   const int sel = blockIdx.z, bh = blockIdx.y;
   const int chunk = r & ((1 << cshift) - 1);
   const int n = r >> cshift;
@@ -83,11 +90,20 @@ __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, cons
     Elem<T>::st(&x.v[2 * pi], y0);
     Elem<T>::st(&x.v[2 * pi + 1], y1);
   }
-  x.store((sel ? ko : qo) + base);
+  if (valid) x.store((sel ? ko : qo) + base);
+  if (sel && knm) {
+    // squared norm of the token: its d/8 threads are consecutive lanes
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { const float e = (float)Elem<T>::ld(&x.v[i]); ss = fmaf(e, e, ss); }
+    ss = (float)group_sum_dpp(valid ? (double)ss : 0.0, 1 << cshift);
+    const float mx = block_max<float, 256>(ss, red);
+    if (threadIdx.x == 0) atomicMax(&knm[bh], __float_as_uint(sqrtf(mx) * (1.0f + 0x1p-12f)));
+  }
 }
 
 hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const void* k, void* qo,
-                       void* ko, const Workspace& w, hipStream_t s) {
+                       void* ko, const Workspace& w, float* k_norm_max, hipStream_t s) {
   const int n0 = g.T * g.dm[1] / 2, n1 = g.Hg * g.dm[2] / 2, n2 = g.Wg * g.dm[3] / 2;
   rope_table_kernel<<<(n0 + n1 + n2 + 255) / 256, 256, 0, s>>>(w.rope_tab, n0, n1, n2, g.dm[1], g.dm[2],
                                                                g.dm[3], p.rope_base);
@@ -97,12 +113,17 @@ hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const
   a.dm[0] = g.dm[1]; a.dm[1] = g.dm[2]; a.dm[2] = g.dm[3];
   a.toff[0] = 0; a.toff[1] = n0; a.toff[2] = n0 + n1;
   const dim3 blocks((unsigned)((g.N * (g.d / 8) + 255) / 256), (unsigned)g.BH, 2);
+  uint32_t* knm = reinterpret_cast<uint32_t*>(k_norm_max);
+  if (knm) {
+    const hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(knm), 0, (size_t)g.BH, s);
+    if (e != hipSuccess) return e;
+  }
   if (g.bf16)
     rope_kernel<uint16_t><<<blocks, 256, 0, s>>>((const uint16_t*)q, (const uint16_t*)k, (uint16_t*)qo,
-                                                 (uint16_t*)ko, w.rope_tab, a);
+                                                 (uint16_t*)ko, w.rope_tab, a, knm);
   else
     rope_kernel<float><<<blocks, 256, 0, s>>>((const float*)q, (const float*)k, (float*)qo, (float*)ko,
-                                              w.rope_tab, a);
+                                              w.rope_tab, a, knm);
   return hipGetLastError();
 }
 

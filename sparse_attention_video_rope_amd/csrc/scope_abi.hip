@@ -157,6 +157,7 @@ scope_status scope_plan(const scope_params* p, const void* q, const void* k, voi
   const void* opt[] = {plan->q_centroids, plan->k_centroids, plan->q_labels, plan->k_codes, plan->seeds, plan->lut};
   for (const void* o : opt)
     if (o && !aligned(o, 8)) return SCOPE_ERR_INVALID;
+  if (plan->k_norm_max && !aligned(plan->k_norm_max, 4)) return SCOPE_ERR_INVALID;
   if ((p->flags & SCOPE_USE_INIT_CENTROIDS) && (!plan->q_centroids || !plan->k_centroids)) return SCOPE_ERR_INVALID;
   const Geo g = make_geo(*p);
   if (plan->work_capacity < work_cap(g)) return SCOPE_ERR_CAPACITY;
@@ -165,7 +166,7 @@ scope_status scope_plan(const scope_params* p, const void* q, const void* k, voi
 
   hipError_t e = hipSuccess;
 #define STEP(x) do { e = (x); if (e != hipSuccess) return hip_status(e); } while (0)
-  STEP(launch_rope(g, *p, q, k, q_rope, k_rope, w, stream));
+  STEP(launch_rope(g, *p, q, k, q_rope, k_rope, w, plan->k_norm_max, stream));
   if (!(p->flags & SCOPE_USE_INIT_CENTROIDS)) STEP(launch_seed(g, q_rope, k_rope, w, stream));
   STEP(launch_prep(g, w, stream));
   STEP(launch_assign(g, q_rope, k_rope, w, 0, stream));

@@ -78,7 +78,7 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base);
 
 // ---- launchers (return hipGetLastError()) ---------------------------------
 hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const void* k, void* qo,
-                       void* ko, const Workspace& w, hipStream_t s);
+                       void* ko, const Workspace& w, float* k_norm_max, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_seed(const Geo& g, const void* qr, const void* kr, const Workspace& w, hipStream_t s);
 hipError_t launch_prep(const Geo& g, const Workspace& w, hipStream_t s);

@@ -3,6 +3,7 @@ point, and rejects bad parameters before any launch."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -27,10 +28,29 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
-def test_struct_layout_matches_header():
-    # 12 int32, 3 double, uint64, int32, uint32 -> 88 bytes; plan: 18 pointer-sized fields
+def test_struct_layout_matches_header(tmp_path):
+    """Every field of the ctypes mirrors sits at the offset the C compiler gives it in include/scope.h."""
     assert ctypes.sizeof(_lib.Params) == 88
-    assert ctypes.sizeof(_lib.PlanStruct) == 18 * 8
+    structs = {"scope_params": _lib.Params, "scope_plan_t": _lib.PlanStruct}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "scope.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.dirname(HEADER), "-I", "/opt/rocm/include", str(src), "-o", str(exe)],
+                   check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        cname, fname, val = line.split()
+        got[(cname, fname)] = int(val)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
 
 
 def test_status_strings():

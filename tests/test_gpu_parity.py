@@ -127,6 +127,34 @@ def test_attend_on_oracle_plan(w, rho):
         say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
 
 
+BF16_SMALL = [w for w in SMALL if w.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("w", BF16_SMALL, ids=[w.name for w in BF16_SMALL])
+def test_attend_softmax_reference_paths(w):
+    """The per-head key-norm bound written by scope_plan, and all three softmax paths of the
+    attention kernel: fixed reference (bound given and tight), running maximum (no bound), and
+    running maximum after a rejected bound (10^4 times too loose)."""
+    say("softmax paths", w.name)
+    heads = oracle_heads(w)
+    q, k, v = workloads.generate(w)
+    p = sav.params_for(w)
+    pl = sav.Plan(p, debug=False)
+    qr, kr, pl = sav.plan(p, to_dev(q, w.dtype), to_dev(k, w.dtype), pl)
+    kn = pl.k_norm_max.clone()
+    for bh, h in enumerate(heads):
+        exact = float(np.sqrt((h["k_rope"] ** 2).sum(1)).max())
+        got = float(kn[bh])
+        assert exact <= got <= exact * (1 + 2**-10), (bh, got, exact)
+    vd = to_dev(v, w.dtype)
+    for name, scale in (("bound", 1.0), ("no bound", 0.0), ("loose bound", 1e4)):
+        pl.k_norm_max.copy_(kn * scale)
+        out = to_np(sav.attend(p, pl, qr, kr, vd)).reshape(w.BH, w.N, w.d)
+        for bh, h in enumerate(heads):
+            mx, mn = assert_attention(out[bh], h["out"], w.dtype, f"{w.name} head {bh} ({name})")
+            say(f"  {name} head {bh}: max {mx:.2e} mean {mn:.2e}")
+
+
 def assert_plan_equal(w, g, heads):
     """End-to-end plan equality (exact) on every head."""
     for bh, o in enumerate(heads):
