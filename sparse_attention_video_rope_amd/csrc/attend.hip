@@ -121,16 +121,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       qb[kb] = __builtin_bit_cast(bf16x8_t, u);
     }
   }
+  // Q scaled by log2(e) / sqrt(d) (rounded to bf16), so the QK^T product gives
+  // the logits in log2 units and the softmax weight of a logit t is exp2(t -
+  // mref); the MFMA accumulator starts at -mref, so the product yields
+  // t - mref directly
+  const float cs = a.scale_log2;
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    const u32x4_t u = __builtin_bit_cast(u32x4_t, qb[kb]);
+    u32x4_t w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t wj = u[j];   // through a scalar (a bit_cast of u[j] compiles as u[0])
+      const f32x2_t f = __builtin_convertvector(__builtin_bit_cast(bf16x2_t, wj), f32x2_t) * cs;
+      w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+    }
+    qb[kb] = __builtin_bit_cast(bf16x8_t, w);
+  }
   f32x16_t o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
-  float mref = -__builtin_inff(), lsum = 0.f;
-  const float cs = a.scale_log2;
+  float mref = 0.f, lsum = 0.f;    // reference (log2 units); set from the first chunk
+  f32x16_t cneg = {};              // -mref in every element: the QK^T accumulator's start
   const int nchunks = (r + BN - 1) / BN;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  // upper bound of this query's logits <q', k'_j> (before the 1/sqrt(d) scale):
-  // ||q'|| (fp32 sum of exact bf16 squares) times the head's key-norm bound,
-  // with a factor 1 + 2^-12 for the roundings; negative when there is no bound
+  // upper bound of this query's scaled logits <q'', k'_j> (q'' the scaled bf16
+  // row): ||q''|| (fp32 sum of exact bf16 squares) times the head's key-norm
+  // bound, with a factor 1 + 2^-12 for the roundings; negative when there is
+  // no bound
   float bound = -1.f;
   {
     float qn2 = 0.f;
@@ -208,7 +226,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         bf16x8_t ak[D / 16];
 #pragma unroll
         for (int kb = 0; kb < D / 16; ++kb) ak[kb] = *(const lds_bf16x8*)(Kc + kro[kb] + st * 32 * D);
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], qb[0], f32x16_t{}, 0, 0, 0);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], qb[0], cneg, 0, 0, 0);
 #pragma unroll
         for (int kb = 1; kb < D / 16; ++kb) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kb], qb[kb], s[st], 0, 0, 0);
       }
@@ -221,23 +239,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
             if (st * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kleft) s[st][v] = -__builtin_inff();
       }
       if (!fixed) {
+        // running maximum: s holds logits minus mref; the first chunk sets
+        // the reference to its maximum, a later one raises it when its
+        // maximum exceeds it by more than RESCALE_LOG2
         float mloc = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
         for (int e = 2; e < 32; e += 2) mloc = fmaxf(fmaxf(mloc, s[e >> 4][e & 15]), s[e >> 4][(e + 1) & 15]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const bool grow_m = (mloc - mref) * cs > RESCALE_LOG2;
+        const bool first = kc == 0;
+        const bool grow_m = first || mloc > RESCALE_LOG2;
         if (__ballot(grow_m)) {
-          const float mnew = grow_m ? mloc : mref;
-          const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * cs);
+          const float dm = grow_m ? mloc : 0.f;
+          const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-dm);
           lsum *= alpha;
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
-          mref = mnew;
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[st][v] -= dm;
+          mref += dm;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) cneg[v] = -mref;
         }
       }
-      const float mc = mref * cs;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -245,8 +272,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           bf16x2_t pk[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][half * 8 + 2 * i], cs, -mc));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][half * 8 + 2 * i + 1], cs, -mc));
+            const float p0 = __builtin_amdgcn_exp2f(s[st][half * 8 + 2 * i]);
+            const float p1 = __builtin_amdgcn_exp2f(s[st][half * 8 + 2 * i + 1]);
             pk[i] = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
             lsum = __builtin_amdgcn_fdot2_f32_bf16(pk[i], ones, lsum, false);
           }
@@ -281,15 +308,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   // path, so the loop starts with no loads outstanding
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // After the first chunk mref is its maximum m0 <= max_j s_j <= bound.  If
-  // (bound - m0) cs <= 124 for every query of the wave, the reference becomes
-  // mref = max(m0, bound - 60 / cs) for the rest of the item: every later
-  // weight is exp2((s - mref) cs) <= 2^60 (no overflow), and the largest one
-  // is >= 2^-64 (the fp32 / bf16 exponent range keeps every weight that is
-  // not negligible next to it), so the chunk maximum is no longer needed.
+  // After the first chunk mref is its maximum m0 <= max_j t_j <= bound (t the
+  // scaled logits).  If bound - m0 <= 124 for every query of the wave, the
+  // reference becomes mref = max(m0, bound - 60) for the rest of the item:
+  // every later weight is exp2(t - mref) <= 2^60 (no overflow), and the
+  // largest one is >= 2^-64 (the fp32 / bf16 exponent range keeps every weight
+  // that is not negligible next to it), so the chunk maximum is no longer
+  // needed.
   auto decide = [&]() {
     if (nchunks < 2 || !active) return;
-    const bool ok = !qvalid || (bound >= mref && (bound - mref) * cs <= 124.f);
+    const bool ok = !qvalid || (bound >= mref && bound - mref <= 124.f);
     // the decision is wave-uniform; it is handed over in a VGPR the compiler
     // cannot see through, so the branches on it compile as exec-masked
     // regions that update O in place (as a uniform branch, the accumulators
@@ -298,14 +326,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     asm volatile("" : "+v"(fv));
     fixed = fv != 0;
     if (fixed) {
-      const float mnew = qvalid ? fmaxf(mref, bound - 60.f / cs) : mref;
-      const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * cs);
+      const float mnew = qvalid ? fmaxf(mref, bound - 60.f) : mref;
+      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
       mref = mnew;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) cneg[v] = -mref;
     }
   };
   for (int kc = 0; kc < nchunks; kc += 2) {
