@@ -232,11 +232,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       }
       const int kleft = r - kc * BN;
       if (kleft < BN) {
+        // key offset of this lane's rows, made opaque here so that the 32 key
+        // positions are formed in this (last-chunk) branch instead of being
+        // kept live in registers across the loop
+        int k4 = 4 * hi;
+        asm volatile("" : "+v"(k4));
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            if (st * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kleft) s[st][v] = -__builtin_inff();
+            if (st * 32 + 8 * (v >> 2) + (v & 3) + k4 >= kleft) s[st][v] = -__builtin_inff();
       }
       if (!fixed) {
         // running maximum: s holds logits minus mref; the first chunk sets
