@@ -14,6 +14,8 @@ struct RopeArgs {
   int BH, N, d, Hg, Wg;
   int off1, off2;               // start of the H and W ranges
   int dm[3], toff[3];
+  uint64_t mhw, mw;             // ceil(2^32 / (Hg Wg)), ceil(2^32 / Wg): n / x = (n * m) >> 32 for n x < 2^32
+  int magic;                    // the token count allows that division
 };
 
 __global__ void rope_table_kernel(double2* tab, int n0, int n1, int n2, int dm0, int dm1, int dm2,
@@ -47,6 +49,30 @@ template <> struct Vec8<float> {
   }
 };
 
+// Round the 8 fp64 results to the storage type.  bf16: round to nearest even
+// at mantissa bit 45 of the fp64 value (then exact as fp32), which is correct
+// for every result of magnitude >= 2^-126 or zero; a wave with any other
+// result takes the general conversion for all its values.
+__device__ __forceinline__ void store_rounded(Vec8<float>& x, const double (&y)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x.v[i] = (float)y[i];
+}
+__device__ __forceinline__ void store_rounded(Vec8<uint16_t>& x, const double (&y)[8]) {
+  bool odd = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint64_t u = (uint64_t)__double_as_longlong(y[i]);
+    u += 0x0FFFFFFFFFFFull + ((u >> 45) & 1ull);
+    u &= ~0x1FFFFFFFFFFFull;
+    x.v[i] = (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
+    odd |= !(fabs(y[i]) >= 0x1p-126) && y[i] != 0.0;
+  }
+  if (__ballot(odd)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x.v[i] = f64_to_bf16(y[i]);
+  }
+}
+
 // One thread rotates 8 consecutive channels (4 pairs) of one token of Q or K.
 // Grid: x over the tokens x (d/8) chunks of one head, y over heads, z over Q / K, so
 // all index arithmetic is 32-bit (d/8 is 8 or 16: a shift).  For K, knm (if set)
@@ -68,28 +94,38 @@ __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, cons
   const int chunk = r & ((1 << cshift) - 1);
   const int n = r >> cshift;
   const int hw = a.Hg * a.Wg;
-  const int t = n / hw, rem = n - t * hw;
-  const int hh = rem / a.Wg, ww = rem - hh * a.Wg;
-  const int pos[3] = {t, hh, ww};
+  int t, hh;
+  if (a.magic) {
+    t = (int)(((uint64_t)(uint32_t)n * a.mhw) >> 32);
+    hh = (int)(((uint64_t)(uint32_t)(n - t * hw) * a.mw) >> 32);
+  } else {
+    t = n / hw;
+    hh = (n - t * hw) / a.Wg;
+  }
+  const int rem = n - t * hw, ww = rem - hh * a.Wg;
   const size_t base = ((size_t)bh * a.N + n) * a.d + chunk * 8;
   Vec8<T> x;
   x.load((sel ? k : q) + base);
+  double y[8];
 #pragma unroll
   for (int pi = 0; pi < 4; ++pi) {
     const int ch = chunk * 8 + 2 * pi;
-    const int m = ch < a.off1 ? 0 : (ch < a.off2 ? 1 : 2);
-    const int o = m == 0 ? 0 : (m == 1 ? a.off1 : a.off2);
-    const double2 cs = tab[a.toff[m] + pos[m] * (a.dm[m] / 2) + (ch - o) / 2];
+    // range of the pair, by selects (a runtime index into the argument struct
+    // would load it from memory)
+    const bool r0 = ch < a.off1, r1 = ch < a.off2;
+    const int o = r0 ? 0 : (r1 ? a.off1 : a.off2);
+    const int tof = r0 ? a.toff[0] : (r1 ? a.toff[1] : a.toff[2]);
+    const int hd = r0 ? a.dm[0] / 2 : (r1 ? a.dm[1] / 2 : a.dm[2] / 2);
+    const int ps = r0 ? t : (r1 ? hh : ww);
+    const double2 cs = tab[tof + ps * hd + (ch - o) / 2];
     const double x0 = Elem<T>::ld(&x.v[2 * pi]), x1 = Elem<T>::ld(&x.v[2 * pi + 1]);
-    double y0, y1;
     {
 #pragma clang fp contract(off)
-      y0 = x0 * cs.x - x1 * cs.y;
-      y1 = x0 * cs.y + x1 * cs.x;
+      y[2 * pi] = x0 * cs.x - x1 * cs.y;
+      y[2 * pi + 1] = x0 * cs.y + x1 * cs.x;
     }
-    Elem<T>::st(&x.v[2 * pi], y0);
-    Elem<T>::st(&x.v[2 * pi + 1], y1);
   }
+  store_rounded(x, y);
   if (valid) x.store((sel ? ko : qo) + base);
   if (sel && knm) {
     // squared norm of the token: its d/8 threads are consecutive lanes
@@ -112,6 +148,10 @@ hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const
   a.off1 = g.off[2]; a.off2 = g.off[3];
   a.dm[0] = g.dm[1]; a.dm[1] = g.dm[2]; a.dm[2] = g.dm[3];
   a.toff[0] = 0; a.toff[1] = n0; a.toff[2] = n0 + n1;
+  const uint64_t hw = (uint64_t)g.Hg * g.Wg;
+  a.mhw = ((1ull << 32) + hw - 1) / hw;
+  a.mw = ((1ull << 32) + g.Wg - 1) / (uint64_t)g.Wg;
+  a.magic = (uint64_t)g.N * hw < (1ull << 32) ? 1 : 0;
   const dim3 blocks((unsigned)((g.N * (g.d / 8) + 255) / 256), (unsigned)g.BH, 2);
   uint32_t* knm = reinterpret_cast<uint32_t*>(k_norm_max);
   if (knm) {
