@@ -1193,27 +1193,138 @@ __global__ __launch_bounds__(ACC_NT) void accum_kernel(const T* __restrict__ qr,
   }
 }
 
+// Changes of the sums: every point whose label differs from the previous
+// assignment's adds its channel values (fp64, exact) to its new cluster and
+// subtracts them from its old one; the sizes change by one each.  Same grid
+// and LDS table as accum_kernel; the nonzero entries of the table are then
+// added to the totals in global memory (fp64 atomics; exact, so in any
+// order).  A wave takes 64 points at a time (their labels loaded one step
+// ahead), lists the changed ones (lane numbers, in LDS) and loads their rows
+// in batches of 8 instructions (64 / SW points each: lanes = channels) before
+// adding them.
+template <int SW>
+__global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __restrict__ qr,
+                                                             const uint16_t* __restrict__ kr, Geo g,
+                                                             const int32_t* __restrict__ labels,
+                                                             const int32_t* __restrict__ prev,
+                                                             double* __restrict__ stot, int32_t* __restrict__ ntot,
+                                                             int parts) {
+  const int part = blockIdx.x, bh = blockIdx.z;
+  int m = 0, sl = blockIdx.y;
+  while (m < 3 && sl >= (g.dm[m] + SW - 1) / SW) { sl -= (g.dm[m] + SW - 1) / SW; ++m; }
+  const int N = g.N, d = g.d, dm = g.dm[m], C = g.C[m];
+  const int s0 = sl * SW, sw = min(SW, dm - s0);
+  if (sw <= 0) return;
+  extern __shared__ __align__(16) unsigned char acc_smem[];
+  double* S = reinterpret_cast<double*>(acc_smem);                         // [C][SW]
+  int32_t* cnt = reinterpret_cast<int32_t*>(acc_smem + (size_t)C * SW * 8);  // [C]
+  __shared__ int32_t wlist[ACC_NT / 64][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < C * SW; i += ACC_NT) S[i] = 0.0;
+  for (int i = tid; i < C; i += ACC_NT) cnt[i] = 0;
+  __syncthreads();
+  const int per = (N + parts - 1) / parts;
+  const int p0 = min(N, part * per), p1 = min(N, p0 + per);
+  const int32_t* lab = labels + ((size_t)bh * 4 + m) * N;
+  const int32_t* prv = prev + ((size_t)bh * 4 + m) * N;
+  const uint16_t* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + g.off[m] + s0;
+  constexpr int G = 64 / SW, U = 8;
+  const int j = lane / SW, ch = lane % SW;
+  const bool chv = ch < sw;
+  int Ln_ = lab[min(p0 + wv * 64 + lane, N - 1)], Lp_ = prv[min(p0 + wv * 64 + lane, N - 1)];
+  for (int c0 = p0 + wv * 64; c0 < p1; c0 += ACC_NT) {
+    const int p = c0 + lane;
+    const bool ok = p < p1;
+    const int L = min(max(Ln_, 0), C - 1), Lp = min(max(Lp_, 0), C - 1);
+    // labels of the next 64 points, in flight during this step
+    Ln_ = lab[min(c0 + ACC_NT + lane, N - 1)];
+    Lp_ = prv[min(c0 + ACC_NT + lane, N - 1)];
+    const bool c = ok && L != Lp;
+    const uint64_t mk = __ballot(c);
+    const int nchg = (int)__popcll(mk);
+    if (nchg == 0) continue;
+    if (c) wlist[wv][__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = lane;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int b = 0; b < nchg; b += U * G) {
+      float xv[U];
+      int ln[U], lo[U];
+      bool vv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = b + u * G + j;
+        vv[u] = idx < nchg;
+        const int q = vv[u] ? wlist[wv][idx] : 0;
+        ln[u] = __shfl(L, q);
+        lo[u] = __shfl(Lp, q);
+        xv[u] = (vv[u] && chv) ? bf16_to_f32(X[(size_t)(c0 + q) * d + ch]) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (vv[u] && chv) {
+          atomicAdd(&S[ln[u] * SW + ch], (double)xv[u]);
+          atomicAdd(&S[lo[u] * SW + ch], -(double)xv[u]);
+        }
+        if (vv[u] && sl == 0 && ch == 0) {
+          atomicAdd(&cnt[ln[u]], 1);
+          atomicAdd(&cnt[lo[u]], -1);
+        }
+      }
+    }
+    // the list is rewritten for the next 64 points
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  __syncthreads();
+  double* st = stot + ((size_t)bh * 4 + m) * g.Cmax * d + s0;
+  for (int i = tid; i < C * SW; i += ACC_NT) {
+    const double v = S[i];
+    if (v != 0.0) atomicAdd(&st[(size_t)(i / SW) * d + i % SW], v);
+  }
+  if (sl == 0) {
+    int32_t* nt = ntot + ((size_t)bh * 4 + m) * g.Cmax;
+    for (int i = tid; i < C; i += ACC_NT)
+      if (cnt[i] != 0) atomicAdd(&nt[i], cnt[i]);
+  }
+}
+
 __global__ __launch_bounds__(256) void finalize_kernel(Geo g, const double* __restrict__ psum,
                                                        const int32_t* __restrict__ pcnt, int SW, int nslices,
-                                                       int parts, float* __restrict__ qcent, float* __restrict__ kcent,
-                                                       uint16_t* __restrict__ cbf, float* __restrict__ cnorm) {
+                                                       int parts, int delta, double* __restrict__ stot,
+                                                       int32_t* __restrict__ ntot, float* __restrict__ qcent,
+                                                       float* __restrict__ kcent, uint16_t* __restrict__ cbf,
+                                                       float* __restrict__ cnorm) {
   const int m = blockIdx.y, bh = blockIdx.z;
   const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (c >= g.C[m]) return;
   const int d = g.d, dm = g.dm[m], lane = threadIdx.x & 63;
+  // totals: the sum of the partials, kept for the next update; with `delta`
+  // the totals were updated in place by accum_delta_kernel
+  int32_t* nt = ntot + ((size_t)bh * 4 + m) * g.Cmax + c;
+  double* st = stot + (((size_t)bh * 4 + m) * g.Cmax + c) * d;
   int n = 0;
-  const int32_t* pc = pcnt + ((size_t)bh * 4 + m) * parts * g.Cmax + c;
-  for (int q = 0; q < parts; ++q) n += pc[(size_t)q * g.Cmax];
+  if (delta) {
+    n = *nt;
+  } else {
+    const int32_t* pc = pcnt + ((size_t)bh * 4 + m) * parts * g.Cmax + c;
+    for (int q = 0; q < parts; ++q) n += pc[(size_t)q * g.Cmax];
+  }
   float* row = m == 0 ? qcent + ((size_t)bh * g.Cq + c) * d : kcent + ((size_t)bh * g.Cm + c) * d + g.off[m];
-  if (n > 0) {
-    for (int ch = lane; ch < dm; ch += 64) {
+  for (int ch = lane; ch < dm; ch += 64) {
+    double sum = 0.0;
+    if (delta) {
+      sum = st[ch];
+    } else {
       const int sl = ch / SW, j = ch % SW;
       const double* ps = psum + (((size_t)bh * 4 + m) * nslices + sl) * parts * (size_t)g.Cmax * SW + (size_t)c * SW + j;
-      double sum = 0.0;
       for (int q = 0; q < parts; ++q) sum += ps[(size_t)q * g.Cmax * SW];
-      row[ch] = (float)(sum / (double)n);
+      st[ch] = sum;
     }
+    if (n > 0) row[ch] = (float)(sum / (double)n);
   }
+  if (lane == 0 && !delta) *nt = n;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1532,8 +1643,15 @@ hipError_t launch_prep(const Geo& g, const Workspace& w, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Assignment i writes w.labels when iters - i is even, else w.labels_alt, so
+// the last one (i = iters) always lands in w.labels.
+static int32_t* labels_of(const Geo& g, const Workspace& w, int i) {
+  return ((g.iters - i) % 2 == 0) ? w.labels : w.labels_alt;
+}
+
 hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Workspace& w, int iter,
                          hipStream_t s) {
+  int32_t* out = labels_of(g, w, iter);
   if (g.bf16) {
     int lds = 0;
     for (int m = 0; m < 4; ++m) lds = max(lds, g.Cpad[m] * (g.dpad[m] + 8) * 2 + g.Cpad[m] * 4 + 4 * 128 * 8);
@@ -1546,37 +1664,50 @@ hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Wor
     for (int m = 0; m < 4; ++m) kbmax = max(kbmax, g.dpad[m] / 16);
     auto go = [&](auto kern) {
       if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      kern<<<grid, ASG_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, w.labels);
+      kern<<<grid, ASG_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, out);
     };
     if (kbmax <= 2) go(assign2_kernel<2>);
     else if (kbmax <= 4) go(assign2_kernel<4>);
     else go(assign2_kernel<8>);
   } else {
     dim3 grid((g.N + 255) / 256, 4, g.BH);
-    assign_exact_f32_kernel<<<grid, 256, 0, s>>>((const float*)qr, (const float*)kr, g, w.qcent, w.kcent, w.labels);
+    assign_exact_f32_kernel<<<grid, 256, 0, s>>>((const float*)qr, (const float*)kr, g, w.qcent, w.kcent, out);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Workspace& w, hipStream_t s) {
-  const int SW = acc_sw(g), ns = acc_slices(g), parts = acc_parts(g);
+hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Workspace& w, int it, hipStream_t s) {
+  const int SW = acc_sw(g), ns = acc_slices(g);
+  const int32_t* cur = labels_of(g, w, it - 1);
+  // bf16 data from the second update on: only the points whose label changed
+  // since the previous assignment move between the exact sums (fp32 data is
+  // summed afresh every time)
+  const bool delta = g.bf16 && it >= 2;
+  const int parts = acc_parts(g);
   int ypairs = 0;
   for (int m = 0; m < 4; ++m) ypairs += (g.dm[m] + SW - 1) / SW;
   const size_t lds = (size_t)g.Cmax * SW * 8 + (size_t)g.Cmax * 4;
   dim3 grid(parts, ypairs, g.BH);
   auto go = [&](auto kern, const auto* q, const auto* k) {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kern<<<grid, ACC_NT, lds, s>>>(q, k, g, w.labels, w.psum, w.pcnt, ns, parts);
+    kern<<<grid, ACC_NT, lds, s>>>(q, k, g, cur, w.psum, w.pcnt, ns, parts);
+  };
+  auto god = [&](auto kern) {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    kern<<<grid, ACC_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, cur, labels_of(g, w, it - 2), w.stot,
+                                  w.ntot, parts);
   };
   const uint16_t *qb = (const uint16_t*)qr, *kb = (const uint16_t*)kr;
   const float *qf = (const float*)qr, *kf = (const float*)kr;
-  if (g.bf16) {
+  if (delta) {
+    if (SW == 32) god(accum_delta_kernel<32>); else god(accum_delta_kernel<16>);
+  } else if (g.bf16) {
     if (SW == 32) go(accum_kernel<uint16_t, 32>, qb, kb); else go(accum_kernel<uint16_t, 16>, qb, kb);
   } else {
     if (SW == 32) go(accum_kernel<float, 32>, qf, kf); else go(accum_kernel<float, 16>, qf, kf);
   }
-  finalize_kernel<<<dim3((g.Cmax + 3) / 4, 4, g.BH), 256, 0, s>>>(g, w.psum, w.pcnt, SW, ns, parts, w.qcent, w.kcent,
-                                                                  w.cbf, w.cnorm);
+  finalize_kernel<<<dim3((g.Cmax + 3) / 4, 4, g.BH), 256, 0, s>>>(g, w.psum, w.pcnt, SW, ns, parts, delta ? 1 : 0,
+                                                                  w.stot, w.ntot, w.qcent, w.kcent, w.cbf, w.cnorm);
   return hipGetLastError();
 }
 

@@ -55,8 +55,11 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
   w.cbf = (uint16_t*)take(2 * BH * 4 * g.CmaxPad * g.DPmax);
   w.cnorm = (float*)take(4 * BH * 4 * g.CmaxPad);
   w.labels = (int32_t*)take(4 * BH * 4 * N);
+  w.labels_alt = (int32_t*)take(4 * BH * 4 * N);
   w.psum = (double*)take(8 * BH * 4 * (size_t)acc_slices(g) * acc_parts(g) * g.Cmax * acc_sw(g));
   w.pcnt = (int32_t*)take(4 * BH * 4 * (size_t)acc_parts(g) * g.Cmax);
+  w.stot = (double*)take(8 * BH * 4 * (size_t)g.Cmax * g.d);
+  w.ntot = (int32_t*)take(4 * BH * 4 * (size_t)g.Cmax);
   w.codes = (uint16_t*)take(8 * BH * N);
   w.qlab = (int32_t*)take(4 * BH * N);
   w.lut = (double*)take(8 * BH * g.Cq * 3 * g.Cm);
@@ -171,7 +174,7 @@ scope_status scope_plan(const scope_params* p, const void* q, const void* k, voi
   STEP(launch_prep(g, w, stream));
   STEP(launch_assign(g, q_rope, k_rope, w, 0, stream));
   for (int it = 1; it <= g.iters; ++it) {
-    STEP(launch_update(g, q_rope, k_rope, w, stream));
+    STEP(launch_update(g, q_rope, k_rope, w, it, stream));
     STEP(launch_assign(g, q_rope, k_rope, w, it, stream));
   }
   STEP(launch_pack(g, w, plan->q_labels, stream));

@@ -48,9 +48,12 @@ struct Workspace {
   float* kcent;                 // [BH][Cm][d]
   uint16_t* cbf;                // [BH][4][CmaxPad][DPmax] bf16 centroids, zero padded
   float* cnorm;                 // [BH][4][CmaxPad] ||bf16 centroid||^2 (FLT_MAX on padding)
-  int32_t* labels;              // [BH][4][N]
+  int32_t* labels;              // [BH][4][N] (labels of the last assignment)
+  int32_t* labels_alt;          // [BH][4][N] (assignments alternate between the two arrays)
   double* psum;                 // [BH][4][acc_slices][acc_parts][Cmax][acc_sw] partial centroid sums
   int32_t* pcnt;                // [BH][4][acc_parts][Cmax] partial cluster sizes
+  double* stot;                 // [BH][4][Cmax][d] exact per-cluster sums of the last update
+  int32_t* ntot;                // [BH][4][Cmax] cluster sizes of the last update
   uint16_t* codes;              // [BH][N][4]
   int32_t* qlab;                // [BH][N] (final query labels)
   double* lut;                  // [BH][Cq][3][Cm]
@@ -84,7 +87,8 @@ hipError_t launch_seed(const Geo& g, const void* qr, const void* kr, const Works
 hipError_t launch_prep(const Geo& g, const Workspace& w, hipStream_t s);
 hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Workspace& w, int iter,
                          hipStream_t s);
-hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Workspace& w, hipStream_t s);
+// Lloyd update `it` (1 .. iters) from the labels of assignment it - 1.
+hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Workspace& w, int it, hipStream_t s);
 hipError_t launch_pack(const Geo& g, const Workspace& w, int32_t* q_labels_out, hipStream_t s);
 hipError_t launch_perm(const Geo& g, const Workspace& w, int32_t* perm_q, int32_t* q_off, hipStream_t s);
 hipError_t launch_lut(const Geo& g, const Workspace& w, hipStream_t s);
