@@ -632,32 +632,67 @@ __global__ __launch_bounds__(NT) void final_select_kernel(SelArgs a, const doubl
     tau = b.tau;
     m = b.m;
   }
-  // ordered compaction: each thread owns 16 consecutive keys of a 4096-key chunk
-  constexpr int KPT = 16;
+  // ordered compaction over chunks of NT * 8 keys: wave w takes keys
+  // j0 + 512 w + 64 i + lane (i = 0..7), so the chunk's order is (wave, i,
+  // lane) = index order and every store instruction writes consecutive
+  // positions.  Per chunk: the ties (s == tau) before each wave, then the
+  // selected keys before each wave, from per-wave counts in LDS.
+  constexpr int KI = 8;
+  const int lane = tid & 63, wv = tid >> 6;
+  int32_t* wcnt = sm.misc;   // [NT / 64] per-wave counts (misc has room for 8)
+  static_assert(NT / 64 <= 8, "per-wave counts fit sm.misc");
   int64_t selBase = 0, tieBase = 0;
-  for (int j0 = 0; j0 < a.N; j0 += NT * KPT) {
-    uint32_t gt = 0, eq = 0;
-    for (int i = 0; i < KPT; ++i) {
-      const int j = j0 + tid * KPT + i;
+  __syncthreads();   // the boundary search's results in sm.misc are read by every thread
+  for (int j0 = 0; j0 < a.N; j0 += NT * KI) {
+    uint64_t gtm[KI], eqm[KI];
+    int wgt = 0, weq = 0;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int j = j0 + wv * 64 * KI + i * 64 + lane;
+      bool g = false, e = false;
       if (j < a.N) {
-        const double s = logit(S, S.codes[j]);
-        gt |= (uint32_t)(s > tau) << i;
-        eq |= (uint32_t)(s == tau) << i;
+        const double sj = logit(S, S.codes[j]);
+        g = sj > tau;
+        e = sj == tau;
       }
+      gtm[i] = __ballot(g);
+      eqm[i] = __ballot(e);
+      wgt += __popcll(gtm[i]);
+      weq += __popcll(eqm[i]);
     }
-    const int ngt = __popc(gt), neq = __popc(eq);
-    int64_t totTie;
-    const int64_t exTie = tieBase + block_incl_scan<int64_t, NT>(neq, sm.i64tmp, &totTie) - neq;
+    // ties before this wave
+    if (lane == 0) wcnt[wv] = weq;
+    __syncthreads();
+    int64_t exTie = tieBase, totTie = 0;
+    for (int w2 = 0; w2 < NT / 64; ++w2) {
+      const int v = wcnt[w2];
+      if (w2 < wv) exTie += v;
+      totTie += v;
+    }
+    __syncthreads();
     int64_t take = (int64_t)m - exTie;
-    take = take < 0 ? 0 : (take > neq ? neq : take);
-    const int64_t nsel = ngt + take;
-    int64_t totSel;
-    int64_t pos = selBase + block_incl_scan<int64_t, NT>(nsel, sm.i64tmp, &totSel) - nsel;
+    take = take < 0 ? 0 : (take > weq ? weq : take);
+    // selected keys before this wave
+    if (lane == 0) wcnt[wv] = wgt + (int)take;
+    __syncthreads();
+    int64_t pos = selBase, totSel = 0;
+    for (int w2 = 0; w2 < NT / 64; ++w2) {
+      const int v = wcnt[w2];
+      if (w2 < wv) pos += v;
+      totSel += v;
+    }
+    __syncthreads();
     int64_t tr = exTie;
-    for (int i = 0; i < KPT; ++i) {
-      const int j = j0 + tid * KPT + i;
-      const bool take1 = ((gt >> i) & 1u) || (((eq >> i) & 1u) && tr++ < m);
-      if (take1) { if (pos < r) out[pos] = j; ++pos; }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const uint64_t below = (1ull << lane) - 1ull;
+      const bool e = (eqm[i] >> lane) & 1ull;
+      const bool take1 = ((gtm[i] >> lane) & 1ull) || (e && tr + __popcll(eqm[i] & below) < m);
+      const uint64_t sm1 = __ballot(take1);
+      const int64_t p = pos + __popcll(sm1 & below);
+      if (take1 && p < r) out[p] = j0 + wv * 64 * KI + i * 64 + lane;
+      pos += __popcll(sm1);
+      tr += __popcll(eqm[i]);
     }
     selBase += totSel;
     tieBase += totTie;
