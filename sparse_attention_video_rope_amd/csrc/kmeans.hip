@@ -1516,13 +1516,22 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
 
 // KBMAX: the largest dpad / 16 of the launch; the kernel's register budget is
 // that of its widest instantiated tile loop, so narrow heads get a narrow kernel.
+// Workgroups of one head: split.start[m] .. split.start[m + 1] - 1 serve
+// clustering m (counts proportional to its estimated work).
+struct AsgSplit {
+  int start[5];
+};
 template <int KBMAX>
 __global__ __launch_bounds__(ASG_NT) void assign2_kernel(const uint16_t* __restrict__ qr,
                                                          const uint16_t* __restrict__ kr, Geo g,
                                                          const uint16_t* __restrict__ cbf,
                                                          const float* __restrict__ cnorm,
-                                                         int32_t* __restrict__ labels) {
-  const int m = blockIdx.y, bh = blockIdx.z;
+                                                         int32_t* __restrict__ labels, AsgSplit split) {
+  const int bx = blockIdx.x, bh = blockIdx.z;
+  const int m = bx < split.start[1] ? 0 : (bx < split.start[2] ? 1 : (bx < split.start[3] ? 2 : 3));
+  const int part = bx - (m == 0 ? 0 : (m == 1 ? split.start[1] : (m == 2 ? split.start[2] : split.start[3])));
+  const int nparts = (m == 0 ? split.start[1] : (m == 1 ? split.start[2] : (m == 2 ? split.start[3] : split.start[4]))) -
+                     (m == 0 ? 0 : (m == 1 ? split.start[1] : (m == 2 ? split.start[2] : split.start[3])));
   const int N = g.N, d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m], Cpad = g.Cpad[m], dpad = g.dpad[m];
   const int ldc = dpad + 8;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -1551,7 +1560,7 @@ __global__ __launch_bounds__(ASG_NT) void assign2_kernel(const uint16_t* __restr
   const uint16_t* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + off;
   const bool vec16 = ((off * 2) % 16 == 0) && ((d * 2) % 16 == 0);
   int32_t* lab = labels + ((size_t)bh * 4 + m) * N;
-  const int gw = blockIdx.x * (ASG_NT / 64) + wv, gstride = gridDim.x * (ASG_NT / 64);
+  const int gw = part * (ASG_NT / 64) + wv, gstride = nparts * (ASG_NT / 64);
   double* xs = xsh + wv * 128;
   const int kbn = dpad / 16;
   auto run = [&](auto kb) {
@@ -1655,16 +1664,28 @@ hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Wor
   if (g.bf16) {
     int lds = 0;
     for (int m = 0; m < 4; ++m) lds = max(lds, g.Cpad[m] * (g.dpad[m] + 8) * 2 + g.Cpad[m] * 4 + 4 * 128 * 8);
-    // about 2048 workgroups in all, at most one wave per 64-point tile
+    // about 3072 workgroups in all, shared among the four clusterings of a
+    // head in proportion to Cpad (dpad / 16 + 1) (MFMA blocks plus the
+    // per-candidate selection work; equal shares left the query clustering,
+    // with the widest rows, as the last to finish), at most one wave per
+    // 64-point tile
     const int ntiles = (g.N + 63) / 64;
-    int parts = (2048 + 4 * g.BH - 1) / (4 * g.BH);
-    parts = max(1, min(parts, (ntiles + 3) / 4));
-    dim3 grid(parts, 4, g.BH);
+    double wsum = 0.0, wm[4];
+    for (int m = 0; m < 4; ++m) { wm[m] = (double)g.Cpad[m] * (g.dpad[m] / 16 + 1); wsum += wm[m]; }
+    const double per_head = (double)(3072 + g.BH - 1) / g.BH;
+    AsgSplit split;
+    split.start[0] = 0;
+    for (int m = 0; m < 4; ++m) {
+      int pm = (int)(per_head * wm[m] / wsum + 0.5);
+      pm = max(1, min(pm, (ntiles + 3) / 4));
+      split.start[m + 1] = split.start[m] + pm;
+    }
+    dim3 grid(split.start[4], 1, g.BH);
     int kbmax = 1;
     for (int m = 0; m < 4; ++m) kbmax = max(kbmax, g.dpad[m] / 16);
     auto go = [&](auto kern) {
       if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      kern<<<grid, ASG_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, out);
+      kern<<<grid, ASG_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, out, split);
     };
     if (kbmax <= 2) go(assign2_kernel<2>);
     else if (kbmax <= 4) go(assign2_kernel<4>);
