@@ -69,7 +69,7 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const lds_u16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 
-template <int D, int WPE>
+template <int D, int WPE, int BN = 64>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void attend_bf16_lds_kernel(
     AttArgs a, const int32_t* __restrict__ work, const int32_t* __restrict__ status,
     const int32_t* __restrict__ perm_q, const int32_t* __restrict__ q_off, const int32_t* __restrict__ cr,
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   constexpr int NW = 4;
   constexpr int BM = 32 * NW;
   static_assert(BM == ATT_BM, "queries per workgroup must equal the work-list chunk");
-  constexpr int BN = 64;
+  constexpr int NST = BN / 32;               // 32-key MFMA row blocks per chunk
   constexpr int PR = D / 8;                  // 16-byte pieces per row
   constexpr int TILE = BN * D;               // elements per tile
   constexpr int BLK = TILE / 512;            // 1 KB blocks per tile
@@ -220,9 +220,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       load_idx(min(kc + 2, nchunks - 1));          // indices of chunk kc+2
     }
     if (active) {
-      f32x16_t s[2];
+      f32x16_t s[NST];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < NST; ++st) {
         bf16x8_t ak[D / 16];
 #pragma unroll
         for (int kb = 0; kb < D / 16; ++kb) ak[kb] = *(const lds_bf16x8*)(Kc + kro[kb] + st * 32 * D);
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         int k4 = 4 * hi;
         asm volatile("" : "+v"(k4));
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < NST; ++st)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             if (st * 32 + 8 * (v >> 2) + (v & 3) + k4 >= kleft) s[st][v] = -__builtin_inff();
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         // maximum exceeds it by more than RESCALE_LOG2
         float mloc = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-        for (int e = 2; e < 32; e += 2) mloc = fmaxf(fmaxf(mloc, s[e >> 4][e & 15]), s[e >> 4][(e + 1) & 15]);
+        for (int e = 2; e < NST * 16; e += 2) mloc = fmaxf(fmaxf(mloc, s[e >> 4][e & 15]), s[e >> 4][(e + 1) & 15]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
         const bool first = kc == 0;
         const bool grow_m = first || mloc > RESCALE_LOG2;
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
             for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
 #pragma unroll
-          for (int st = 0; st < 2; ++st)
+          for (int st = 0; st < NST; ++st)
 #pragma unroll
             for (int v = 0; v < 16; ++v) s[st][v] -= dm;
           mref += dm;
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         }
       }
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < NST; ++st) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           bf16x2_t pk[4];
