@@ -73,13 +73,16 @@ __device__ __forceinline__ void store_rounded(Vec8<uint16_t>& x, const double (&
   }
 }
 
-// One thread rotates 8 consecutive channels (4 pairs) of one token of Q or K.
+// One thread rotates 8 consecutive channels (4 pairs) of one token of Q or K,
+// for ROPE_R chunks: sub-block k of the workgroup's ROPE_R * 256 chunks; the
+// loads of all ROPE_R chunks are issued before any is processed.
 // Grid: x over the tokens x (d/8) chunks of one head, y over heads, z over Q / K, so
 // all index arithmetic is 32-bit (d/8 is 8 or 16: a shift).  For K, knm (if set)
 // receives an upper bound of the head's largest ||k'|| over the stored
 // (rounded) rows: the fp32 norm times 1 + 2^-12 (which covers the rounding of
 // the fp32 sum and the square root), as float bits via atomicMax (zeroed
 // beforehand; non-negative floats order like their bits).
+constexpr int ROPE_R = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    T* __restrict__ qo, T* __restrict__ ko,
@@ -87,53 +90,68 @@ __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, cons
                                                    uint32_t* __restrict__ knm) {
   __shared__ float red[256 / 64];
   const int cshift = a.d == 128 ? 4 : 3;
-  const int r0 = blockIdx.x * blockDim.x + threadIdx.x;   // token * (d/8) + chunk
-  const bool valid = r0 < (a.N << cshift);
-  const int r = valid ? r0 : 0;
   const int sel = blockIdx.z, bh = blockIdx.y;
-  const int chunk = r & ((1 << cshift) - 1);
-  const int n = r >> cshift;
   const int hw = a.Hg * a.Wg;
-  int t, hh;
-  if (a.magic) {
-    t = (int)(((uint64_t)(uint32_t)n * a.mhw) >> 32);
-    hh = (int)(((uint64_t)(uint32_t)(n - t * hw) * a.mw) >> 32);
-  } else {
-    t = n / hw;
-    hh = (n - t * hw) / a.Wg;
-  }
-  const int rem = n - t * hw, ww = rem - hh * a.Wg;
-  const size_t base = ((size_t)bh * a.N + n) * a.d + chunk * 8;
-  Vec8<T> x;
-  x.load((sel ? k : q) + base);
-  double y[8];
+  const int nchunk = a.N << cshift;
+  Vec8<T> x[ROPE_R];
+  size_t base[ROPE_R];
+  int rr[ROPE_R];
 #pragma unroll
-  for (int pi = 0; pi < 4; ++pi) {
-    const int ch = chunk * 8 + 2 * pi;
-    // range of the pair, by selects (a runtime index into the argument struct
-    // would load it from memory)
-    const bool r0 = ch < a.off1, r1 = ch < a.off2;
-    const int o = r0 ? 0 : (r1 ? a.off1 : a.off2);
-    const int tof = r0 ? a.toff[0] : (r1 ? a.toff[1] : a.toff[2]);
-    const int hd = r0 ? a.dm[0] / 2 : (r1 ? a.dm[1] / 2 : a.dm[2] / 2);
-    const int ps = r0 ? t : (r1 ? hh : ww);
-    const double2 cs = tab[tof + ps * hd + (ch - o) / 2];
-    const double x0 = Elem<T>::ld(&x.v[2 * pi]), x1 = Elem<T>::ld(&x.v[2 * pi + 1]);
-    {
+  for (int kk = 0; kk < ROPE_R; ++kk) {
+    const int r0 = (blockIdx.x * ROPE_R + kk) * 256 + threadIdx.x;   // token * (d/8) + chunk
+    rr[kk] = r0 < nchunk ? r0 : -1;
+    const int r = r0 < nchunk ? r0 : 0;
+    base[kk] = ((size_t)bh * a.N + (r >> cshift)) * a.d + (r & ((1 << cshift) - 1)) * 8;
+    x[kk].load((sel ? k : q) + base[kk]);
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < ROPE_R; ++kk) {
+    const bool valid = rr[kk] >= 0;
+    const int r = valid ? rr[kk] : 0;
+    const int chunk = r & ((1 << cshift) - 1);
+    const int n = r >> cshift;
+    int t, hh;
+    if (a.magic) {
+      t = (int)(((uint64_t)(uint32_t)n * a.mhw) >> 32);
+      hh = (int)(((uint64_t)(uint32_t)(n - t * hw) * a.mw) >> 32);
+    } else {
+      t = n / hw;
+      hh = (n - t * hw) / a.Wg;
+    }
+    const int rem = n - t * hw, ww = rem - hh * a.Wg;
+    double y[8];
+#pragma unroll
+    for (int pi = 0; pi < 4; ++pi) {
+      const int ch = chunk * 8 + 2 * pi;
+      // range of the pair, by selects (a runtime index into the argument
+      // struct would load it from memory)
+      const bool in0 = ch < a.off1, in1 = ch < a.off2;
+      const int o = in0 ? 0 : (in1 ? a.off1 : a.off2);
+      const int tof = in0 ? a.toff[0] : (in1 ? a.toff[1] : a.toff[2]);
+      const int hd = in0 ? a.dm[0] / 2 : (in1 ? a.dm[1] / 2 : a.dm[2] / 2);
+      const int ps = in0 ? t : (in1 ? hh : ww);
+      const double2 cs = tab[tof + ps * hd + (ch - o) / 2];
+      const double x0 = Elem<T>::ld(&x[kk].v[2 * pi]), x1 = Elem<T>::ld(&x[kk].v[2 * pi + 1]);
+      {
 #pragma clang fp contract(off)
-      y[2 * pi] = x0 * cs.x - x1 * cs.y;
-      y[2 * pi + 1] = x0 * cs.y + x1 * cs.x;
+        y[2 * pi] = x0 * cs.x - x1 * cs.y;
+        y[2 * pi + 1] = x0 * cs.y + x1 * cs.x;
+      }
+    }
+    store_rounded(x[kk], y);
+    if (valid) x[kk].store((sel ? ko : qo) + base[kk]);
+    if (sel && knm) {
+      // squared norm of the token: its d/8 threads are consecutive lanes
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { const float e = (float)Elem<T>::ld(&x[kk].v[i]); ss = fmaf(e, e, ss); }
+      ss = (float)group_sum_dpp(valid ? (double)ss : 0.0, 1 << cshift);
+      mx = fmaxf(mx, ss);
     }
   }
-  store_rounded(x, y);
-  if (valid) x.store((sel ? ko : qo) + base);
   if (sel && knm) {
-    // squared norm of the token: its d/8 threads are consecutive lanes
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { const float e = (float)Elem<T>::ld(&x.v[i]); ss = fmaf(e, e, ss); }
-    ss = (float)group_sum_dpp(valid ? (double)ss : 0.0, 1 << cshift);
-    const float mx = block_max<float, 256>(ss, red);
+    mx = block_max<float, 256>(mx, red);
     if (threadIdx.x == 0) atomicMax(&knm[bh], __float_as_uint(sqrtf(mx) * (1.0f + 0x1p-12f)));
   }
 }
@@ -152,7 +170,7 @@ hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const
   a.mhw = ((1ull << 32) + hw - 1) / hw;
   a.mw = ((1ull << 32) + g.Wg - 1) / (uint64_t)g.Wg;
   a.magic = (uint64_t)g.N * hw < (1ull << 32) ? 1 : 0;
-  const dim3 blocks((unsigned)((g.N * (g.d / 8) + 255) / 256), (unsigned)g.BH, 2);
+  const dim3 blocks((unsigned)((g.N * (g.d / 8) + 256 * ROPE_R - 1) / (256 * ROPE_R)), (unsigned)g.BH, 2);
   uint32_t* knm = reinterpret_cast<uint32_t*>(k_norm_max);
   if (knm) {
     const hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(knm), 0, (size_t)g.BH, s);
