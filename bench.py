@@ -12,6 +12,10 @@ synthetic inputs resident in HBM.  Prints one JSON line.
   roofline   the attention kernel (bf16 MFMA): its algorithmic flops per
              launch / its average launch time, HIP events on its stream
   cpu_baseline  the CPU oracle on one head of the same workload
+  warm_start the same step on a later denoising step's inputs (the workload's
+             step-1 stand-in), with Lloyd started from the step-0 plan's
+             centroids (SCOPE_USE_INIT_CENTROIDS, no k-means++) and fewer
+             iterations; timed and compared with a full plan of those inputs
 """
 from __future__ import annotations
 
@@ -38,6 +42,8 @@ def parse():
     ap.add_argument("--config", default="cogvideox")
     ap.add_argument("--rho", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-iters", type=int, default=2,
+                    help="Lloyd iterations of the warm-started plan (negative: skip the warm-start measurement)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attend_traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (used if present and current)")
     ap.add_argument("--profile-pass", action="store_true",
@@ -136,6 +142,96 @@ def cpu_baseline(w, rho):
             "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
+def _min_dist_sum(x, c):
+    """sum over rows of x of the squared distance to the nearest row of c (per head, fp32)."""
+    import torch
+    tot = 0.0
+    for h in range(x.shape[0]):
+        tot += float(torch.cdist(x[h], c[h]).pow(2).min(dim=1).values.double().sum())
+    return tot
+
+
+def _inertia(w, qr, kr, pl):
+    """k-means objective of the plan's query centroids and of its three key subspace codebooks."""
+    import torch
+    BH, N, d = w.BH, w.N, w.d
+    q = qr.view(BH, N, d).float()
+    k = kr.view(BH, N, d).float()
+    cq = pl.q_centroids.view(BH, w.Cq, d)
+    ck = pl.k_centroids.view(BH, w.Cm, d)
+    kin, o = 0.0, 0
+    for dm in w.split:
+        kin += _min_dist_sum(k[:, :, o:o + dm].contiguous(), ck[:, :, o:o + dm].contiguous())
+        o += dm
+    return _min_dist_sum(q, cq), kin
+
+
+def _dense_rel_l2(w, qr, kr, vd, outs, torch):
+    """||out - dense attention|| / ||dense attention|| for each of outs (fp32, head by head)."""
+    BH, N, d = w.BH, w.N, w.d
+    q, k, v = (t.view(BH, N, d) for t in (qr, kr, vd))
+    num = [0.0] * len(outs)
+    den = 0.0
+    for h in range(BH):
+        qh, kh, vh = q[h].float(), k[h].float(), v[h].float()
+        ref = torch.softmax((qh @ kh.t().contiguous()) / float(np.sqrt(d)), dim=1) @ vh
+        den += float(ref.double().pow(2).sum())
+        for i, o in enumerate(outs):
+            num[i] += float((o.view(BH, N, d)[h].float() - ref).double().pow(2).sum())
+    return [float(np.sqrt(x / den)) for x in num]
+
+
+def warm_start(a, w, rho, qd, kd, vd, sav, torch):
+    """Codebook reuse across denoising steps on the workload's step-1 stand-in inputs."""
+    import workloads
+    dev = qd.device
+    p_cold = sav.params_for(w, rho=rho)
+    p_warm = sav.params_for(w, rho=rho, iters=a.warm_iters, init_centroids=True)
+    to = lambda x: torch.from_numpy(x.reshape(-1)).to(qd.dtype).to(dev)
+    q1, k1, _ = workloads.generate(w, step=1)
+    q1d, k1d = to(q1), to(k1)
+    del q1, k1
+    qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+    pl0 = sav.Plan(p_cold, device=dev, debug=False, centroids=True)
+    sav.plan(p_cold, qd, kd, pl0, qr, kr)                      # step 0: full plan
+    # step 1, full plan: the reference the warm start is compared with
+    plc = sav.Plan(p_cold, device=dev, debug=False, centroids=True)
+    sav.plan(p_cold, q1d, k1d, plc, qr, kr)
+    out_c = sav.attend(p_cold, plc, qr, kr, vd)
+    inert_c = _inertia(w, qr, kr, plc)
+    plw = sav.Plan(p_warm, device=dev, debug=False, centroids=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.warmup + a.steps)]
+    out_w = torch.empty_like(vd)
+    for e0, e1, e2 in ev:
+        plw.q_centroids.copy_(pl0.q_centroids)
+        plw.k_centroids.copy_(pl0.k_centroids)
+        e0.record()
+        sav.plan(p_warm, q1d, k1d, plw, qr, kr)
+        e1.record()
+        sav.attend(p_warm, plw, qr, kr, vd, out_w)
+        e2.record()
+    torch.cuda.synchronize()
+    ev = ev[a.warmup:]
+    plan_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    step_ms = float(np.mean([e0.elapsed_time(e2) for e0, _, e2 in ev]))
+    inert_w = _inertia(w, qr, kr, plw)
+
+    def density(pl):
+        n = (pl.q_off.view(w.BH, w.Cq + 1)[:, 1:] - pl.q_off.view(w.BH, w.Cq + 1)[:, :-1]).double()
+        return float((n * pl.counts_r.view(w.BH, w.Cq).double()).sum()) / (w.BH * float(w.N) ** 2)
+
+    dc, dw = out_c.float(), out_w.float()
+    err_w, err_c = _dense_rel_l2(w, qr, kr, vd, [out_w, out_c], torch)
+    return {"inputs": "step-1 stand-in (every Gaussian draw of Q and K rotated 0.05 rad towards a fresh one)",
+            "init": "centroids of the full plan of the step-0 inputs", "lloyd_iters": a.warm_iters,
+            "plan_ms": round(plan_ms, 4), "step_ms": round(step_ms, 4),
+            "q_inertia_vs_full": round(inert_w[0] / inert_c[0], 5),
+            "k_inertia_vs_full": round(inert_w[1] / inert_c[1], 5),
+            "density": round(density(plw), 4), "density_full": round(density(plc), 4),
+            "out_rel_l2_vs_full": float(torch.linalg.vector_norm(dw - dc) / torch.linalg.vector_norm(dc)),
+            "out_rel_l2_vs_dense": err_w, "out_rel_l2_vs_dense_full": err_c}
+
+
 def main():
     a = parse()
     if a.traffic_from:
@@ -228,6 +324,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "wall_s": round(wall, 3),
     }
+    if a.warm_iters >= 0:
+        line["warm_start"] = warm_start(a, w, rho, qd, kd, vd, sav, torch)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, rho)
     print(json.dumps(line), flush=True)

@@ -115,7 +115,10 @@ class Plan:
     """Caller-owned device buffers of one plan (torch tensors) plus the C struct."""
 
     def __init__(self, p: Params, device="cuda", debug: bool = True, sel_capacity: Optional[int] = None,
-                 norm_bound: bool = True):
+                 norm_bound: bool = True, centroids: Optional[bool] = None):
+        """debug: also keep labels, codes, seeds and LUT; centroids (default:
+        debug): keep the final centroids, which a later plan can start from
+        with SCOPE_USE_INIT_CENTROIDS."""
         import torch
         ws, sel_worst, work_cap = sizes(p)
         BH, N, Cq, Cm, d = p.BH, p.N, p.Cq, p.Cm, p.d
@@ -136,15 +139,17 @@ class Plan:
         self.k_norm_max = torch.zeros(BH, dtype=torch.float32, device=device) if norm_bound else None
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
         self.debug = debug
-        if debug:
+        self.q_centroids = self.k_centroids = None
+        if debug if centroids is None else centroids:
             self.q_centroids = torch.zeros(BH * Cq * d, dtype=torch.float32, device=device)
             self.k_centroids = torch.zeros(BH * Cm * d, dtype=torch.float32, device=device)
+        if debug:
             self.q_labels = torch.empty(BH * N, **i32)
             self.k_codes = torch.empty(BH * N * 4, dtype=torch.int16, device=device)
             self.seeds = torch.empty(BH * 4 * max(Cq, Cm), **i32)
             self.lut = torch.empty(BH * Cq * 3 * Cm, dtype=torch.float64, device=device)
         else:
-            self.q_centroids = self.k_centroids = self.q_labels = self.k_codes = self.seeds = self.lut = None
+            self.q_labels = self.k_codes = self.seeds = self.lut = None
         s = PlanStruct()
         for name in ("perm_q", "q_off", "counts_t", "counts_b", "counts_r", "k_head", "sel_off", "sel_idx", "work",
                      "status", "q_centroids", "k_centroids", "q_labels", "k_codes", "seeds", "lut", "k_norm_max"):

@@ -287,3 +287,26 @@ def test_wan14b_rho_sweep_nested():
             a, b, cc = (set(h["sel"][c].tolist()) for h in hs)
             assert a <= b <= cc
         assert np.all(runs[0].t[bh] <= runs[1].t[bh]) and np.all(runs[1].t[bh] <= runs[2].t[bh])
+
+
+@pytest.mark.parametrize("name", ["cogvideox", "wan13b_480p"])
+def test_warm_start_from_own_centroids_is_a_fixed_point(name):
+    """A plan started from a finished plan's final centroids with no Lloyd
+    iteration (codebook reuse on unchanged inputs) reproduces that plan: the
+    final assignment of a plan is the one to its final centroids."""
+    run = full_run(name)
+    w = run.w
+    qd, kd, _ = run.inputs
+    p = sav.params_for(w, rho=run.rho, iters=0, init_centroids=True)
+    pl = sav.Plan(p, debug=True)
+    pl.q_centroids.copy_(run.pl.q_centroids)
+    pl.k_centroids.copy_(run.pl.k_centroids)
+    sav.plan(p, qd, kd, pl)
+    torch.cuda.synchronize()
+    assert int(pl.status[1]) == 0
+    for f in ("q_centroids", "k_centroids", "q_labels", "lut", "perm_q", "q_off", "counts_t", "counts_b",
+              "counts_r", "k_head", "sel_off"):
+        assert torch.equal(getattr(pl, f), getattr(run.pl, f)), f
+    assert torch.equal(pl.k_codes.view(-1, 4)[:, :3], run.pl.k_codes.view(-1, 4)[:, :3])
+    n = int(run.sel_off[-1])
+    assert torch.equal(pl.sel_idx[:n], run.pl.sel_idx[:n])

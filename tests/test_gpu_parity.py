@@ -186,6 +186,28 @@ def test_end_to_end_matches_oracle(w, rho):
         say(f"  head {bh}: max {mx:.2e} mean {mn:.2e} density {np.sum(o['n'] * o['r']) / w.N**2:.3f}")
 
 
+@pytest.mark.parametrize("iters", [0, 2])
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_warm_start_end_to_end(w, iters):
+    """Codebook reuse across denoising steps: the plan of the step-1 stand-in
+    inputs with Lloyd started from the oracle's final step-0 centroids (in the
+    plan's fp32 centroid format) instead of k-means++."""
+    say("warm start", w.name, iters)
+    heads0 = oracle_heads(w)
+    init_q = np.stack([h["q_centroids"] for h in heads0]).astype(np.float32).astype(np.float64)
+    init_k = np.stack([h["k_centroids"] for h in heads0]).astype(np.float32).astype(np.float64)
+    q, k, v = workloads.generate(w, step=1)
+    wi = w.with_(iters=iters)
+    heads = [O.workload_head(wi, bh, q[bh], k[bh], v[bh], init_q=init_q[bh], init_k=init_k[bh])
+             for bh in range(w.BH)]
+    g = run_gpu(wi, init_q=init_q, init_k=init_k, inputs=(q, k, v))
+    assert g["status"][1] == 0
+    assert_plan_equal(w, g, heads)
+    for bh, o in enumerate(heads):
+        mx, mn = assert_attention(g["out"][bh], o["out"], w.dtype, f"{w.name} head {bh}")
+        say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
+
+
 def test_tiny_config_end_to_end():
     w = workloads.CONFIGS["tiny"]
     say("tiny")

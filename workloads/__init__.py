@@ -16,6 +16,12 @@ available; these fields stand in for them with the same shapes):
   coefficient vector per tensor, scaled to unit RMS, plus i.i.d.
   N(0, 0.1^2) noise;
 * V ~ N(0, 1);
+* step s > 0 stands in for a later denoising step of the same head (for
+  codebook reuse across steps): the same bumps, and every Gaussian draw of
+  Q and K (coefficients and noise) replaced by cos(a) x + sin(a) z, with x
+  step 0's draw, z a fresh one of step s and a = drift * s radians
+  (drift = 0.05 by default), so the draws stay N(0, 1) and move by about
+  5% per step; V is unchanged;
 * bf16 configurations round every input element to bf16 (through fp32,
   round-to-nearest-even at each step); the values handed out are exactly
   representable in the configuration's dtype.
@@ -113,8 +119,12 @@ def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def generate_head(w: Workload, b: int, h: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Pre-RoPE q, k and v of head (b, h) as fp64 arrays [N, d] holding dtype values."""
+def generate_head(w: Workload, b: int, h: int, step: int = 0,
+                  drift: float = 0.05) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Pre-RoPE q, k and v of head (b, h) as fp64 arrays [N, d] holding dtype values.
+
+    step > 0: the later-step stand-in (same bumps, every Gaussian draw of Q
+    and K rotated towards a fresh one by drift * step radians)."""
     seed = BASE_SEED + w.index
     N, d = w.N, w.d
     pos = grid_positions(w.T, w.Hg, w.Wg).astype(np.float64)
@@ -130,22 +140,28 @@ def generate_head(w: Workload, b: int, h: int) -> Tuple[np.ndarray, np.ndarray, 
     for tensor_id in (0, 1):
         rng = np.random.default_rng([seed, b, h, tensor_id])
         coef = rng.standard_normal((w.R, d))
+        noise = rng.standard_normal((N, d))
+        if step:
+            a = drift * step
+            fresh = np.random.default_rng([seed, b, h, tensor_id, 5, step])
+            coef = np.cos(a) * coef + np.sin(a) * fresh.standard_normal((w.R, d))
+            noise = np.cos(a) * noise + np.sin(a) * fresh.standard_normal((N, d))
         field = phi.T @ coef                              # [N, d], rank R over (t, h, w)
         field /= np.sqrt(np.mean(field * field))
-        field += 0.1 * rng.standard_normal((N, d))
+        field += 0.1 * noise
         out.append(_cast(field, w.dtype))
     v = np.random.default_rng([seed, b, h, 2]).standard_normal((N, d))
     out.append(_cast(v, w.dtype))
     return out[0], out[1], out[2]
 
 
-def generate(w: Workload, heads: Optional[list] = None):
+def generate(w: Workload, heads: Optional[list] = None, step: int = 0):
     """Stacked inputs [len(heads), N, d] for the given flat head indices bh = b*H + h."""
     if heads is None:
         heads = list(range(w.BH))
     qs, ks, vs = [], [], []
     for bh in heads:
-        q, k, v = generate_head(w, bh // w.H, bh % w.H)
+        q, k, v = generate_head(w, bh // w.H, bh % w.H, step)
         qs.append(q)
         ks.append(k)
         vs.append(v)
