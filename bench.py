@@ -12,6 +12,11 @@ synthetic inputs resident in HBM.  Prints one JSON line.
   roofline   the attention kernel (bf16 MFMA): its algorithmic flops per
              launch / its average launch time, HIP events on its stream
   cpu_baseline  the CPU oracle on one head of the same workload
+  --fidelity instead: the proxy-fidelity sweep (recall of each sampled query's
+             true top-10% keys by its cluster's key set, softmax mass on that
+             set, rank correlation of the Eq. (6) proxy with the exact logits,
+             error against dense attention) over rho in {0.5 .. 0.99} at
+             alpha = 0.1, three input seeds; one JSON line
   warm_start the same step on a later denoising step's inputs (the workload's
              step-1 stand-in), with Lloyd started from the step-0 plan's
              centroids (SCOPE_USE_INIT_CENTROIDS, no k-means++) and fewer
@@ -42,6 +47,8 @@ def parse():
     ap.add_argument("--config", default="cogvideox")
     ap.add_argument("--rho", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fidelity", action="store_true", help="run the proxy-fidelity sweep instead of the bench")
+    ap.add_argument("--fidelity-rows", type=int, default=32, help="sampled query rows per head for --fidelity")
     ap.add_argument("--warm-iters", type=int, default=2,
                     help="Lloyd iterations of the warm-started plan (negative: skip the warm-start measurement)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attend_traffic.json"),
@@ -232,6 +239,116 @@ def warm_start(a, w, rho, qd, kd, vd, sav, torch):
             "out_rel_l2_vs_dense": err_w, "out_rel_l2_vs_dense_full": err_c}
 
 
+def _avg_ranks(x):
+    """Ranks 0..n-1 of a 1-D tensor, equal values sharing the mean of their ranks (fp64)."""
+    import torch
+    srt, order = torch.sort(x)
+    _, inv, cnt = torch.unique_consecutive(srt, return_inverse=True, return_counts=True)
+    start = torch.cumsum(cnt, 0) - cnt
+    r = torch.empty_like(x, dtype=torch.float64)
+    r[order] = (start.double() + (cnt.double() - 1.0) / 2.0)[inv]
+    return r
+
+
+def proxy_fidelity_rows(qr, kr, v, labels, lut, codes, sets, out, rows, top_frac=0.1):
+    """Proxy fidelity at sampled query rows of one head (fp64 throughout).
+
+    qr, kr, v, out [N, d]; labels [N] query clusters; lut [Cq, 3, Cm] = P^m[c][z]
+    (no 1/sqrt(d)); codes [N, 3] key codes; sets(c) -> key indices of S_c;
+    rows: the query rows.  Per row i with cluster c: recall of the true top
+    ceil(top_frac N) keys by exact logit within S_c, softmax mass on S_c,
+    Spearman correlation (mean ranks for ties) of the Eq. (6) proxy s[c, :]
+    with the exact logits q_i . k_j / sqrt(d).  Also the squared error of the
+    output rows against dense attention and the squared norm of the latter."""
+    import math
+    import torch
+    N, d = kr.shape
+    lg = (qr[rows].double() @ kr.double().t()) / math.sqrt(d)
+    cs = labels[rows].long()
+    cd = codes.long()
+    lt = lut.double()
+    prox = (lt[cs, 0][:, cd[:, 0]] + lt[cs, 1][:, cd[:, 1]] + lt[cs, 2][:, cd[:, 2]]) / math.sqrt(d)
+    member = torch.zeros(len(rows), N, dtype=torch.bool, device=kr.device)
+    for i, c in enumerate(cs.tolist()):
+        member[i, sets(c).long()] = True
+    kt = math.ceil(top_frac * N)
+    top = lg.topk(kt, dim=1).indices
+    recall = member.gather(1, top).double().mean(1)
+    p = torch.softmax(lg, dim=1)
+    mass = (p * member.double()).sum(1)
+    rho_s = []
+    for i in range(len(rows)):
+        a, b = _avg_ranks(prox[i]), _avg_ranks(lg[i])
+        a, b = a - a.mean(), b - b.mean()
+        rho_s.append(float((a * b).sum() / torch.sqrt((a * a).sum() * (b * b).sum())))
+    dense = p @ v.double()
+    err2 = float((out[rows].double() - dense).pow(2).sum())
+    return {"recall": recall.cpu().numpy(), "mass": mass.cpu().numpy(), "spearman": np.array(rho_s),
+            "err2": err2, "ref2": float(dense.pow(2).sum())}
+
+
+FID_RHOS = (0.5, 0.7, 0.9, 0.95, 0.99)
+FID_ALPHA = 0.1
+FID_REPS = 3
+
+
+def fidelity(a):
+    """Proxy-fidelity sweep on the GPU plans of the workload (three input seeds)."""
+    import torch
+    import sparse_attention_video_rope_amd as sav
+    import workloads
+    w0 = workloads.CONFIGS[a.config]
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w0.dtype == "bf16" else torch.float32
+    res = {rho: {"recall": [], "mass": [], "spearman": [], "density": [], "err": []} for rho in FID_RHOS}
+    for rep in range(FID_REPS):
+        w = w0.with_(index=w0.index + 1000 * rep, alpha=FID_ALPHA)
+        q, k, v = workloads.generate(w)
+        qd, kd, vd = (torch.from_numpy(x.reshape(-1)).to(dt).to(dev) for x in (q, k, v))
+        del q, k, v
+        for rho in FID_RHOS:
+            rng = np.random.default_rng([w.index, 77])     # the same sampled rows at every rho
+            p = sav.params_for(w, rho=rho)
+            pl = sav.Plan(p, device=dev, debug=True)
+            qr, kr, _ = sav.plan(p, qd, kd, pl)
+            out = sav.attend(p, pl, qr, kr, vd)
+            torch.cuda.synchronize()
+            assert int(pl.status[1]) == 0, "selected-key capacity overflow"
+            N, d, Cq, Cm = w.N, w.d, w.Cq, w.Cm
+            sel_off = pl.sel_off.cpu().numpy()
+            n = (pl.q_off.view(w.BH, Cq + 1)[:, 1:] - pl.q_off.view(w.BH, Cq + 1)[:, :-1]).double()
+            pairs = float((n * pl.counts_r.view(w.BH, Cq).double()).sum())
+            acc = {"recall": [], "mass": [], "spearman": [], "err2": 0.0, "ref2": 0.0}
+            for bh in range(w.BH):
+                hs = slice(bh * N * d, (bh + 1) * N * d)
+                rows = torch.from_numpy(np.sort(rng.choice(N, a.fidelity_rows, replace=False))).to(dev)
+                base = bh * Cq
+                sets = lambda c, base=base: pl.sel_idx[int(sel_off[base + c]):int(sel_off[base + c + 1])]
+                r = proxy_fidelity_rows(
+                    qr[hs].view(N, d), kr[hs].view(N, d), vd[hs].view(N, d), pl.q_labels[bh * N:(bh + 1) * N],
+                    pl.lut[bh * Cq * 3 * Cm:(bh + 1) * Cq * 3 * Cm].view(Cq, 3, Cm),
+                    pl.k_codes[bh * N * 4:(bh + 1) * N * 4].view(N, 4)[:, :3].int() & 0xFFFF, sets,
+                    out[hs].view(N, d), rows)
+                for key in ("recall", "mass", "spearman"):
+                    acc[key].append(r[key])
+                acc["err2"] += r["err2"]
+                acc["ref2"] += r["ref2"]
+            e = res[rho]
+            for key in ("recall", "mass", "spearman"):
+                e[key].append(float(np.mean(np.concatenate(acc[key]))))
+            e["density"].append(pairs / (w.BH * float(N) ** 2))
+            e["err"].append(float(np.sqrt(acc["err2"] / acc["ref2"])))
+            print(json.dumps({"rep": rep, "rho": rho, "density": round(e["density"][-1], 4),
+                              "recall_top10": round(e["recall"][-1], 4), "mass": round(e["mass"][-1], 4),
+                              "spearman": round(e["spearman"][-1], 4), "rel_l2_vs_dense": round(e["err"][-1], 5)}),
+                  flush=True)
+            del pl
+    summary = {rho: {key: {"mean": float(np.mean(vals)), "std": float(np.std(vals, ddof=1))}
+                     for key, vals in e.items()} for rho, e in res.items()}
+    print(json.dumps({"fidelity": w0.name, "alpha": FID_ALPHA, "reps": FID_REPS, "rows_per_head": a.fidelity_rows,
+                      "top_frac": 0.1, "by_rho": {str(r): v for r, v in summary.items()}}), flush=True)
+
+
 def main():
     a = parse()
     if a.traffic_from:
@@ -242,6 +359,8 @@ def main():
         sys.exit(2)
     if a.profile_pass:
         return profile_pass(a)
+    if a.fidelity:
+        return fidelity(a)
     import torch
     import sparse_attention_video_rope_amd as sav
     import workloads
