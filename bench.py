@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fidelity", action="store_true", help="run the proxy-fidelity sweep instead of the bench")
     ap.add_argument("--fidelity-rows", type=int, default=32, help="sampled query rows per head for --fidelity")
+    ap.add_argument("--partition", choices=("rope", "random"), default="rope",
+                    help="--fidelity: proxy subspaces from the 3D-RoPE ranges or from a seeded random channel order")
     ap.add_argument("--warm-iters", type=int, default=2,
                     help="Lloyd iterations of the warm-started plan (negative: skip the warm-start measurement)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attend_traffic.json"),
@@ -306,9 +308,12 @@ def fidelity(a):
         q, k, v = workloads.generate(w)
         qd, kd, vd = (torch.from_numpy(x.reshape(-1)).to(dt).to(dev) for x in (q, k, v))
         del q, k, v
+        perm = None
+        if a.partition == "random":
+            perm = np.random.default_rng([w.index, 11]).permutation(w.d).tolist()
         for rho in FID_RHOS:
             rng = np.random.default_rng([w.index, 77])     # the same sampled rows at every rho
-            p = sav.params_for(w, rho=rho)
+            p = sav.params_for(w, rho=rho, channel_perm=perm)
             pl = sav.Plan(p, device=dev, debug=True)
             qr, kr, _ = sav.plan(p, qd, kd, pl)
             out = sav.attend(p, pl, qr, kr, vd)
@@ -345,7 +350,7 @@ def fidelity(a):
             del pl
     summary = {rho: {key: {"mean": float(np.mean(vals)), "std": float(np.std(vals, ddof=1))}
                      for key, vals in e.items()} for rho, e in res.items()}
-    print(json.dumps({"fidelity": w0.name, "alpha": FID_ALPHA, "reps": FID_REPS, "rows_per_head": a.fidelity_rows,
+    print(json.dumps({"fidelity": w0.name, "partition": a.partition, "alpha": FID_ALPHA, "reps": FID_REPS, "rows_per_head": a.fidelity_rows,
                       "top_frac": 0.1, "by_rho": {str(r): v for r, v in summary.items()}}), flush=True)
 
 

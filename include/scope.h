@@ -63,6 +63,9 @@ typedef enum { SCOPE_F32 = 0, SCOPE_BF16 = 1 } scope_dtype;
 /* scope_params.flags */
 #define SCOPE_USE_INIT_CENTROIDS 0x1u /* start Lloyd from plan->q_centroids / k_centroids
                                          instead of seeded k-means++ */
+#define SCOPE_PERMUTE_CHANNELS 0x2u   /* proxy subspaces from channel_perm instead of the
+                                         3D-RoPE ranges (the partition ablation, Table 3 of
+                                         the SCOPE paper's experiments): see channel_perm */
 
 typedef struct {
   int32_t B, H;            /* batch and heads; every (b, h) is independent; B*H <= 65535 */
@@ -77,7 +80,17 @@ typedef struct {
   double alpha;            /* fixed Top-k floor of Eq. (8) as a fraction of N, 0..1 */
   uint64_t seed;           /* k-means++ draws: SplitMix64 outputs */
   int32_t dtype;           /* scope_dtype */
-  uint32_t flags;          /* SCOPE_USE_INIT_CENTROIDS */
+  uint32_t flags;          /* SCOPE_USE_INIT_CENTROIDS | SCOPE_PERMUTE_CHANNELS */
+  /* With SCOPE_PERMUTE_CHANNELS: entries 0..d-1 are a permutation of
+   * 0..d-1 (else SCOPE_ERR_INVALID); the query clustering, the three key
+   * codebooks, the centroids and the LUT then work on the RoPE'd rows with
+   * their channels in this order (position i holds channel channel_perm[i]),
+   * so key subspace 0 is channels channel_perm[0 .. d_t), 1 the next d_h and
+   * 2 the last d_w.  q_rope / k_rope and the attention are unchanged (a
+   * common reordering of Q and K channels leaves every q.k); the workspace
+   * then holds one reordered copy of q_rope and of k_rope.  Ignored without
+   * the flag; entries d..127 are never read. */
+  uint8_t channel_perm[128];
 } scope_params;
 
 /* Device buffers of one plan (all caller-allocated; sizes in elements).

@@ -328,23 +328,34 @@ def scope_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, grid, split, dtyp
                Cq: int, Cm: int, iters: int, rho: float, alpha: float = 0.0,
                seed: int = 0, bh: int = 0, rope_base: float = 10000.0,
                init_q: Optional[np.ndarray] = None, init_k: Optional[np.ndarray] = None,
-               with_attention: bool = True) -> Dict[str, object]:
+               with_attention: bool = True, channel_perm: Optional[np.ndarray] = None) -> Dict[str, object]:
     """The whole path for one head; inputs are fp64 arrays holding `dtype` values.
 
     init_q [Cq, d] / init_k [Cm, d] replace k-means++ when given.
+
+    channel_perm (the partition ablation of the SCOPE paper's experiments,
+    Table 3: a random channel partition in place of the 3D-RoPE one): the
+    clustering, centroids, LUT and proxy use the RoPE'd rows with their
+    channels reordered, row[:, channel_perm], so key subspace m is the m-th
+    run of split[m] reordered channels; attention uses the rows as they are.
     """
     N, d = q.shape
     qr = round_storage(rope_3d(q, grid, split, rope_base), dtype)
     kr = round_storage(rope_3d(k, grid, split, rope_base), dtype)
+    qc, kc = qr, kr
+    if channel_perm is not None:
+        channel_perm = np.asarray(channel_perm)
+        assert sorted(channel_perm.tolist()) == list(range(d))
+        qc, kc = qr[:, channel_perm], kr[:, channel_perm]
 
-    kq = kmeans(qr, Cq, iters, dtype, seed, bh, 0, init_q)
+    kq = kmeans(qc, Cq, iters, dtype, seed, bh, 0, init_q)
     offs = subspace_offsets(split)
     k_cent = np.zeros((Cm, d))
     codes = np.zeros((N, 3), dtype=np.int64)
     k_seeds = []
     for m, (o, dm) in enumerate(zip(offs, split)):
         init = None if init_k is None else init_k[:, o:o + dm]
-        km = kmeans(kr[:, o:o + dm], Cm, iters, dtype, seed, bh, 1 + m, init)
+        km = kmeans(kc[:, o:o + dm], Cm, iters, dtype, seed, bh, 1 + m, init)
         k_cent[:, o:o + dm] = km["centroids"]
         codes[:, m] = km["labels"]
         k_seeds.append(km["seeds"])

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libscope.so")
 SCOPE_F32 = 0
 SCOPE_BF16 = 1
 SCOPE_USE_INIT_CENTROIDS = 0x1
+SCOPE_PERMUTE_CHANNELS = 0x2
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small",
           4: "plan buffer too small", 5: "HIP error"}
@@ -33,7 +34,8 @@ class Params(ctypes.Structure):
                 ("d", c_int32), ("d_t", c_int32), ("d_h", c_int32), ("d_w", c_int32),
                 ("Cq", c_int32), ("Cm", c_int32), ("iters", c_int32),
                 ("rope_base", c_double), ("rho", c_double), ("alpha", c_double),
-                ("seed", c_uint64), ("dtype", c_int32), ("flags", c_uint32)]
+                ("seed", c_uint64), ("dtype", c_int32), ("flags", c_uint32),
+                ("channel_perm", ctypes.c_uint8 * 128)]
 
     @property
     def N(self) -> int:
@@ -79,7 +81,9 @@ def load():
 
 
 def make_params(*, B, H, T, Hg, Wg, d, split, Cq, Cm, iters=10, rope_base=10000.0, rho=0.9, alpha=0.0,
-                seed=0, dtype="bf16", init_centroids=False) -> Params:
+                seed=0, dtype="bf16", init_centroids=False, channel_perm=None) -> Params:
+    """channel_perm: None, or the channel order of the proxy subspaces (a
+    permutation of 0..d-1; sets SCOPE_PERMUTE_CHANNELS)."""
     p = Params()
     p.B, p.H, p.T, p.Hg, p.Wg, p.d = B, H, T, Hg, Wg, d
     p.d_t, p.d_h, p.d_w = split
@@ -87,6 +91,13 @@ def make_params(*, B, H, T, Hg, Wg, d, split, Cq, Cm, iters=10, rope_base=10000.
     p.rope_base, p.rho, p.alpha, p.seed = float(rope_base), float(rho), float(alpha), int(seed)
     p.dtype = SCOPE_BF16 if dtype == "bf16" else SCOPE_F32
     p.flags = SCOPE_USE_INIT_CENTROIDS if init_centroids else 0
+    if channel_perm is not None:
+        cp = [int(c) for c in channel_perm]
+        if len(cp) != d:
+            raise ValueError(f"channel_perm: expected {d} entries, got {len(cp)}")
+        for i, c in enumerate(cp):
+            p.channel_perm[i] = c
+        p.flags |= SCOPE_PERMUTE_CHANNELS
     return p
 
 

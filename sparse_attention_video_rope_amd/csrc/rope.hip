@@ -185,4 +185,36 @@ hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const
   return hipGetLastError();
 }
 
+// Reordered copy of the RoPE'd rows for the partition ablation:
+// out[row][i] = in[row][perm[i]].  One thread per output element (coalesced
+// stores; the gathered loads stay inside one row of d elements).
+template <typename T>
+__global__ void __launch_bounds__(256) permute_kernel(const T* __restrict__ qi, const T* __restrict__ ki,
+                                                      T* __restrict__ qo, T* __restrict__ ko, ChanPerm perm,
+                                                      int d, size_t total) {
+  __shared__ uint8_t pl[128];
+  if (threadIdx.x < 128) pl[threadIdx.x] = perm.p[threadIdx.x];
+  __syncthreads();
+  const T* in = blockIdx.y ? ki : qi;
+  T* out = blockIdx.y ? ko : qo;
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const size_t row = e / (size_t)d;
+  const int i = (int)(e - row * (size_t)d);
+  out[e] = in[row * (size_t)d + pl[i]];
+}
+
+hipError_t launch_permute(const Geo& g, const ChanPerm& perm, const void* qr, const void* kr, const Workspace& w,
+                          hipStream_t s) {
+  const size_t total = (size_t)g.BH * g.N * g.d;
+  const dim3 blocks((unsigned)((total + 255) / 256), 2);
+  if (g.bf16)
+    permute_kernel<uint16_t><<<blocks, 256, 0, s>>>((const uint16_t*)qr, (const uint16_t*)kr, (uint16_t*)w.qperm,
+                                                   (uint16_t*)w.kperm, perm, g.d, total);
+  else
+    permute_kernel<float><<<blocks, 256, 0, s>>>((const float*)qr, (const float*)kr, (float*)w.qperm,
+                                                (float*)w.kperm, perm, g.d, total);
+  return hipGetLastError();
+}
+
 }  // namespace scope

@@ -31,6 +31,7 @@ Geo make_geo(const scope_params& p) {
     if (g.Cpad[m] > g.CmaxPad) g.CmaxPad = g.Cpad[m];
   }
   g.bf16 = p.dtype == SCOPE_BF16;
+  g.permute = (p.flags & SCOPE_PERMUTE_CHANNELS) ? 1 : 0;
   g.seed = p.seed;
   return g;
 }
@@ -66,6 +67,11 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
   w.csel = (ClusterSel*)take(sizeof(ClusterSel) * BH * g.Cq);
   w.htot = (int64_t*)take(8 * BH);
   w.hist1 = (int32_t*)take(4 * BH * g.Cq * (size_t)SEL_NB);
+  if (g.permute) {
+    const size_t rows = (size_t)(g.bf16 ? 2 : 4) * BH * N * g.d;
+    w.qperm = take(rows);
+    w.kperm = take(rows);
+  }
   w.bytes = o;
   if (plan) {
     if (plan->seeds) w.seeds = plan->seeds;
@@ -95,7 +101,15 @@ static scope_status validate(const scope_params* p) {
   if (!(p->rho > 0.0 && p->rho <= 1.0)) return SCOPE_ERR_INVALID;
   if (!(p->alpha >= 0.0 && p->alpha <= 1.0)) return SCOPE_ERR_INVALID;
   if (p->dtype != SCOPE_F32 && p->dtype != SCOPE_BF16) return SCOPE_ERR_INVALID;
-  if (p->flags & ~SCOPE_USE_INIT_CENTROIDS) return SCOPE_ERR_INVALID;
+  if (p->flags & ~(SCOPE_USE_INIT_CENTROIDS | SCOPE_PERMUTE_CHANNELS)) return SCOPE_ERR_INVALID;
+  if (p->flags & SCOPE_PERMUTE_CHANNELS) {
+    bool seen[128] = {};
+    for (int i = 0; i < p->d; ++i) {
+      const int c = p->channel_perm[i];
+      if (c >= p->d || seen[c]) return SCOPE_ERR_INVALID;
+      seen[c] = true;
+    }
+  }
   return SCOPE_OK;
 }
 
@@ -170,12 +184,22 @@ scope_status scope_plan(const scope_params* p, const void* q, const void* k, voi
   hipError_t e = hipSuccess;
 #define STEP(x) do { e = (x); if (e != hipSuccess) return hip_status(e); } while (0)
   STEP(launch_rope(g, *p, q, k, q_rope, k_rope, w, plan->k_norm_max, stream));
-  if (!(p->flags & SCOPE_USE_INIT_CENTROIDS)) STEP(launch_seed(g, q_rope, k_rope, w, stream));
+  // the clustering reads the rows in proxy channel order
+  const void* qc = q_rope;
+  const void* kc = k_rope;
+  if (g.permute) {
+    ChanPerm cp;
+    memcpy(cp.p, p->channel_perm, sizeof(cp.p));
+    STEP(launch_permute(g, cp, q_rope, k_rope, w, stream));
+    qc = w.qperm;
+    kc = w.kperm;
+  }
+  if (!(p->flags & SCOPE_USE_INIT_CENTROIDS)) STEP(launch_seed(g, qc, kc, w, stream));
   STEP(launch_prep(g, w, stream));
-  STEP(launch_assign(g, q_rope, k_rope, w, 0, stream));
+  STEP(launch_assign(g, qc, kc, w, 0, stream));
   for (int it = 1; it <= g.iters; ++it) {
-    STEP(launch_update(g, q_rope, k_rope, w, it, stream));
-    STEP(launch_assign(g, q_rope, k_rope, w, it, stream));
+    STEP(launch_update(g, qc, kc, w, it, stream));
+    STEP(launch_assign(g, qc, kc, w, it, stream));
   }
   STEP(launch_pack(g, w, plan->q_labels, stream));
   STEP(launch_perm(g, w, plan->perm_q, plan->q_off, stream));

@@ -23,7 +23,13 @@ struct Geo {
   int off[4], dm[4], C[4], Cpad[4], dpad[4];
   int Cmax, CmaxPad, DPmax;
   int bf16;                     // 1: bf16 storage, 0: fp32
+  int permute;                  // 1: clustering on channel-reordered copies of q_rope / k_rope
   uint64_t seed;
+};
+
+// Channel order of the proxy subspaces (kernel argument of the reordering kernel).
+struct ChanPerm {
+  uint8_t p[128];
 };
 
 // Per-cluster state of the selection kernels.
@@ -60,6 +66,8 @@ struct Workspace {
   ClusterSel* csel;             // [BH][Cq]
   int64_t* htot;                // [BH] per-head total of r_c, then the head's offset in sel_idx
   int32_t* hist1;               // [BH][Cq][SEL_NB] level-1 key counts of the Top-p pass (reused by the final selection)
+  void* qperm;                  // [BH][N][d] q_rope with reordered channels (SCOPE_PERMUTE_CHANNELS only)
+  void* kperm;                  // [BH][N][d] k_rope likewise
   size_t bytes;
 };
 
@@ -82,6 +90,8 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base);
 // ---- launchers (return hipGetLastError()) ---------------------------------
 hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const void* k, void* qo,
                        void* ko, const Workspace& w, float* k_norm_max, hipStream_t s);
+hipError_t launch_permute(const Geo& g, const ChanPerm& perm, const void* qr, const void* kr, const Workspace& w,
+                          hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_seed(const Geo& g, const void* qr, const void* kr, const Workspace& w, hipStream_t s);
 hipError_t launch_prep(const Geo& g, const Workspace& w, hipStream_t s);

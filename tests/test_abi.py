@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layout_matches_header(tmp_path):
     """Every field of the ctypes mirrors sits at the offset the C compiler gives it in include/scope.h."""
-    assert ctypes.sizeof(_lib.Params) == 88
+    assert ctypes.sizeof(_lib.Params) == 216
     structs = {"scope_params": _lib.Params, "scope_plan_t": _lib.PlanStruct}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "scope.h"', "int main(void) {"]
     for cname, py in structs.items():
@@ -79,6 +79,27 @@ def test_invalid_parameters(kw, code):
     p = good(**kw)
     st = sav.load().scope_workspace_size(ctypes.byref(p), None, None, None)
     assert st == code
+
+
+def test_channel_permutation_validation():
+    lib = sav.load()
+    perm = list(range(63, -1, -1))
+    p = good(channel_perm=perm)
+    assert lib.scope_workspace_size(ctypes.byref(p), None, None, None) == 0
+    for bad in (perm[:-1] + [perm[0]], [64] + perm[1:]):     # repeated channel; channel >= d
+        q = good()
+        for i, c in enumerate(bad):
+            q.channel_perm[i] = c
+        q.flags = _lib.SCOPE_PERMUTE_CHANNELS
+        assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 1
+    q = good()
+    q.flags = 0x4                                           # unknown flag
+    assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 1
+    # entries beyond d are not read; the reordered copies of q_rope / k_rope (bf16) enlarge the workspace
+    p.channel_perm[100] = 200
+    ws_p, _, _ = sav.sizes(p)
+    ws, _, _ = sav.sizes(good())
+    assert ws_p >= ws + 2 * (2 * 2 * 256 * 64)
 
 
 def test_workspace_size_and_capacities():

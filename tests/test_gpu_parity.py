@@ -252,6 +252,21 @@ def test_end_to_end_large_token_count(w):
         say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
 
 
+@pytest.mark.parametrize("w", SMALL + LARGE[:1], ids=IDS + LARGE_IDS[:1])
+def test_random_channel_partition_end_to_end(w):
+    """The partition ablation: proxy subspaces from a seeded random channel
+    order (SCOPE_PERMUTE_CHANNELS) instead of the 3D-RoPE ranges."""
+    perm = tuple(int(c) for c in np.random.default_rng([w.index, 11]).permutation(w.d))
+    say("random partition", w.name)
+    heads = oracle_heads(w, channel_perm=perm)
+    g = run_gpu(w, channel_perm=perm)
+    assert g["status"][1] == 0
+    assert_plan_equal(w, g, heads)
+    for bh, o in enumerate(heads):
+        mx, mn = assert_attention(g["out"][bh], o["out"], w.dtype, f"{w.name} head {bh}")
+        say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
+
+
 @pytest.mark.parametrize("grid", [(4, 61, 71), (7, 50, 77)])
 def test_kmeanspp_seeds_three_or_more_point_groups(grid):
     """Seeds only, at 17324 and 26950 tokens (3 and 4 groups of 8192 points)."""

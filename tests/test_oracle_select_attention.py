@@ -42,6 +42,47 @@ def test_check_a_proxy_is_exact_logit_when_every_key_is_its_own_centroid():
     np.testing.assert_allclose(s_rows, exact, rtol=1e-12, atol=1e-12)
 
 
+# --- the partition ablation (a reordered channel partition) -----------------
+
+def test_check_a_holds_for_a_random_channel_partition():
+    """Every key its own centroid: with any channel partition the proxy of a
+    query's own cluster is its exact logit row (a reordering applied to one
+    side only, or to different channels on the two sides, breaks this)."""
+    w = workloads.small("a", 2, 3, 4, 64, (16, 24, 24), "f32", 24, 24, H=1, iters=3)
+    q, k, v = workloads.generate(w)
+    perm = np.random.default_rng(5).permutation(64)
+    r = O.workload_head(w, 0, q[0], k[0], v[0], channel_perm=perm)
+    exact = r["q_rope"] @ r["k_rope"].T / 8.0
+    np.testing.assert_allclose(r["scores"][r["q_labels"]], exact, rtol=1e-12, atol=1e-12)
+    # the centroids live in the reordered channel space
+    np.testing.assert_array_equal(r["q_centroids"][r["q_labels"]], r["q_rope"][:, perm])
+
+
+def test_channel_order_inside_each_rope_range_does_not_change_the_plan():
+    """Reordering channels only inside each 3D-RoPE range leaves every
+    distance, and so the clustering, the proxy and the key sets, as they are;
+    the identity reordering reproduces the plain path exactly."""
+    w = workloads.small("p", 3, 5, 6, 64, (16, 24, 24), "bf16", 6, 10, H=1, iters=3)
+    q, k, v = workloads.generate(w)
+    base = O.workload_head(w, 0, q[0], k[0], v[0])
+    ident = O.workload_head(w, 0, q[0], k[0], v[0], channel_perm=np.arange(64))
+    rng = np.random.default_rng(9)
+    inside = np.concatenate([o + rng.permutation(dm) for o, dm in zip((0, 16, 40), (16, 24, 24))])
+    r = O.workload_head(w, 0, q[0], k[0], v[0], channel_perm=inside)
+    for x in (ident, r):
+        np.testing.assert_array_equal(x["q_labels"], base["q_labels"])
+        np.testing.assert_array_equal(x["k_codes"], base["k_codes"])
+        np.testing.assert_allclose(x["scores"], base["scores"], rtol=1e-12, atol=1e-12)
+        for a, b in zip(x["sel"], base["sel"]):
+            np.testing.assert_array_equal(a, b)
+        np.testing.assert_allclose(x["out"], base["out"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(r["q_centroids"], base["q_centroids"][:, inside])
+    np.testing.assert_array_equal(ident["k_centroids"], base["k_centroids"])
+    # a partition that mixes the ranges is a different proxy
+    mixed = O.workload_head(w, 0, q[0], k[0], v[0], channel_perm=rng.permutation(64))
+    assert not np.array_equal(mixed["k_codes"], base["k_codes"])
+
+
 # --- Top-p (Eq. (7)) --------------------------------------------------------
 
 def test_top_p_closed_form_when_all_scores_tie():
