@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--fidelity-rows", type=int, default=32, help="sampled query rows per head for --fidelity")
     ap.add_argument("--partition", choices=("rope", "random"), default="rope",
                     help="--fidelity: proxy subspaces from the 3D-RoPE ranges or from a seeded random channel order")
+    ap.add_argument("--selection", choices=("scope", "fixed-topk"), default="scope",
+                    help="--fidelity: the full selection, or Top-p / fixed Top-k without the online per-head Top-k "
+                         "at a rho matched to the full selection's density")
     ap.add_argument("--warm-iters", type=int, default=2,
                     help="Lloyd iterations of the warm-started plan (negative: skip the warm-start measurement)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attend_traffic.json"),
@@ -294,15 +297,76 @@ FID_ALPHA = 0.1
 FID_REPS = 3
 
 
+def _density(w, pl):
+    n = (pl.q_off.view(w.BH, w.Cq + 1)[:, 1:] - pl.q_off.view(w.BH, w.Cq + 1)[:, :-1]).double()
+    return float((n * pl.counts_r.view(w.BH, w.Cq).double()).sum()) / (w.BH * float(w.N) ** 2)
+
+
+def _fidelity_of_plan(a, w, p, pl, qd, kd, vd, rng):
+    """Plan + attend with p, then the proxy_fidelity_rows measures over every head."""
+    import torch
+    import sparse_attention_video_rope_amd as sav
+    qr, kr, _ = sav.plan(p, qd, kd, pl)
+    out = sav.attend(p, pl, qr, kr, vd)
+    torch.cuda.synchronize()
+    assert int(pl.status[1]) == 0, "selected-key capacity overflow"
+    N, d, Cq, Cm = w.N, w.d, w.Cq, w.Cm
+    sel_off = pl.sel_off.cpu().numpy()
+    acc = {"recall": [], "mass": [], "spearman": [], "err2": 0.0, "ref2": 0.0}
+    for bh in range(w.BH):
+        hs = slice(bh * N * d, (bh + 1) * N * d)
+        rows = torch.from_numpy(np.sort(rng.choice(N, a.fidelity_rows, replace=False))).to(qd.device)
+        base = bh * Cq
+        sets = lambda c, base=base: pl.sel_idx[int(sel_off[base + c]):int(sel_off[base + c + 1])]
+        r = proxy_fidelity_rows(
+            qr[hs].view(N, d), kr[hs].view(N, d), vd[hs].view(N, d), pl.q_labels[bh * N:(bh + 1) * N],
+            pl.lut[bh * Cq * 3 * Cm:(bh + 1) * Cq * 3 * Cm].view(Cq, 3, Cm),
+            pl.k_codes[bh * N * 4:(bh + 1) * N * 4].view(N, 4)[:, :3].int() & 0xFFFF, sets,
+            out[hs].view(N, d), rows)
+        for key in ("recall", "mass", "spearman"):
+            acc[key].append(r[key])
+        acc["err2"] += r["err2"]
+        acc["ref2"] += r["ref2"]
+    res = {key: float(np.mean(np.concatenate(acc[key]))) for key in ("recall", "mass", "spearman")}
+    res["density"] = _density(w, pl)
+    res["err"] = float(np.sqrt(acc["err2"] / acc["ref2"]))
+    return res
+
+
+def _matched_rho(w, sav, qd, kd, pl, target, lo, perm, steps=14):
+    """rho of the fixed-Top-k-only selection whose realised density is closest to target (bisection;
+    the density is nondecreasing in rho)."""
+    import torch
+    best = (float("inf"), 1.0)
+    hi = 1.0
+    for _ in range(steps):
+        mid = 0.5 * (lo + hi)
+        p = sav.params_for(w, rho=mid, channel_perm=perm, online_khead=False)
+        sav.plan(p, qd, kd, pl)
+        torch.cuda.synchronize()
+        dens = _density(w, pl)
+        best = min(best, (abs(dens - target), mid))
+        if dens < target:
+            lo = mid
+        else:
+            hi = mid
+    return best[1]
+
+
 def fidelity(a):
-    """Proxy-fidelity sweep on the GPU plans of the workload (three input seeds)."""
+    """Proxy-fidelity sweep on the GPU plans of the workload (three input seeds).
+
+    --selection fixed-topk: at every rho, the selection without the online
+    per-head Top-k (r_c = b_c), with its own rho' set so that its realised
+    density matches the full method's at rho (the Fig. 7 comparison)."""
     import torch
     import sparse_attention_video_rope_amd as sav
     import workloads
     w0 = workloads.CONFIGS[a.config]
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w0.dtype == "bf16" else torch.float32
-    res = {rho: {"recall": [], "mass": [], "spearman": [], "density": [], "err": []} for rho in FID_RHOS}
+    keys = ("recall", "mass", "spearman", "density", "err", "rho_used")
+    res = {rho: {k: [] for k in keys} for rho in FID_RHOS}
     for rep in range(FID_REPS):
         w = w0.with_(index=w0.index + 1000 * rep, alpha=FID_ALPHA)
         q, k, v = workloads.generate(w)
@@ -311,47 +375,27 @@ def fidelity(a):
         perm = None
         if a.partition == "random":
             perm = np.random.default_rng([w.index, 11]).permutation(w.d).tolist()
+        pl = sav.Plan(sav.params_for(w, channel_perm=perm), device=dev, debug=True)
         for rho in FID_RHOS:
             rng = np.random.default_rng([w.index, 77])     # the same sampled rows at every rho
             p = sav.params_for(w, rho=rho, channel_perm=perm)
-            pl = sav.Plan(p, device=dev, debug=True)
-            qr, kr, _ = sav.plan(p, qd, kd, pl)
-            out = sav.attend(p, pl, qr, kr, vd)
-            torch.cuda.synchronize()
-            assert int(pl.status[1]) == 0, "selected-key capacity overflow"
-            N, d, Cq, Cm = w.N, w.d, w.Cq, w.Cm
-            sel_off = pl.sel_off.cpu().numpy()
-            n = (pl.q_off.view(w.BH, Cq + 1)[:, 1:] - pl.q_off.view(w.BH, Cq + 1)[:, :-1]).double()
-            pairs = float((n * pl.counts_r.view(w.BH, Cq).double()).sum())
-            acc = {"recall": [], "mass": [], "spearman": [], "err2": 0.0, "ref2": 0.0}
-            for bh in range(w.BH):
-                hs = slice(bh * N * d, (bh + 1) * N * d)
-                rows = torch.from_numpy(np.sort(rng.choice(N, a.fidelity_rows, replace=False))).to(dev)
-                base = bh * Cq
-                sets = lambda c, base=base: pl.sel_idx[int(sel_off[base + c]):int(sel_off[base + c + 1])]
-                r = proxy_fidelity_rows(
-                    qr[hs].view(N, d), kr[hs].view(N, d), vd[hs].view(N, d), pl.q_labels[bh * N:(bh + 1) * N],
-                    pl.lut[bh * Cq * 3 * Cm:(bh + 1) * Cq * 3 * Cm].view(Cq, 3, Cm),
-                    pl.k_codes[bh * N * 4:(bh + 1) * N * 4].view(N, 4)[:, :3].int() & 0xFFFF, sets,
-                    out[hs].view(N, d), rows)
-                for key in ("recall", "mass", "spearman"):
-                    acc[key].append(r[key])
-                acc["err2"] += r["err2"]
-                acc["ref2"] += r["ref2"]
-            e = res[rho]
-            for key in ("recall", "mass", "spearman"):
-                e[key].append(float(np.mean(np.concatenate(acc[key]))))
-            e["density"].append(pairs / (w.BH * float(N) ** 2))
-            e["err"].append(float(np.sqrt(acc["err2"] / acc["ref2"])))
-            print(json.dumps({"rep": rep, "rho": rho, "density": round(e["density"][-1], 4),
-                              "recall_top10": round(e["recall"][-1], 4), "mass": round(e["mass"][-1], 4),
-                              "spearman": round(e["spearman"][-1], 4), "rel_l2_vs_dense": round(e["err"][-1], 5)}),
-                  flush=True)
-            del pl
+            rho_used = rho
+            if a.selection == "fixed-topk":
+                sav.plan(p, qd, kd, pl)
+                torch.cuda.synchronize()
+                rho_used = _matched_rho(w, sav, qd, kd, pl, _density(w, pl), rho, perm)
+                p = sav.params_for(w, rho=rho_used, channel_perm=perm, online_khead=False)
+            r = _fidelity_of_plan(a, w, p, pl, qd, kd, vd, rng)
+            r["rho_used"] = rho_used
+            for key in keys:
+                res[rho][key].append(r[key])
+            print(json.dumps({"rep": rep, "rho": rho, **{k_: round(r[k_], 5) for k_ in keys}}), flush=True)
+        del pl
     summary = {rho: {key: {"mean": float(np.mean(vals)), "std": float(np.std(vals, ddof=1))}
                      for key, vals in e.items()} for rho, e in res.items()}
-    print(json.dumps({"fidelity": w0.name, "partition": a.partition, "alpha": FID_ALPHA, "reps": FID_REPS, "rows_per_head": a.fidelity_rows,
-                      "top_frac": 0.1, "by_rho": {str(r): v for r, v in summary.items()}}), flush=True)
+    print(json.dumps({"fidelity": w0.name, "partition": a.partition, "selection": a.selection, "alpha": FID_ALPHA,
+                      "reps": FID_REPS, "rows_per_head": a.fidelity_rows, "top_frac": 0.1,
+                      "by_rho": {str(r): v for r, v in summary.items()}}), flush=True)
 
 
 def main():

@@ -66,6 +66,10 @@ typedef enum { SCOPE_F32 = 0, SCOPE_BF16 = 1 } scope_dtype;
 #define SCOPE_PERMUTE_CHANNELS 0x2u   /* proxy subspaces from channel_perm instead of the
                                          3D-RoPE ranges (the partition ablation, Table 3 of
                                          the SCOPE paper's experiments): see channel_perm */
+#define SCOPE_FIXED_TOPK_ONLY 0x4u    /* r_c = b_c (Eq. 8) for non-empty clusters: the hybrid
+                                         Top-p / fixed Top-k selection without the online
+                                         per-head Top-k extension of Eq. (10) (the Fig. 7
+                                         ablation); k_head is still computed and written */
 
 typedef struct {
   int32_t B, H;            /* batch and heads; every (b, h) is independent; B*H <= 65535 */
@@ -80,7 +84,7 @@ typedef struct {
   double alpha;            /* fixed Top-k floor of Eq. (8) as a fraction of N, 0..1 */
   uint64_t seed;           /* k-means++ draws: SplitMix64 outputs */
   int32_t dtype;           /* scope_dtype */
-  uint32_t flags;          /* SCOPE_USE_INIT_CENTROIDS | SCOPE_PERMUTE_CHANNELS */
+  uint32_t flags;          /* SCOPE_USE_INIT_CENTROIDS | SCOPE_PERMUTE_CHANNELS | SCOPE_FIXED_TOPK_ONLY */
   /* With SCOPE_PERMUTE_CHANNELS: entries 0..d-1 are a permutation of
    * 0..d-1 (else SCOPE_ERR_INVALID); the query clustering, the three key
    * codebooks, the centroids and the LUT then work on the RoPE'd rows with

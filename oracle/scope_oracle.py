@@ -269,20 +269,23 @@ def k_head_of(n: Sequence[int], b: Sequence[int]) -> int:
     return -((-num) // den)
 
 
-def hybrid_select(s: np.ndarray, n: np.ndarray, rho: float, alpha: float):
+def hybrid_select(s: np.ndarray, n: np.ndarray, rho: float, alpha: float, online_khead: bool = True):
     """Top-p counts t, base counts b (Eq. 8), k_head (Eq. 9), final counts r (Eq. 10), key sets.
 
     b_c = max(t_c, ceil(alpha*N)) (reading: alpha is the fixed Top-k floor as a
     fraction of N); r_c = max(b_c, k_head) for non-empty clusters, 0 for empty
     ones; the keys of cluster c are its first r_c keys in key_order, returned
-    in ascending index order.
+    in ascending index order.  online_khead=False: r_c = b_c (the hybrid
+    Top-p / fixed Top-k selection the method extends, as in the SCOPE
+    paper's Fig. 7 ablation); k_head is still returned.
     """
     Cq, N = s.shape
     floor = math.ceil(alpha * N)
     t = np.array([top_p_count(s[c], rho) for c in range(Cq)], dtype=np.int64)
     b = np.maximum(t, floor)
     kh = k_head_of(n, b)
-    r = np.where(n > 0, np.maximum(b, kh), 0)
+    # without the online extension (the Fig. 7 ablation): the base counts alone
+    r = np.where(n > 0, np.maximum(b, kh) if online_khead else b, 0)
     sel = [np.sort(key_order(s[c])[: r[c]]) for c in range(Cq)]
     return t, b, kh, r, sel
 
@@ -328,7 +331,8 @@ def scope_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, grid, split, dtyp
                Cq: int, Cm: int, iters: int, rho: float, alpha: float = 0.0,
                seed: int = 0, bh: int = 0, rope_base: float = 10000.0,
                init_q: Optional[np.ndarray] = None, init_k: Optional[np.ndarray] = None,
-               with_attention: bool = True, channel_perm: Optional[np.ndarray] = None) -> Dict[str, object]:
+               with_attention: bool = True, channel_perm: Optional[np.ndarray] = None,
+               online_khead: bool = True) -> Dict[str, object]:
     """The whole path for one head; inputs are fp64 arrays holding `dtype` values.
 
     init_q [Cq, d] / init_k [Cm, d] replace k-means++ when given.
@@ -363,7 +367,7 @@ def scope_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, grid, split, dtyp
     P = lookup_tables(kq["centroids"], k_cent, split)
     s = proxy_logits(P, codes, d)
     n = np.bincount(kq["labels"], minlength=Cq)
-    t, b, kh, r, sel = hybrid_select(s, n, rho, alpha)
+    t, b, kh, r, sel = hybrid_select(s, n, rho, alpha, online_khead)
     perm, q_off = cluster_permutation(kq["labels"], Cq)
     res = {
         "q_rope": qr, "k_rope": kr,

@@ -5,8 +5,8 @@ hybrid Top-p with online per-head k_head, gathered exact attention) runs in
 the HIP library libscope.so behind the C ABI of include/scope.h; this package
 is its Python binding.
 """
-from ._lib import (SCOPE_BF16, SCOPE_F32, SCOPE_PERMUTE_CHANNELS, SCOPE_USE_INIT_CENTROIDS, Params, Plan, ScopeError,
+from ._lib import (SCOPE_BF16, SCOPE_F32, SCOPE_FIXED_TOPK_ONLY, SCOPE_PERMUTE_CHANNELS, SCOPE_USE_INIT_CENTROIDS, Params, Plan, ScopeError,
                    attend, load, make_params, params_for, plan, plan_finalize, sizes)
 
-__all__ = ["SCOPE_BF16", "SCOPE_F32", "SCOPE_PERMUTE_CHANNELS", "SCOPE_USE_INIT_CENTROIDS", "Params", "Plan",
+__all__ = ["SCOPE_BF16", "SCOPE_F32", "SCOPE_FIXED_TOPK_ONLY", "SCOPE_PERMUTE_CHANNELS", "SCOPE_USE_INIT_CENTROIDS", "Params", "Plan",
            "ScopeError", "attend", "load", "make_params", "params_for", "plan", "plan_finalize", "sizes"]

@@ -18,6 +18,7 @@ SCOPE_F32 = 0
 SCOPE_BF16 = 1
 SCOPE_USE_INIT_CENTROIDS = 0x1
 SCOPE_PERMUTE_CHANNELS = 0x2
+SCOPE_FIXED_TOPK_ONLY = 0x4
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small",
           4: "plan buffer too small", 5: "HIP error"}
@@ -81,9 +82,10 @@ def load():
 
 
 def make_params(*, B, H, T, Hg, Wg, d, split, Cq, Cm, iters=10, rope_base=10000.0, rho=0.9, alpha=0.0,
-                seed=0, dtype="bf16", init_centroids=False, channel_perm=None) -> Params:
+                seed=0, dtype="bf16", init_centroids=False, channel_perm=None, online_khead=True) -> Params:
     """channel_perm: None, or the channel order of the proxy subspaces (a
-    permutation of 0..d-1; sets SCOPE_PERMUTE_CHANNELS)."""
+    permutation of 0..d-1; sets SCOPE_PERMUTE_CHANNELS); online_khead=False
+    sets SCOPE_FIXED_TOPK_ONLY (r_c = b_c)."""
     p = Params()
     p.B, p.H, p.T, p.Hg, p.Wg, p.d = B, H, T, Hg, Wg, d
     p.d_t, p.d_h, p.d_w = split
@@ -91,6 +93,8 @@ def make_params(*, B, H, T, Hg, Wg, d, split, Cq, Cm, iters=10, rope_base=10000.
     p.rope_base, p.rho, p.alpha, p.seed = float(rope_base), float(rho), float(alpha), int(seed)
     p.dtype = SCOPE_BF16 if dtype == "bf16" else SCOPE_F32
     p.flags = SCOPE_USE_INIT_CENTROIDS if init_centroids else 0
+    if not online_khead:
+        p.flags |= SCOPE_FIXED_TOPK_ONLY
     if channel_perm is not None:
         cp = [int(c) for c in channel_perm]
         if len(cp) != d:

@@ -32,6 +32,7 @@ Geo make_geo(const scope_params& p) {
   }
   g.bf16 = p.dtype == SCOPE_BF16;
   g.permute = (p.flags & SCOPE_PERMUTE_CHANNELS) ? 1 : 0;
+  g.online_khead = (p.flags & SCOPE_FIXED_TOPK_ONLY) ? 0 : 1;
   g.seed = p.seed;
   return g;
 }
@@ -101,7 +102,7 @@ static scope_status validate(const scope_params* p) {
   if (!(p->rho > 0.0 && p->rho <= 1.0)) return SCOPE_ERR_INVALID;
   if (!(p->alpha >= 0.0 && p->alpha <= 1.0)) return SCOPE_ERR_INVALID;
   if (p->dtype != SCOPE_F32 && p->dtype != SCOPE_BF16) return SCOPE_ERR_INVALID;
-  if (p->flags & ~(SCOPE_USE_INIT_CENTROIDS | SCOPE_PERMUTE_CHANNELS)) return SCOPE_ERR_INVALID;
+  if (p->flags & ~(SCOPE_USE_INIT_CENTROIDS | SCOPE_PERMUTE_CHANNELS | SCOPE_FIXED_TOPK_ONLY)) return SCOPE_ERR_INVALID;
   if (p->flags & SCOPE_PERMUTE_CHANNELS) {
     bool seen[128] = {};
     for (int i = 0; i < p->d; ++i) {

@@ -24,6 +24,7 @@ struct Geo {
   int Cmax, CmaxPad, DPmax;
   int bf16;                     // 1: bf16 storage, 0: fp32
   int permute;                  // 1: clustering on channel-reordered copies of q_rope / k_rope
+  int online_khead;             // 1: r_c = max(b_c, k_head) (Eq. 10); 0: r_c = b_c
   uint64_t seed;
 };
 

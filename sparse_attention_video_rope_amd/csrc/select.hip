@@ -515,7 +515,9 @@ __global__ __launch_bounds__(NT) void topp_kernel(SelArgs a, const double* __res
 }
 
 // ---------------------------------------------------------------------------
-// Stage 5b: k_head (Eq. 9), r_c (Eq. 10) and the CSR offsets.
+// Stage 5b: k_head (Eq. 9), r_c (Eq. 10) and the CSR offsets (r_c = b_c when
+// the online per-head Top-k is switched off: the hybrid Top-p / fixed Top-k
+// selection SCOPE builds on).
 // khead_kernel (one workgroup per head) writes k_head, r_c, the head-local
 // prefix of r_c into sel_off and the head total; seloff_scan_kernel turns the
 // head totals into head offsets (and flags a capacity overflow);
@@ -523,7 +525,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(SelArgs a, const double* __res
 // ---------------------------------------------------------------------------
 constexpr int KH_NT = 256;
 
-__global__ __launch_bounds__(KH_NT) void khead_kernel(int Cq, int N, const int32_t* __restrict__ q_off,
+__global__ __launch_bounds__(KH_NT) void khead_kernel(int Cq, int N, int online, const int32_t* __restrict__ q_off,
                                                       const int32_t* __restrict__ cb, int32_t* __restrict__ cr,
                                                       int32_t* __restrict__ khead, int64_t* __restrict__ sel_off,
                                                       int64_t* __restrict__ htot) {
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(KH_NT) void khead_kernel(int Cq, int N, const int32
     if (c < Cq) {
       const int64_t n = qo[c + 1] - qo[c];
       const int64_t b = cb[(size_t)bh * Cq + c];
-      r = n > 0 ? (b > kh ? b : kh) : 0;
+      r = n > 0 ? ((online && kh > b) ? kh : b) : 0;
       if (r > N) r = N;
       cr[(size_t)bh * Cq + c] = (int32_t)r;
     }
@@ -762,7 +764,7 @@ hipError_t launch_topp(const Geo& g, const scope_params& p, const Workspace& w, 
 }
 
 hipError_t launch_khead(const Geo& g, const scope_plan_t& plan, const Workspace& w, hipStream_t s) {
-  khead_kernel<<<g.BH, KH_NT, 0, s>>>(g.Cq, g.N, plan.q_off, plan.counts_b, plan.counts_r, plan.k_head, plan.sel_off,
+  khead_kernel<<<g.BH, KH_NT, 0, s>>>(g.Cq, g.N, g.online_khead, plan.q_off, plan.counts_b, plan.counts_r, plan.k_head, plan.sel_off,
                                       w.htot);
   seloff_scan_kernel<<<1, 1024, 0, s>>>(g.BH, g.Cq, w.htot, plan.sel_off, plan.sel_capacity, plan.status);
   seloff_add_kernel<<<dim3((g.Cq + 255) / 256, g.BH), 256, 0, s>>>(g.Cq, w.htot, plan.sel_off);

@@ -92,8 +92,9 @@ def test_channel_permutation_validation():
             q.channel_perm[i] = c
         q.flags = _lib.SCOPE_PERMUTE_CHANNELS
         assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 1
-    q = good()
-    q.flags = 0x4                                           # unknown flag
+    q = good(online_khead=False)
+    assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 0
+    q.flags = 0x8                                           # unknown flag
     assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 1
     # entries beyond d are not read; the reordered copies of q_rope / k_rope (bf16) enlarge the workspace
     p.channel_perm[100] = 200

@@ -310,3 +310,38 @@ def test_warm_start_from_own_centroids_is_a_fixed_point(name):
     assert torch.equal(pl.k_codes.view(-1, 4)[:, :3], run.pl.k_codes.view(-1, 4)[:, :3])
     n = int(run.sel_off[-1])
     assert torch.equal(pl.sel_idx[:n], run.pl.sel_idx[:n])
+
+
+def test_alpha_floor_with_and_without_online_topk_full_size():
+    """CogVideoX-like at the alpha = 0.1 floor: Eq. (8)-(10) count relations on
+    every head with the online per-head Top-k, and r_c = b_c without it
+    (SCOPE_FIXED_TOPK_ONLY), whose key sets are then prefixes of the full ones."""
+    base = full_run("cogvideox")
+    w = base.w.with_(alpha=0.1)
+    qd, kd, _ = base.inputs
+    got = {}
+    for online in (True, False):
+        p = sav.params_for(w, rho=base.rho, online_khead=online)
+        pl = sav.Plan(p, debug=False)
+        sav.plan(p, qd, kd, pl)
+        torch.cuda.synchronize()
+        assert int(pl.status[1]) == 0
+        BH, Cq = w.BH, w.Cq
+        t = pl.counts_t.cpu().numpy().reshape(BH, Cq)
+        b = pl.counts_b.cpu().numpy().reshape(BH, Cq)
+        r = pl.counts_r.cpu().numpy().reshape(BH, Cq)
+        kh = pl.k_head.cpu().numpy()
+        n = np.diff(pl.q_off.cpu().numpy().reshape(BH, Cq + 1), axis=1)
+        assert np.array_equal(b, np.maximum(t, math.ceil(0.1 * w.N)))
+        for bh in range(BH):
+            assert kh[bh] == -((-int(np.dot(n[bh].astype(np.int64), b[bh]))) // w.N)
+        want = np.maximum(b, kh[:, None]) if online else b
+        assert np.array_equal(r, np.where(n > 0, want, 0))
+        so = pl.sel_off.cpu().numpy()
+        assert int(so[-1]) == int(r.sum())
+        got[online] = (so, pl.sel_idx[:int(so[-1])].cpu().numpy(), t)
+    assert np.array_equal(got[True][2], got[False][2])
+    (so1, s1, _), (so0, s0, _) = got[True], got[False]
+    for c in range(0, w.Cq * 2):          # heads 0 and 1
+        a = set(s0[so0[c]:so0[c + 1]].tolist())
+        assert a <= set(s1[so1[c]:so1[c + 1]].tolist())

@@ -267,6 +267,21 @@ def test_random_channel_partition_end_to_end(w):
         say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
 
 
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_fixed_topk_only_end_to_end(w):
+    """The selection without the online per-head Top-k (SCOPE_FIXED_TOPK_ONLY,
+    r_c = b_c) at the alpha = 0.1 floor."""
+    wa = w.with_(alpha=0.1)
+    say("fixed top-k only", w.name)
+    heads = oracle_heads(wa, online_khead=False)
+    g = run_gpu(wa, online_khead=False)
+    assert g["status"][1] == 0
+    assert_plan_equal(wa, g, heads)
+    for bh, o in enumerate(heads):
+        mx, mn = assert_attention(g["out"][bh], o["out"], w.dtype, f"{w.name} head {bh}")
+        say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
+
+
 @pytest.mark.parametrize("grid", [(4, 61, 71), (7, 50, 77)])
 def test_kmeanspp_seeds_three_or_more_point_groups(grid):
     """Seeds only, at 17324 and 26950 tokens (3 and 4 groups of 8192 points)."""

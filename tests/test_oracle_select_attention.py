@@ -42,6 +42,27 @@ def test_check_a_proxy_is_exact_logit_when_every_key_is_its_own_centroid():
     np.testing.assert_allclose(s_rows, exact, rtol=1e-12, atol=1e-12)
 
 
+# --- without the online per-head Top-k (the Fig. 7 ablation) ---------------
+
+def test_fixed_topk_only_keeps_the_base_counts():
+    """r_c = b_c without the Eq. (10) extension; the key sets are prefixes of
+    the full method's (same order), and only clusters with b_c < k_head shrink."""
+    rng = np.random.default_rng(4)
+    Cq, N = 6, 200
+    s = rng.standard_normal((Cq, N)) * np.array([[0.1], [3.0], [1.0], [8.0], [0.5], [2.0]])
+    n = np.array([30, 5, 0, 60, 10, 95])
+    t, b, kh, r, sel = O.hybrid_select(s, n, 0.8, 0.05)
+    t2, b2, kh2, r2, sel2 = O.hybrid_select(s, n, 0.8, 0.05, online_khead=False)
+    assert np.array_equal(t, t2) and np.array_equal(b, b2) and kh == kh2
+    assert np.array_equal(r2, np.where(n > 0, b, 0))
+    assert r2[2] == 0 and r[2] == 0
+    for c in range(Cq):
+        assert set(sel2[c].tolist()) <= set(sel[c].tolist())
+        assert len(sel2[c]) == r2[c]
+    assert np.any(r2 < r)                       # the extension matters on this example
+    assert np.array_equal(r2[b >= kh], r[b >= kh])
+
+
 # --- the partition ablation (a reordered channel partition) -----------------
 
 def test_check_a_holds_for_a_random_channel_partition():
