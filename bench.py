@@ -184,12 +184,15 @@ def _dense_rel_l2(w, qr, kr, vd, outs, torch):
     q, k, v = (t.view(BH, N, d) for t in (qr, kr, vd))
     num = [0.0] * len(outs)
     den = 0.0
+    rows = 4096                                   # query rows per block (bounded memory at any N)
     for h in range(BH):
-        qh, kh, vh = q[h].float(), k[h].float(), v[h].float()
-        ref = torch.softmax((qh @ kh.t().contiguous()) / float(np.sqrt(d)), dim=1) @ vh
-        den += float(ref.double().pow(2).sum())
-        for i, o in enumerate(outs):
-            num[i] += float((o.view(BH, N, d)[h].float() - ref).double().pow(2).sum())
+        kt, vh = k[h].float().t().contiguous(), v[h].float()
+        for r0 in range(0, N, rows):
+            qh = q[h, r0:r0 + rows].float()
+            ref = torch.softmax((qh @ kt) / float(np.sqrt(d)), dim=1) @ vh
+            den += float(ref.double().pow(2).sum())
+            for i, o in enumerate(outs):
+                num[i] += float((o.view(BH, N, d)[h, r0:r0 + rows].float() - ref).double().pow(2).sum())
     return [float(np.sqrt(x / den)) for x in num]
 
 
