@@ -114,7 +114,11 @@ typedef struct {
   int64_t sel_capacity;  /* elements of sel_idx; B*H*Cq*N always suffices */
   int32_t* work;         /* [2*work_capacity]: attention work items (built by scope_plan) */
   int64_t work_capacity; /* items; from scope_workspace_size */
-  int32_t* status;       /* [4]: [0] work items, [1] set if sum r_c > sel_capacity */
+  int32_t* status;       /* [4]: [0] work items, [1] set if sum r_c > sel_capacity,
+                            [2] set if the workgroups that share one k-means++
+                            clustering (large N, bf16) stopped waiting on each other
+                            (not expected: they are launched cooperatively; the
+                            plan's clusters are then not valid) */
   float* q_centroids;    /* [B*H][Cq][d] final query centroids (fp32) */
   float* k_centroids;    /* [B*H][Cm][d] key centroids, row z = (mu^T_z | mu^H_z | mu^W_z) */
   int32_t* q_labels;     /* [B*H][N] query cluster of each token */

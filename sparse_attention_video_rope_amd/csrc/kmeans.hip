@@ -100,11 +100,33 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Exchange area of one clustering when W workgroups share its points
+// (SeedSync::W > 1, a cooperative launch: all of them are resident at once).
+// Each workgroup owns a contiguous run of groups; per draw it publishes the
+// exact sum of its D^2, waits for the others, and the workgroup holding the
+// crossing publishes the drawn index (two waits per draw).
+static_assert(SEED_SYNC_BYTES == 8 + 8 * SEED_MAX_GROUPS + 4 * MAX_C, "exchange area layout");
+constexpr uint32_t SEED_SPIN_LIMIT = 1u << 18;   // polls before giving up: well over a second, far above one draw
+struct SeedSync {
+  char* base;        // [BH][4] areas of SEED_SYNC_BYTES: counter, drawn index, part[32], lowest[MAX_C]
+  int32_t* abort;    // set when a wait ran out (every later wait is then skipped)
+  int W;             // workgroups per clustering (1: no exchange)
+};
+
+__global__ void seed_sync_init_kernel(char* base, int chains, int32_t* abort) {
+  const int c = blockIdx.x;
+  int32_t* a = reinterpret_cast<int32_t*>(base + (size_t)c * SEED_SYNC_BYTES);
+  int32_t* lo = reinterpret_cast<int32_t*>(base + (size_t)c * SEED_SYNC_BYTES + 8 + 8 * SEED_MAX_GROUPS);
+  if (threadIdx.x == 0) { a[0] = 0; a[1] = 0; }
+  for (int i = threadIdx.x; i < MAX_C; i += blockDim.x) lo[i] = 0x7FFFFFFF;
+  if (c == 0 && threadIdx.x == 0) *abort = 0;
+}
+
 template <typename T, bool RESIDENT>
 __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr, const T* __restrict__ kr, Geo g,
                                                        double* __restrict__ d2all, uint16_t* __restrict__ nearall,
                                                        int32_t* __restrict__ seeds, float* __restrict__ qcent,
-                                                       float* __restrict__ kcent) {
+                                                       float* __restrict__ kcent, SeedSync sy) {
   const int m = blockIdx.y, bh = blockIdx.x;
   const int N = g.N, d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m];
   const T* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + off;
@@ -118,7 +140,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
   __shared__ double wsum[SEED_MAX_GROUPS * SEED_NW];
   __shared__ double gscr[SEED_RG * 64];
   __shared__ double sh_excl, sh_target;
-  __shared__ int32_t sh_grp, sh_wave, sh_mode, sh_lo, sh_hi;
+  __shared__ int32_t sh_grp, sh_wave, sh_mode, sh_lo, sh_hi, sh_own;
   extern __shared__ __align__(16) unsigned char seed_smem[];
   int32_t* lp = reinterpret_cast<int32_t*>(seed_smem) + (threadIdx.x >> 6) * SEED_LIST;
   double* ldist = reinterpret_cast<double*>(seed_smem + SEED_NW * SEED_LIST * 4) + (threadIdx.x >> 6) * SEED_LIST;
@@ -164,6 +186,64 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
 #pragma unroll
   for (int k = 0; k < SEED_RG; ++k) { gd2[k] = 0.0; nr_set(k, NR_MARK); }
 
+  // this workgroup's groups [gi0, gi1) of the clustering
+  const int W = sy.W, wg = blockIdx.z;
+  const int gi0 = (int)((int64_t)wg * G / W), gi1 = (int)((int64_t)(wg + 1) * G / W);
+  char* xs = sy.base + ((size_t)bh * 4 + m) * SEED_SYNC_BYTES;
+  int32_t* x_ctr = reinterpret_cast<int32_t*>(xs);
+  int32_t* x_ci = x_ctr + 1;
+  unsigned long long* x_part = reinterpret_cast<unsigned long long*>(xs + 8);
+  int32_t* x_lo = reinterpret_cast<int32_t*>(xs + 8 + 8 * SEED_MAX_GROUPS);
+  // the crossing wave (ww) of group gg: rounds of its group, then lanes of
+  // the crossing round; sh_excl is the sum of D^2 before the wave's points
+  auto cross_wave = [&](int gg, int ww) __attribute__((always_inline)) {
+    const int r0 = gg * SEED_RG;
+    if (RESIDENT) {
+#pragma unroll
+      for (int k = 0; k < SEED_RG; ++k) gscr[k * 64 + lane] = gd2[k];
+    } else {
+      for (int k = 0; k < SEED_RG; ++k) {
+        const int p = pidx(r0, k);
+        gscr[k * 64 + lane] = p < N ? D2g[p] : 0.0;
+      }
+    }
+    wave_sync_lds();
+    double excl = sh_excl;
+    const double target = sh_target;
+    int ksel = -1, klast = -1;
+    for (int k = 0; k < SEED_RG; ++k) {
+      const double rs = wave_sum_dpp(gscr[k * 64 + lane]);
+      if (rs > 0.0) klast = k;
+      if (ksel < 0) { if (excl + rs > target) ksel = k; else excl += rs; }
+    }
+    if (ksel < 0) ksel = klast;   // rounding: the group's last round with weight
+    const double v = gscr[ksel * 64 + lane];
+    const double inc = excl + wave_incl_scan(v);
+    const uint64_t hit = __ballot(inc > target);
+    const uint64_t pos = __ballot(v > 0.0);
+    const int L = hit ? __ffsll((unsigned long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+    if (lane == 0) sh_lo = r0 * SEED_NT + ww * (SEED_RG * 64) + ksel * 64 + L;
+    wave_sync_lds();
+  };
+  int nwait = 0;
+  // every workgroup of the clustering reaches this point (bounded polling)
+  auto chain_wait = [&]() __attribute__((always_inline)) {
+    __syncthreads();
+    ++nwait;
+    if (tid == 0) {
+      __threadfence();
+      atomicAdd(x_ctr, 1);
+      const int want = W * nwait;
+      uint32_t spins = 0;
+      while (__hip_atomic_load(x_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+        if (__hip_atomic_load(sy.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+        if (++spins > SEED_SPIN_LIMIT) { atomicExch(sy.abort, 1); break; }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __threadfence();
+    }
+    __syncthreads();
+  };
   int ci = 0;
   for (int s = 0; s < C; ++s) {
     // ---- centre s ----------------------------------------------------------------
@@ -171,6 +251,107 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
       const uint64_t k0 = splitmix64(g.seed, stream) >> 11;
       const uint64_t lo = k0 * (uint64_t)N, hi = __umul64hi(k0, (uint64_t)N);
       ci = (int)((hi << 11) | (lo >> 53));
+    } else if (W > 1) {
+      // ---- the workgroups of the clustering together ----------------------------
+      if (wv == 0) {
+        const int n0 = gi0 * SEED_NW, n1 = gi1 * SEED_NW;
+        double run = 0.0;
+        for (int c0 = n0; c0 < n1; c0 += 64) {
+          const double v = c0 + lane < n1 ? wsum[c0 + lane] : 0.0;
+          run += __shfl(wave_incl_scan(v), 63);
+        }
+        if (lane == 0)
+          __hip_atomic_store(x_part + wg, (unsigned long long)__double_as_longlong(run), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      chain_wait();
+      if (wv == 0) {
+        // every workgroup: the same exact sums in the same order, so the same owner
+        const double v = lane < W ? __longlong_as_double((long long)__hip_atomic_load(
+                                        x_part + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                                  : 0.0;
+        const double inc = wave_incl_scan(v);
+        const double total = __shfl(inc, 63);
+        int mode = 2, owner = 0;
+        double excl = 0.0, target = 0.0;
+        if (total > 0.0) {
+          const uint64_t ku = splitmix64(g.seed, stream + (uint64_t)s) >> 11;
+          target = ((double)ku * 0x1p-53) * total;
+          const uint64_t hit = __ballot(lane < W && inc > target);
+          if (hit) {
+            mode = 0;
+            owner = __ffsll((unsigned long long)hit) - 1;
+            excl = __shfl(inc - v, owner);
+          } else {
+            mode = 1;
+            const uint64_t pos = __ballot(lane < W && v > 0.0);
+            owner = 63 - __clzll((long long)pos);
+          }
+        }
+        int gg = -1, ww = -1;
+        if (mode == 0 && wg == owner) {
+          // the owner walks its (group, wave) sums from the sum before it
+          const int n0 = gi0 * SEED_NW, n1 = gi1 * SEED_NW;
+          double run = excl;
+          for (int c0 = n0; c0 < n1; c0 += 64) {
+            const bool in = c0 + lane < n1;
+            const double u = in ? wsum[c0 + lane] : 0.0;
+            const double ic = wave_incl_scan(u);
+            const uint64_t h = __ballot(in && run + ic > target);
+            if (h) {
+              const int L = __ffsll((unsigned long long)h) - 1;
+              const double prev = __shfl(ic, L > 0 ? L - 1 : 0);
+              excl = run + (L > 0 ? prev : 0.0);
+              gg = (c0 + L) / SEED_NW;
+              ww = (c0 + L) % SEED_NW;
+              break;
+            }
+            run += __shfl(ic, 63);
+          }
+          if (gg < 0) { gg = gi1 - 1; ww = SEED_NW - 1; }   // not reached: the owner's sums cross
+        }
+        if (lane == 0) {
+          sh_grp = gg; sh_wave = ww; sh_excl = excl; sh_target = target;
+          sh_mode = mode; sh_own = owner;
+          sh_lo = 0x7FFFFFFF; sh_hi = -1;
+        }
+      }
+      __syncthreads();
+      const int mode = sh_mode, owner = sh_own;
+      if (mode == 2) {
+        for (int gi = gi0; gi < gi1; ++gi) {
+          const int r0 = gi * SEED_RG;
+          const uint32_t vm = valid_mask(r0);
+          if (!RESIDENT) load_group(r0, vm);
+          uint32_t free_ = 0;
+#pragma unroll
+          for (int k = 0; k < SEED_RG; ++k) free_ |= (uint32_t)!(nr_get(k) & NR_MARK) << k;
+          free_ &= vm;
+          if (free_) { atomicMin(x_lo + s, pidx(r0, __ffs(free_) - 1)); break; }
+        }
+      } else if (wg == owner) {
+        if (mode == 1) {
+          for (int gi = gi1 - 1; gi >= gi0; --gi) {
+            const int r0 = gi * SEED_RG;
+            const uint32_t vm = valid_mask(r0);
+            if (!RESIDENT) load_group(r0, vm);
+            uint32_t posm = 0;
+#pragma unroll
+            for (int k = 0; k < SEED_RG; ++k) posm |= (uint32_t)(gd2[k] > 0.0) << k;
+            posm &= vm;
+            if (posm) { atomicMax(&sh_hi, pidx(r0, 31 - __clz(posm))); break; }
+          }
+        } else if (wv == sh_wave) {
+          cross_wave(sh_grp, sh_wave);
+        }
+        __syncthreads();
+        if (tid == 0)
+          __hip_atomic_store(x_ci, sh_lo != 0x7FFFFFFF ? sh_lo : sh_hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      chain_wait();
+      ci = mode == 2 ? __hip_atomic_load(x_lo + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     : __hip_atomic_load(x_ci, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (ci < 0 || ci >= N) ci = 0;
     } else {
       if (wv == 0) {
         // wave 0 walks the (group, wave) sums in index order
@@ -236,41 +417,14 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
           if (posm) { atomicMax(&sh_hi, pidx(r0, 31 - __clz(posm))); break; }
         }
       } else if (wv == ww) {
-        // the crossing wave: rounds of its group, then lanes of the crossing round
-        const int r0 = gg * SEED_RG;
-        if (RESIDENT) {
-#pragma unroll
-          for (int k = 0; k < SEED_RG; ++k) gscr[k * 64 + lane] = gd2[k];
-        } else {
-          for (int k = 0; k < SEED_RG; ++k) {
-            const int p = pidx(r0, k);
-            gscr[k * 64 + lane] = p < N ? D2g[p] : 0.0;
-          }
-        }
-        wave_sync_lds();
-        double excl = sh_excl;
-        const double target = sh_target;
-        int ksel = -1, klast = -1;
-        for (int k = 0; k < SEED_RG; ++k) {
-          const double rs = wave_sum_dpp(gscr[k * 64 + lane]);
-          if (rs > 0.0) klast = k;
-          if (ksel < 0) { if (excl + rs > target) ksel = k; else excl += rs; }
-        }
-        if (ksel < 0) ksel = klast;   // rounding: the group's last round with weight
-        const double v = gscr[ksel * 64 + lane];
-        const double inc = excl + wave_incl_scan(v);
-        const uint64_t hit = __ballot(inc > target);
-        const uint64_t pos = __ballot(v > 0.0);
-        const int L = hit ? __ffsll((unsigned long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
-        if (lane == 0) sh_lo = r0 * SEED_NT + ww * (SEED_RG * 64) + ksel * 64 + L;
-        wave_sync_lds();
+        cross_wave(gg, ww);
       }
       __syncthreads();
       ci = sh_lo != 0x7FFFFFFF ? sh_lo : sh_hi;
       if (ci < 0 || ci >= N) ci = 0;
     }
     // ---- centre vector, cache row and distances to the previous centres -----------
-    if (tid == 0) { chosen[s] = ci; sd[s] = ci; }
+    if (tid == 0) { chosen[s] = ci; if (wg == 0) sd[s] = ci; }
     if (tid < dm) {
       const T xv = X[(size_t)ci * d + tid];
       cvec[tid] = Elem<T>::ld(&xv);
@@ -289,7 +443,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
     }
     __syncthreads();
     // ---- D^2 update, group by group; (group, wave) sums for the next draw ----------
-    for (int gi = 0; gi < G; ++gi) {
+    for (int gi = gi0; gi < gi1; ++gi) {
       const int r0 = gi * SEED_RG;
       const uint32_t vm = valid_mask(r0);
       if (!RESIDENT) {
@@ -407,7 +561,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
     __syncthreads();
   }
   // ---- initial centroids = the chosen points ----------------------------------------
-  for (int idx = tid; idx < C * dm; idx += SEED_NT) {
+  for (int idx = wg == 0 ? tid : C * dm; idx < C * dm; idx += SEED_NT) {
     const int c = idx / dm, ch = idx % dm;
     const float val = Elem<T>::ldf(X + (size_t)chosen[c] * d + ch);
     if (m == 0) qcent[((size_t)bh * g.Cq + c) * d + ch] = val;
@@ -1586,7 +1740,7 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {
 }
 
 template <typename T>
-static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace& w, hipStream_t s) {
+static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace& w, int32_t* status, hipStream_t s) {
   dim3 grid(g.BH, 4);
   size_t cache = 0;
   for (int m = 0; m < 4; ++m) {
@@ -1634,16 +1788,46 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
     return;
   }
   const size_t lds = (size_t)SEED_NW * SEED_LIST * 12 + cache;
-  auto go = [&](auto kern) {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kern<<<grid, SEED_NT, lds, s>>>(qr, kr, g, w.d2, (uint16_t*)w.nearest, w.seeds, w.qcent, w.kcent);
-  };
-  go(seed_kernel<T, false>);
+  // Several workgroups per clustering when the chip holds them all at once
+  // (a cooperative launch guarantees that, or fails and one is used).
+  const auto kern = seed_kernel<T, false>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const int chains = g.BH * 4;
+  const int G = ((g.N + SEED_NT - 1) / SEED_NT + SEED_RG - 1) / SEED_RG;
+  // bf16 data only: there every sum of D^2 is exact, so splitting the running
+  // sum at workgroup boundaries cannot change a draw
+  int W = 1, dev = 0, ncu = 0, coop = 0, per_cu = 0;
+  if (sizeof(T) == 2 && hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, SEED_NT, lds) == hipSuccess)
+    W = max(1, min(G, ncu * per_cu / chains));
+  seed_sync_init_kernel<<<chains, 256, 0, s>>>(w.seed_sync, chains, status + 2);
+  SeedSync sy;
+  sy.base = w.seed_sync;
+  sy.abort = status + 2;
+  sy.W = W;
+  double* d2 = w.d2;
+  uint16_t* nr = reinterpret_cast<uint16_t*>(w.nearest);
+  int32_t* sd = w.seeds;
+  float* qc = w.qcent;
+  float* kc = w.kcent;
+  if (W > 1) {
+    void* args[] = {(void*)&qr, (void*)&kr, (void*)&g, (void*)&d2, (void*)&nr, (void*)&sd, (void*)&qc, (void*)&kc,
+                    (void*)&sy};
+    if (hipLaunchCooperativeKernel((const void*)kern, dim3(g.BH, 4, W), dim3(SEED_NT), args, (unsigned)lds, s) ==
+        hipSuccess)
+      return;
+    (void)hipGetLastError();
+    sy.W = 1;
+  }
+  kern<<<grid, SEED_NT, lds, s>>>(qr, kr, g, d2, nr, sd, qc, kc, sy);
 }
 
-hipError_t launch_seed(const Geo& g, const void* qr, const void* kr, const Workspace& w, hipStream_t s) {
-  if (g.bf16) seed_launch<uint16_t>(g, (const uint16_t*)qr, (const uint16_t*)kr, w, s);
-  else seed_launch<float>(g, (const float*)qr, (const float*)kr, w, s);
+hipError_t launch_seed(const Geo& g, const void* qr, const void* kr, const Workspace& w, int32_t* status,
+                       hipStream_t s) {
+  if (g.bf16) seed_launch<uint16_t>(g, (const uint16_t*)qr, (const uint16_t*)kr, w, status, s);
+  else seed_launch<float>(g, (const float*)qr, (const float*)kr, w, status, s);
   return hipGetLastError();
 }
 

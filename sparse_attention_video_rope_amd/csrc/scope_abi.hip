@@ -68,6 +68,7 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
   w.csel = (ClusterSel*)take(sizeof(ClusterSel) * BH * g.Cq);
   w.htot = (int64_t*)take(8 * BH);
   w.hist1 = (int32_t*)take(4 * BH * g.Cq * (size_t)SEL_NB);
+  w.seed_sync = (char*)take((size_t)SEED_SYNC_BYTES * BH * 4);
   if (g.permute) {
     const size_t rows = (size_t)(g.bf16 ? 2 : 4) * BH * N * g.d;
     w.qperm = take(rows);
@@ -195,7 +196,7 @@ scope_status scope_plan(const scope_params* p, const void* q, const void* k, voi
     qc = w.qperm;
     kc = w.kperm;
   }
-  if (!(p->flags & SCOPE_USE_INIT_CENTROIDS)) STEP(launch_seed(g, qc, kc, w, stream));
+  if (!(p->flags & SCOPE_USE_INIT_CENTROIDS)) STEP(launch_seed(g, qc, kc, w, plan->status, stream));
   STEP(launch_prep(g, w, stream));
   STEP(launch_assign(g, qc, kc, w, 0, stream));
   for (int it = 1; it <= g.iters; ++it) {

@@ -13,6 +13,9 @@ constexpr int ATT_BM = 128;     // queries per attention work item (4 waves x 32
 constexpr int SEL_NB = 2048;    // histogram bins per level in the selection kernels
 constexpr int SEL_CAP = 2048;   // boundary candidates sorted in LDS
 constexpr int MAX_C = 1024;     // largest Cq / Cm supported
+// per-clustering exchange area of the k-means++ kernel when one clustering
+// spans several workgroups: counter, drawn index, 32 partial sums, MAX_C minima
+constexpr int SEED_SYNC_BYTES = 8 + 8 * 32 + 4 * MAX_C;
 constexpr int MAX_N = 1 << 18;  // largest token count supported (16 groups of 16 rounds of 1024)
 
 // Geometry of the four clusterings of a head: 0 = queries (full d),
@@ -67,6 +70,7 @@ struct Workspace {
   ClusterSel* csel;             // [BH][Cq]
   int64_t* htot;                // [BH] per-head total of r_c, then the head's offset in sel_idx
   int32_t* hist1;               // [BH][Cq][SEL_NB] level-1 key counts of the Top-p pass (reused by the final selection)
+  char* seed_sync;              // [BH][4] k-means++ exchange areas (SEED_SYNC_BYTES) when a clustering spans workgroups
   void* qperm;                  // [BH][N][d] q_rope with reordered channels (SCOPE_PERMUTE_CHANNELS only)
   void* kperm;                  // [BH][N][d] k_rope likewise
   size_t bytes;
@@ -94,7 +98,8 @@ hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const
 hipError_t launch_permute(const Geo& g, const ChanPerm& perm, const void* qr, const void* kr, const Workspace& w,
                           hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
-hipError_t launch_seed(const Geo& g, const void* qr, const void* kr, const Workspace& w, hipStream_t s);
+hipError_t launch_seed(const Geo& g, const void* qr, const void* kr, const Workspace& w, int32_t* status,
+                       hipStream_t s);
 hipError_t launch_prep(const Geo& g, const Workspace& w, hipStream_t s);
 hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Workspace& w, int iter,
                          hipStream_t s);

@@ -123,7 +123,7 @@ def sha(a, dtype):
 def test_counts_relations_every_head(name):
     run = full_run(name)
     w = run.w
-    assert run.status[1] == 0
+    assert run.status[1] == 0 and run.status[2] == 0
     n = np.diff(run.q_off, axis=1)
     assert np.all(n.sum(1) == w.N)
     floor = math.ceil(w.alpha * w.N)

@@ -282,9 +282,10 @@ def test_fixed_topk_only_end_to_end(w):
         say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
 
 
-@pytest.mark.parametrize("grid", [(4, 61, 71), (7, 50, 77)])
+@pytest.mark.parametrize("grid", [(4, 61, 71), (7, 50, 77), (9, 61, 67)])
 def test_kmeanspp_seeds_three_or_more_point_groups(grid):
-    """Seeds only, at 17324 and 26950 tokens (3 and 4 groups of 8192 points)."""
+    """Seeds only, at 17324, 26950 and 36783 tokens (3, 4 and 5 groups of 8192
+    points); from 18433 tokens on, one clustering spans several workgroups."""
     w = workloads.small("seedN", *grid, 64, (16, 24, 24), "bf16", 24, 24, index=109, H=1, iters=0)
     say("seeds", grid, w.N)
     q, k, _ = workloads.generate(w)
@@ -296,3 +297,36 @@ def test_kmeanspp_seeds_three_or_more_point_groups(grid):
     for m, (off, dm) in enumerate(zip(O.subspace_offsets(w.split), w.split)):
         want = O.kmeanspp_seeds(kr[:, off:off + dm], w.Cm, w.kmeans_seed, 0, 1 + m)
         assert g["seeds"][0, 1 + m, :w.Cm].tolist() == list(want), f"subspace {m}"
+
+
+def _seeds_vs_oracle(w, q, k, g):
+    gridt = (w.T, w.Hg, w.Wg)
+    qr = O.round_storage(O.rope_3d(q[0], gridt, w.split, w.rope_base), w.dtype)
+    kr = O.round_storage(O.rope_3d(k[0], gridt, w.split, w.rope_base), w.dtype)
+    assert g["seeds"][0, 0, :w.Cq].tolist() == list(O.kmeanspp_seeds(qr, w.Cq, w.kmeans_seed, 0, 0))
+    for m, (off, dm) in enumerate(zip(O.subspace_offsets(w.split), w.split)):
+        want = O.kmeanspp_seeds(kr[:, off:off + dm], w.Cm, w.kmeans_seed, 0, 1 + m)
+        assert g["seeds"][0, 1 + m, :w.Cm].tolist() == list(want), f"subspace {m}"
+
+
+def test_kmeanspp_seeds_d128_split_over_workgroups():
+    """d = 128 at 36783 tokens (5 groups of 8192 points, one workgroup each)."""
+    w = workloads.small("seedN128", 9, 61, 67, 128, (44, 42, 42), "bf16", 40, 33, index=110, H=1, iters=0)
+    say("seeds d128", w.N)
+    q, k, _ = workloads.generate(w)
+    g = run_gpu(w, inputs=(q, k, k))
+    assert g["status"][2] == 0
+    _seeds_vs_oracle(w, q, k, g)
+
+
+def test_kmeanspp_seeds_all_points_coincide():
+    """Queries all zero (every RoPE'd query is the origin): after the first
+    draw every D^2 is 0 and each later centre is the lowest index not chosen
+    yet, found across the workgroups that share the clustering."""
+    w = workloads.small("seedZ", 9, 61, 67, 64, (16, 24, 24), "bf16", 30, 12, index=111, H=1, iters=0)
+    say("seeds zero", w.N)
+    q, k, _ = workloads.generate(w)
+    q = np.zeros_like(q)
+    g = run_gpu(w, inputs=(q, k, k))
+    assert g["status"][2] == 0
+    _seeds_vs_oracle(w, q, k, g)
