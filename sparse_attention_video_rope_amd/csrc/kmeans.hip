@@ -104,11 +104,12 @@ __device__ __forceinline__ void wave_sync_lds() {
 // (SeedSync::W > 1, a cooperative launch: all of them are resident at once).
 // Each workgroup owns a contiguous run of groups; per draw it publishes the
 // exact sum of its D^2, waits for the others, and the workgroup holding the
-// crossing publishes the drawn index (two waits per draw).
-static_assert(SEED_SYNC_BYTES == 8 + 8 * SEED_MAX_GROUPS + 4 * MAX_C, "exchange area layout");
+// crossing publishes the drawn index, tagged with the draw, which the others
+// poll for.
+static_assert(SEED_SYNC_BYTES == 8 + 2 * 8 * SEED_MAX_GROUPS + 4 * MAX_C, "exchange area layout");
 constexpr uint32_t SEED_SPIN_LIMIT = 1u << 18;   // polls before giving up: well over a second, far above one draw
 struct SeedSync {
-  char* base;        // [BH][4] areas of SEED_SYNC_BYTES: counter, drawn index, part[32], lowest[MAX_C]
+  char* base;        // [BH][4] areas of SEED_SYNC_BYTES: counter, drawn index, part[2][32], lowest[MAX_C]
   int32_t* abort;    // set when a wait ran out (every later wait is then skipped)
   int W;             // workgroups per clustering (1: no exchange)
 };
@@ -116,7 +117,7 @@ struct SeedSync {
 __global__ void seed_sync_init_kernel(char* base, int chains, int32_t* abort) {
   const int c = blockIdx.x;
   int32_t* a = reinterpret_cast<int32_t*>(base + (size_t)c * SEED_SYNC_BYTES);
-  int32_t* lo = reinterpret_cast<int32_t*>(base + (size_t)c * SEED_SYNC_BYTES + 8 + 8 * SEED_MAX_GROUPS);
+  int32_t* lo = reinterpret_cast<int32_t*>(base + (size_t)c * SEED_SYNC_BYTES + 8 + 2 * 8 * SEED_MAX_GROUPS);
   if (threadIdx.x == 0) { a[0] = 0; a[1] = 0; }
   for (int i = threadIdx.x; i < MAX_C; i += blockDim.x) lo[i] = 0x7FFFFFFF;
   if (c == 0 && threadIdx.x == 0) *abort = 0;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
   __shared__ double wsum[SEED_MAX_GROUPS * SEED_NW];
   __shared__ double gscr[SEED_RG * 64];
   __shared__ double sh_excl, sh_target;
-  __shared__ int32_t sh_grp, sh_wave, sh_mode, sh_lo, sh_hi, sh_own;
+  __shared__ int32_t sh_grp, sh_wave, sh_mode, sh_lo, sh_hi, sh_own, sh_ci;
   extern __shared__ __align__(16) unsigned char seed_smem[];
   int32_t* lp = reinterpret_cast<int32_t*>(seed_smem) + (threadIdx.x >> 6) * SEED_LIST;
   double* ldist = reinterpret_cast<double*>(seed_smem + SEED_NW * SEED_LIST * 4) + (threadIdx.x >> 6) * SEED_LIST;
@@ -193,7 +194,9 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
   int32_t* x_ctr = reinterpret_cast<int32_t*>(xs);
   int32_t* x_ci = x_ctr + 1;
   unsigned long long* x_part = reinterpret_cast<unsigned long long*>(xs + 8);
-  int32_t* x_lo = reinterpret_cast<int32_t*>(xs + 8 + 8 * SEED_MAX_GROUPS);
+  // partial sums by draw parity: a workgroup may publish draw s + 1's while a
+  // slower one still reads draw s's (it cannot get two draws ahead)
+  int32_t* x_lo = reinterpret_cast<int32_t*>(xs + 8 + 2 * 8 * SEED_MAX_GROUPS);
   // the crossing wave (ww) of group gg: rounds of its group, then lanes of
   // the crossing round; sh_excl is the sum of D^2 before the wave's points
   auto cross_wave = [&](int gg, int ww) __attribute__((always_inline)) {
@@ -226,12 +229,16 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
     wave_sync_lds();
   };
   int nwait = 0;
-  // every workgroup of the clustering reaches this point (bounded polling)
-  auto chain_wait = [&]() __attribute__((always_inline)) {
+  // every workgroup of the clustering reaches this point (bounded polling).
+  // heavy: a device-wide fence on both sides (data written by any thread);
+  // light: only thread 0's own agent-scope atomic stores are published
+  // (waited for before the counter moves), so no cache write-back is needed.
+  auto chain_wait = [&](bool heavy) __attribute__((always_inline)) {
     __syncthreads();
     ++nwait;
     if (tid == 0) {
-      __threadfence();
+      if (heavy) __threadfence();
+      else __builtin_amdgcn_s_waitcnt(0);
       atomicAdd(x_ctr, 1);
       const int want = W * nwait;
       uint32_t spins = 0;
@@ -240,9 +247,25 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
         if (++spins > SEED_SPIN_LIMIT) { atomicExch(sy.abort, 1); break; }
         __builtin_amdgcn_s_sleep(2);
       }
-      __threadfence();
+      if (heavy) __threadfence();
     }
     __syncthreads();
+  };
+  // the drawn index of draw s, published by its owner as (s << 20) | index
+  auto wait_ci = [&](int s) __attribute__((always_inline)) -> int {
+    if (tid == 0) {
+      uint32_t spins = 0;
+      int v = __hip_atomic_load(x_ci, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      while ((v >> 20) != s) {
+        if (__hip_atomic_load(sy.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+        if (++spins > SEED_SPIN_LIMIT) { atomicExch(sy.abort, 1); break; }
+        __builtin_amdgcn_s_sleep(1);
+        v = __hip_atomic_load(x_ci, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      sh_ci = v & 0xFFFFF;
+    }
+    __syncthreads();
+    return sh_ci;
   };
   int ci = 0;
   for (int s = 0; s < C; ++s) {
@@ -261,14 +284,16 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
           run += __shfl(wave_incl_scan(v), 63);
         }
         if (lane == 0)
-          __hip_atomic_store(x_part + wg, (unsigned long long)__double_as_longlong(run), __ATOMIC_RELAXED,
+          __hip_atomic_store(x_part + (s & 1) * SEED_MAX_GROUPS + wg, (unsigned long long)__double_as_longlong(run),
+                             __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
       }
-      chain_wait();
+      chain_wait(false);
       if (wv == 0) {
         // every workgroup: the same exact sums in the same order, so the same owner
         const double v = lane < W ? __longlong_as_double((long long)__hip_atomic_load(
-                                        x_part + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                                        x_part + (s & 1) * SEED_MAX_GROUPS + lane, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT))
                                   : 0.0;
         const double inc = wave_incl_scan(v);
         const double total = __shfl(inc, 63);
@@ -327,7 +352,11 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
 #pragma unroll
           for (int k = 0; k < SEED_RG; ++k) free_ |= (uint32_t)!(nr_get(k) & NR_MARK) << k;
           free_ &= vm;
-          if (free_) { atomicMin(x_lo + s, pidx(r0, __ffs(free_) - 1)); break; }
+          if (free_) {
+            atomicMin(x_lo + s, pidx(r0, __ffs(free_) - 1));
+            __builtin_amdgcn_s_waitcnt(0);   // performed before the wait below publishes it
+            break;
+          }
         }
       } else if (wg == owner) {
         if (mode == 1) {
@@ -345,12 +374,17 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
           cross_wave(sh_grp, sh_wave);
         }
         __syncthreads();
-        if (tid == 0)
-          __hip_atomic_store(x_ci, sh_lo != 0x7FFFFFFF ? sh_lo : sh_hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
+          const int own = sh_lo != 0x7FFFFFFF ? sh_lo : sh_hi;
+          __hip_atomic_store(x_ci, (s << 20) | (own & 0xFFFFF), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
-      chain_wait();
-      ci = mode == 2 ? __hip_atomic_load(x_lo + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                     : __hip_atomic_load(x_ci, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (mode == 2) {
+        chain_wait(true);
+        ci = __hip_atomic_load(x_lo + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        ci = wait_ci(s);
+      }
       if (ci < 0 || ci >= N) ci = 0;
     } else {
       if (wv == 0) {

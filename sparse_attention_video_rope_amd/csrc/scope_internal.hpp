@@ -14,8 +14,8 @@ constexpr int SEL_NB = 2048;    // histogram bins per level in the selection ker
 constexpr int SEL_CAP = 2048;   // boundary candidates sorted in LDS
 constexpr int MAX_C = 1024;     // largest Cq / Cm supported
 // per-clustering exchange area of the k-means++ kernel when one clustering
-// spans several workgroups: counter, drawn index, 32 partial sums, MAX_C minima
-constexpr int SEED_SYNC_BYTES = 8 + 8 * 32 + 4 * MAX_C;
+// spans several workgroups: counter, drawn index, 2 x 32 partial sums, MAX_C minima
+constexpr int SEED_SYNC_BYTES = 8 + 2 * 8 * 32 + 4 * MAX_C;
 constexpr int MAX_N = 1 << 18;  // largest token count supported (16 groups of 16 rounds of 1024)
 
 // Geometry of the four clusterings of a head: 0 = queries (full d),
