@@ -101,7 +101,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 }
 
 // Exchange area of one clustering when W workgroups share its points
-// (SeedSync::W > 1, a cooperative launch: all of them are resident at once).
+// (SeedSync::Wq or Wk > 1, a cooperative launch: all of them are resident at once).
 // Each workgroup owns a contiguous run of groups; per draw it publishes the
 // exact sum of its D^2, waits for the others, and the workgroup holding the
 // crossing publishes the drawn index, tagged with the draw, which the others
@@ -111,7 +111,9 @@ constexpr uint32_t SEED_SPIN_LIMIT = 1u << 18;   // polls before giving up: well
 struct SeedSync {
   char* base;        // [BH][4] areas of SEED_SYNC_BYTES: counter, drawn index, part[2][32], lowest[MAX_C]
   int32_t* abort;    // set when a wait ran out (every later wait is then skipped)
-  int W;             // workgroups per clustering (1: no exchange)
+  int Wq, Wk;        // workgroups per query / key clustering (1 and 1: no exchange)
+  int flat;          // 1: blockIdx.x enumerates the BH*Wq query workgroups, then the
+                     // 3*BH*Wk key workgroups; 0: grid (BH, 4) with one each
 };
 
 __global__ void seed_sync_init_kernel(char* base, int chains, int32_t* abort) {
@@ -128,7 +130,17 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
                                                        double* __restrict__ d2all, uint16_t* __restrict__ nearall,
                                                        int32_t* __restrict__ seeds, float* __restrict__ qcent,
                                                        float* __restrict__ kcent, SeedSync sy) {
-  const int m = blockIdx.y, bh = blockIdx.x;
+  int m = blockIdx.y, bh = blockIdx.x, wg = 0;
+  if (sy.flat) {
+    const int b = blockIdx.x, nq = g.BH * sy.Wq;
+    if (b < nq) {
+      m = 0; bh = b / sy.Wq; wg = b - bh * sy.Wq;
+    } else {
+      const int c = (b - nq) / sy.Wk;
+      wg = (b - nq) - c * sy.Wk; bh = c / 3; m = 1 + (c - bh * 3);
+    }
+  }
+  const int W = m == 0 ? sy.Wq : sy.Wk;
   const int N = g.N, d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m];
   const T* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + off;
   double* D2g = d2all + ((size_t)bh * 4 + m) * N;
@@ -188,7 +200,6 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
   for (int k = 0; k < SEED_RG; ++k) { gd2[k] = 0.0; nr_set(k, NR_MARK); }
 
   // this workgroup's groups [gi0, gi1) of the clustering
-  const int W = sy.W, wg = blockIdx.z;
   const int gi0 = (int)((int64_t)wg * G / W), gi1 = (int)((int64_t)(wg + 1) * G / W);
   char* xs = sy.base + ((size_t)bh * 4 + m) * SEED_SYNC_BYTES;
   int32_t* x_ctr = reinterpret_cast<int32_t*>(xs);
@@ -1830,31 +1841,40 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
   const int G = ((g.N + SEED_NT - 1) / SEED_NT + SEED_RG - 1) / SEED_RG;
   // bf16 data only: there every sum of D^2 is exact, so splitting the running
   // sum at workgroup boundaries cannot change a draw
-  int W = 1, dev = 0, ncu = 0, coop = 0, per_cu = 0;
+  // The slots left after every clustering has Wk go to the query clusterings
+  // (the widest rows).
+  int Wq = 1, Wk = 1, dev = 0, ncu = 0, coop = 0, per_cu = 0;
   if (sizeof(T) == 2 && hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
       hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, SEED_NT, lds) == hipSuccess)
-    W = max(1, min(G, ncu * per_cu / chains));
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, SEED_NT, lds) == hipSuccess) {
+    const int cap = ncu * per_cu;
+    Wk = max(1, min(G, cap / chains));
+    Wq = max(Wk, min(G, (cap - 3 * g.BH * Wk) / g.BH));
+  }
   seed_sync_init_kernel<<<chains, 256, 0, s>>>(w.seed_sync, chains, status + 2);
   SeedSync sy;
   sy.base = w.seed_sync;
   sy.abort = status + 2;
-  sy.W = W;
+  sy.Wq = Wq;
+  sy.Wk = Wk;
+  sy.flat = 1;
   double* d2 = w.d2;
   uint16_t* nr = reinterpret_cast<uint16_t*>(w.nearest);
   int32_t* sd = w.seeds;
   float* qc = w.qcent;
   float* kc = w.kcent;
-  if (W > 1) {
+  if (Wq > 1 || Wk > 1) {
     void* args[] = {(void*)&qr, (void*)&kr, (void*)&g, (void*)&d2, (void*)&nr, (void*)&sd, (void*)&qc, (void*)&kc,
                     (void*)&sy};
-    if (hipLaunchCooperativeKernel((const void*)kern, dim3(g.BH, 4, W), dim3(SEED_NT), args, (unsigned)lds, s) ==
+    const unsigned nblk = (unsigned)(g.BH * Wq + 3 * g.BH * Wk);
+    if (hipLaunchCooperativeKernel((const void*)kern, dim3(nblk), dim3(SEED_NT), args, (unsigned)lds, s) ==
         hipSuccess)
       return;
     (void)hipGetLastError();
-    sy.W = 1;
   }
+  sy.Wq = sy.Wk = 1;
+  sy.flat = 0;
   kern<<<grid, SEED_NT, lds, s>>>(qr, kr, g, d2, nr, sd, qc, kc, sy);
 }
 
