@@ -1918,16 +1918,37 @@ hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Wor
       pm = max(1, min(pm, (ntiles + 3) / 4));
       split.start[m + 1] = split.start[m] + pm;
     }
-    dim3 grid(split.start[4], 1, g.BH);
-    int kbmax = 1;
-    for (int m = 0; m < 4; ++m) kbmax = max(kbmax, g.dpad[m] / 16);
-    auto go = [&](auto kern) {
-      if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      kern<<<grid, ASG_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, out, split);
+    auto lds_of = [&](int m) { return g.Cpad[m] * (g.dpad[m] + 8) * 2 + g.Cpad[m] * 4 + 4 * 128 * 8; };
+    auto launch = [&](const AsgSplit& sp, int lo_m, int hi_m) {
+      int bytes = 0, kb = 1;
+      for (int m = lo_m; m < hi_m; ++m) { bytes = max(bytes, lds_of(m)); kb = max(kb, g.dpad[m] / 16); }
+      const dim3 grid(sp.start[hi_m] - sp.start[lo_m], 1, g.BH);
+      auto go = [&](auto kern) {
+        if (bytes > 64 * 1024)
+          (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        kern<<<grid, ASG_NT, bytes, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, out, sp);
+      };
+      if (kb <= 2) go(assign2_kernel<2>);
+      else if (kb <= 4) go(assign2_kernel<4>);
+      else go(assign2_kernel<8>);
     };
-    if (kbmax <= 2) go(assign2_kernel<2>);
-    else if (kbmax <= 4) go(assign2_kernel<4>);
-    else go(assign2_kernel<8>);
+    int lds_k = 0;
+    for (int m = 1; m < 4; ++m) lds_k = max(lds_k, lds_of(m));
+    constexpr int kLdsCU = 160 * 1024;   // LDS of one CU
+    if (lds_of(0) > 64 * 1024 && kLdsCU / lds_k > kLdsCU / lds_of(0)) {
+      // The query clustering's centroid table alone limits a CU to one
+      // workgroup: the key clusterings get a launch of their own with their
+      // smaller tables (several workgroups per CU).
+      AsgSplit q = split, k = split;
+      for (int m = 2; m <= 4; ++m) q.start[m] = q.start[1];
+      const int b = split.start[1];
+      k.start[0] = k.start[1] = 0;
+      for (int m = 2; m <= 4; ++m) k.start[m] = split.start[m] - b;
+      launch(q, 0, 1);
+      launch(k, 1, 4);
+    } else {
+      launch(split, 0, 4);
+    }
   } else {
     dim3 grid((g.N + 255) / 256, 4, g.BH);
     assign_exact_f32_kernel<<<grid, 256, 0, s>>>((const float*)qr, (const float*)kr, g, w.qcent, w.kcent, out);

@@ -20,6 +20,9 @@ SMALL = [
     workloads.small("s128h", 3, 11, 17, 128, (16, 56, 56), "bf16", 5, 33, index=103),
     workloads.small("s64f", 3, 6, 7, 64, (16, 24, 24), "f32", 4, 9, index=104),
     workloads.small("s128f", 2, 5, 9, 128, (44, 42, 42), "f32", 3, 7, index=105, H=1),
+    # 300 query clusters at d = 128: the query assignment's centroid table
+    # fills a CU's LDS, so the key clusterings are assigned in a launch of their own
+    workloads.small("s128c", 3, 10, 12, 128, (44, 42, 42), "bf16", 300, 60, index=112),
 ]
 IDS = [w.name for w in SMALL]
 
