@@ -949,11 +949,32 @@ __host__ __device__ inline SeedLLayout seedl_layout(int N, int C, int dm) {
 template <bool VEC>
 __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
                                                       Geo g, double* __restrict__ d2all, int32_t* __restrict__ seeds,
-                                                      float* __restrict__ qcent, float* __restrict__ kcent) {
-  const int m = blockIdx.y, bh = blockIdx.x;
-  const int N = g.N, d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m];
-  const uint16_t* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + off;
-  double* D2g = d2all + ((size_t)bh * 4 + m) * N;
+                                                      float* __restrict__ qcent, float* __restrict__ kcent, SeedSync sy) {
+  int m = blockIdx.y, bh = blockIdx.x, wg = 0;
+  if (sy.flat) {
+    const int b = blockIdx.x, nq = g.BH * sy.Wq;
+    if (b < nq) {
+      m = 0; bh = b / sy.Wq; wg = b - bh * sy.Wq;
+    } else {
+      const int c = (b - nq) / sy.Wk;
+      wg = (b - nq) - c * sy.Wk; bh = c / 3; m = 1 + (c - bh * 3);
+    }
+  }
+  // W workgroups share the clustering: this one owns the points
+  // [pbase, pbase + N) (local indices below; drawn centres are global)
+  const int W = m == 0 ? sy.Wq : sy.Wk;
+  const int Nall = g.N;
+  const int pbase = (int)((int64_t)wg * Nall / W);
+  const int N = (int)((int64_t)(wg + 1) * Nall / W) - pbase;
+  const int d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m];
+  const uint16_t* Xh = (m == 0 ? qr : kr) + (size_t)bh * Nall * d + off;
+  const uint16_t* X = Xh + (size_t)pbase * d;
+  double* D2g = d2all + ((size_t)bh * 4 + m) * Nall + pbase;
+  char* xs = sy.base + ((size_t)bh * 4 + m) * SEED_SYNC_BYTES;
+  int32_t* x_ctr = reinterpret_cast<int32_t*>(xs);
+  int32_t* x_ci = x_ctr + 1;
+  unsigned long long* x_part = reinterpret_cast<unsigned long long*>(xs + 8);
+  int32_t* x_lo = reinterpret_cast<int32_t*>(xs + 8 + 2 * 8 * SEED_MAX_GROUPS);
   int32_t* sd = seeds + ((size_t)bh * 4 + m) * g.Cmax;
   const SeedLLayout L = seedl_layout(N, C, dm);
   extern __shared__ __align__(16) unsigned char seedl_smem[];
@@ -967,7 +988,8 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
   __shared__ double cvec[128];
   __shared__ double dtmp[SL_NT / 64 + 1];
   __shared__ int32_t itmp[SL_NT / 64 + 1];
-  __shared__ int32_t sh_ci, sh_lo, sh_hi;
+  __shared__ int32_t sh_ci, sh_lo, sh_hi, sh_mode, sh_own;
+  __shared__ double sh_pre, sh_tgt, sh_cn;
   const int cld = dm + 2;
   const bool cached = L.cached;
 
@@ -980,6 +1002,29 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
   for (int i = threadIdx.x; i < SL_NT * P; i += SL_NT) { d2s[i] = 0u; nrs[i] = (uint16_t)NR_MARK; }
   tsum[threadIdx.x] = 0.0;
   __syncthreads();
+
+  int nwait = 0;
+  // all W workgroups of the clustering reach this point (bounded polling);
+  // heavy: a device-wide fence on both sides, light: thread 0's own
+  // agent-scope atomic stores only
+  auto chain_wait = [&](bool heavy) __attribute__((always_inline)) {
+    __syncthreads();
+    ++nwait;
+    if (threadIdx.x == 0) {
+      if (heavy) __threadfence();
+      else __builtin_amdgcn_s_waitcnt(0);
+      atomicAdd(x_ctr, 1);
+      const int want = W * nwait;
+      uint32_t spins = 0;
+      while (__hip_atomic_load(x_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+        if (__hip_atomic_load(sy.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+        if (++spins > SEED_SPIN_LIMIT) { atomicExch(sy.abort, 1); break; }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (heavy) __threadfence();
+    }
+    __syncthreads();
+  };
 
   int ci = 0;
   for (int s = 0; s < C; ++s) {
@@ -996,8 +1041,110 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
     // ---- 1. centre s -------------------------------------------------------------
     if (s == 0) {
       const uint64_t k0 = splitmix64(g.seed, stream) >> 11;
-      const uint64_t lo = k0 * (uint64_t)N, hi = __umul64hi(k0, (uint64_t)N);
+      const uint64_t lo = k0 * (uint64_t)Nall, hi = __umul64hi(k0, (uint64_t)Nall);
       ci = (int)((hi << 11) | (lo >> 53));
+    } else if (W > 1) {
+      // ---- the workgroups of the clustering together ------------------------------
+      const double loc = tsum[tid];
+      double total;   // this workgroup's (exact)
+      const double incl = block_incl_scan_dpp<double, SL_NT>(loc, dtmp, &total);
+      if (tid == 0)
+        __hip_atomic_store(x_part + (s & 1) * SEED_MAX_GROUPS + wg, (unsigned long long)__double_as_longlong(total),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      chain_wait(false);
+      if (wv == 0) {
+        // every workgroup: the same exact sums in the same order, so the same owner
+        const double v = lane < W ? __longlong_as_double((long long)__hip_atomic_load(
+                                        x_part + (s & 1) * SEED_MAX_GROUPS + lane, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT))
+                                  : 0.0;
+        const double inc = wave_incl_scan(v);
+        const double gtot = __shfl(inc, 63);
+        int mode = 2, owner = 0;
+        double pre = 0.0, tgt = 0.0;
+        if (gtot > 0.0) {
+          const uint64_t ku = splitmix64(g.seed, stream + (uint64_t)s) >> 11;
+          tgt = ((double)ku * 0x1p-53) * gtot;
+          const uint64_t hit = __ballot(lane < W && inc > tgt);
+          if (hit) {
+            mode = 0;
+            owner = __ffsll((unsigned long long)hit) - 1;
+            pre = __shfl(inc - v, owner);
+          } else {
+            mode = 1;
+            owner = 63 - __clzll((long long)__ballot(lane < W && v > 0.0));
+          }
+        }
+        if (lane == 0) {
+          sh_mode = mode; sh_own = owner; sh_pre = pre; sh_tgt = tgt;
+          sh_ci = -1; sh_lo = 0x7FFFFFFF; sh_hi = -1;
+        }
+      }
+      __syncthreads();
+      const int mode = sh_mode;
+      if (mode == 2) {
+        // every point coincides with a centre: the lowest index not chosen yet
+        int low = 0x7FFFFFFF;
+        for (int k = P - 1; k >= 0; --k) {
+          const int p = p0 + k;
+          if (p < N && !(nrs[k * SL_NT + tid] & NR_MARK)) low = p;
+        }
+        if (low != 0x7FFFFFFF) {
+          atomicMin(x_lo + s, pbase + low);
+          __builtin_amdgcn_s_waitcnt(0);   // performed before the wait below publishes it
+        }
+        chain_wait(true);
+        ci = __hip_atomic_load(x_lo + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        if (wg == sh_own) {
+          const double pre = sh_pre, target = sh_tgt;
+          int lci = -1;
+          if (mode == 0) {
+            const double excl = pre + (incl - loc), inc2 = pre + incl;
+            const uint64_t cross = __ballot(excl <= target && inc2 > target);
+            if (cross) {
+              const int L = __ffsll((unsigned long long)cross) - 1;
+              const double ex = __shfl(excl, L);
+              const int q0 = (wv * 64 + L) * P;
+              const int p = q0 + lane;
+              const double v = (lane < P && p < N) ? D2g[p] : 0.0;
+              const double inc = ex + wave_incl_scan_dpp(v);
+              const uint64_t hit = __ballot(lane < P && p < N && inc > target);
+              const uint64_t pos = __ballot(v > 0.0);
+              const int k = hit ? __ffsll((unsigned long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+              if (lane == 0) sh_ci = q0 + k;
+            }
+            __syncthreads();
+            lci = sh_ci;
+          }
+          if (lci < 0) {
+            // the last point with D^2 > 0 (rounding left the target at the end)
+            int best = -1;
+            for (int k = 0; k < P; ++k) { const int p = p0 + k; if (p < N && D2g[p] > 0.0) best = p; }
+            if (best >= 0) atomicMax(&sh_hi, best);
+            __syncthreads();
+            lci = sh_hi;
+          }
+          if (tid == 0)
+            __hip_atomic_store(x_ci, (s << 20) | ((pbase + max(lci, 0)) & 0xFFFFF), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // the drawn index, published by its owner as (s << 20) | index
+        if (tid == 0) {
+          uint32_t spins = 0;
+          int v = __hip_atomic_load(x_ci, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          while ((v >> 20) != s) {
+            if (__hip_atomic_load(sy.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+            if (++spins > SEED_SPIN_LIMIT) { atomicExch(sy.abort, 1); break; }
+            __builtin_amdgcn_s_sleep(1);
+            v = __hip_atomic_load(x_ci, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          sh_lo = v & 0xFFFFF;
+        }
+        __syncthreads();
+        ci = sh_lo;
+      }
+      if (ci < 0 || ci >= Nall) ci = 0;
     } else {
       const double loc = tsum[tid];
       double total;
@@ -1047,18 +1194,25 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
       if (ci < 0 || ci >= N) ci = 0;
     }
     // ---- 2. centre row ---------------------------------------------------------------
-    if (tid == 0) { chosen[s] = ci; sd[s] = ci; }
+    if (tid == 0) { chosen[s] = ci; if (wg == 0) sd[s] = ci; }
     if (tid < dm) {
-      const uint16_t xv = X[(size_t)ci * d + tid];
+      const uint16_t xv = Xh[(size_t)ci * d + tid];
       cvec[tid] = (double)bf16_to_f32(xv);
       if (cached) cache[(size_t)s * cld + tid] = xv;
     }
     __syncthreads();
+    if (W > 1 && wv == 0) {
+      // squared norm of the centre (for its bf16 norm when it is another workgroup's point)
+      double t = 0.0;
+      for (int ch = lane; ch < dm; ch += 64) t = fma(cvec[ch], cvec[ch], t);
+      t = wave_sum_dpp(t);
+      if (lane == 0) sh_cn = t;
+    }
     // ---- 3. distances to the earlier centres (lanes = channels) -------------------------
     for (int a = wv; a < s; a += SL_NT / 64) {
       double t = 0.0;
       for (int ch = lane; ch < dm; ch += 64) {
-        const double xa = (double)bf16_to_f32(cached ? cache[(size_t)a * cld + ch] : X[(size_t)chosen[a] * d + ch]);
+        const double xa = (double)bf16_to_f32(cached ? cache[(size_t)a * cld + ch] : Xh[(size_t)chosen[a] * d + ch]);
         const double df = xa - cvec[ch];
         t = fma(df, df, t);
       }
@@ -1076,8 +1230,17 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
     //     g > 0 and g^2 >= 1.0001 dv imply ||x - c_s||^2 >= D^2.
     uint32_t need = vmask;
     if (s > 0) {
-      const uint32_t cw = d2s[(ci - (ci / P) * P) * SL_NT + ci / P];
-      const float cb = __uint_as_float(cw << 16);
+      // the centre's bf16 norm: from its slot when the centre is this
+      // workgroup's point, else from its row (any bf16 rounding of the norm
+      // keeps the test's bound)
+      const int lc = ci - pbase;
+      float cb;
+      if (lc >= 0 && lc < N) {
+        const uint32_t cw = d2s[(lc - (lc / P) * P) * SL_NT + lc / P];
+        cb = __uint_as_float(cw << 16);
+      } else {
+        cb = __uint_as_float(bf16_rn_bits(sqrtf((float)sh_cn)) << 16);
+      }
       need = 0;
       for (int k0 = 0; k0 < P; k0 += 8) {
         // eight slots at a time: their LDS reads issue together
@@ -1171,15 +1334,16 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
       }
       __syncthreads();
     }
-    if (tid == 0) {
-      const int t = ci / P, k = ci - t * P;
+    if (tid == 0 && ci - pbase >= 0 && ci - pbase < N) {
+      const int lc = ci - pbase;
+      const int t = lc / P, k = lc - t * P;
       nrs[k * SL_NT + t] |= (uint16_t)NR_MARK;
     }
     __syncthreads();
   }
-  for (int idx = threadIdx.x; idx < C * dm; idx += SL_NT) {
+  for (int idx = wg == 0 ? (int)threadIdx.x : C * dm; idx < C * dm; idx += SL_NT) {
     const int c = idx / dm, ch = idx % dm;
-    const float val = bf16_to_f32(X[(size_t)chosen[c] * d + ch]);
+    const float val = bf16_to_f32(Xh[(size_t)chosen[c] * d + ch]);
     if (m == 0) qcent[((size_t)bh * g.Cq + c) * d + ch] = val;
     else kcent[((size_t)bh * g.Cm + c) * d + off + ch] = val;
   }
@@ -1805,12 +1969,45 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
       for (int m = 0; m < 4; ++m) vec = vec && g.off[m] % 8 == 0 && g.dm[m] % 8 == 0;
       const void* fn = vec ? (const void*)seedl_kernel<true> : (const void*)seedl_kernel<false>;
       (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)need);
+      // Resident slots left over after one workgroup per clustering go to the
+      // query clusterings (the widest rows), at least 4 points per thread each.
+      const int chains = g.BH * 4;
+      const int wmax = max(1, g.N / (4 * SL_NT));
+      int Wq = 1, Wk = 1, dev = 0, ncu = 0, coop = 0, per_cu = 0;
+      if (hipGetDevice(&dev) == hipSuccess &&
+          hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+          hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, SL_NT, need) == hipSuccess) {
+        const int cap = ncu * per_cu;
+        Wk = max(1, min(wmax, cap / chains));
+        Wq = max(Wk, min(wmax, (cap - 3 * g.BH * Wk) / g.BH));
+      }
+      seed_sync_init_kernel<<<chains, 256, 0, s>>>(w.seed_sync, chains, status + 2);
+      SeedSync sy;
+      sy.base = w.seed_sync;
+      sy.abort = status + 2;
+      sy.Wq = Wq;
+      sy.Wk = Wk;
+      sy.flat = 1;
+      const uint16_t* q16 = (const uint16_t*)qr;
+      const uint16_t* k16 = (const uint16_t*)kr;
+      double* d2 = w.d2;
+      int32_t* sd = w.seeds;
+      float* qc = w.qcent;
+      float* kc = w.kcent;
+      if (Wq > 1 || Wk > 1) {
+        void* args[] = {(void*)&q16, (void*)&k16, (void*)&g, (void*)&d2, (void*)&sd, (void*)&qc, (void*)&kc,
+                        (void*)&sy};
+        const unsigned nblk = (unsigned)(g.BH * Wq + 3 * g.BH * Wk);
+        if (hipLaunchCooperativeKernel(fn, dim3(nblk), dim3(SL_NT), args, (unsigned)need, s) == hipSuccess) return;
+        (void)hipGetLastError();
+      }
+      sy.Wq = sy.Wk = 1;
+      sy.flat = 0;
       if (vec)
-        seedl_kernel<true><<<grid, SL_NT, need, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.d2, w.seeds,
-                                                     w.qcent, w.kcent);
+        seedl_kernel<true><<<grid, SL_NT, need, s>>>(q16, k16, g, d2, sd, qc, kc, sy);
       else
-        seedl_kernel<false><<<grid, SL_NT, need, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.d2, w.seeds,
-                                                      w.qcent, w.kcent);
+        seedl_kernel<false><<<grid, SL_NT, need, s>>>(q16, k16, g, d2, sd, qc, kc, sy);
       return;
     }
   }
