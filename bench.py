@@ -464,6 +464,7 @@ def main():
     kh = pl.k_head.cpu().numpy()
     status = pl.status.cpu().numpy()
     assert status[1] == 0, "selected-key capacity overflow"
+    assert status[2] == 0, "k-means++ workgroups stopped waiting on each other"
 
     traffic = None
     if os.path.exists(a.traffic_json):
