@@ -11,7 +11,7 @@ namespace scope {
 
 constexpr int ATT_BM = 128;     // queries per attention work item (4 waves x 32)
 constexpr int SEL_NB = 2048;    // histogram bins per level in the selection kernels
-constexpr int SEL_CAP = 2048;   // boundary candidates sorted in LDS
+constexpr int SEL_CAP = 1024;   // boundary candidates sorted in LDS (more fall back to a walk over distinct logits)
 constexpr int MAX_C = 1024;     // largest Cq / Cm supported
 // per-clustering exchange area of the k-means++ kernel when one clustering
 // spans several workgroups: counter, drawn index, 2 x 32 partial sums, MAX_C minima
