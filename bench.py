@@ -1,6 +1,6 @@
 """Benchmark of the SCOPE hot path (plan + attend) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config cogvideox] [--rho 0.9]
+    python bench.py [--steps K] [--warmup W] [--config hunyuan_720p] [--rho 0.9]
 
 One step = scope_plan (3D RoPE, k-means++ and Lloyd on queries and the three
 key subspaces, LUT, proxy scoring, hybrid Top-p / k_head selection) plus
@@ -42,9 +42,10 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="cogvideox")
+    # the largest workload (HunyuanVideo-like 720p, 129 frames), the setting of the SCOPE abstract's headline
+    ap.add_argument("--config", default="hunyuan_720p")
     ap.add_argument("--rho", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fidelity", action="store_true", help="run the proxy-fidelity sweep instead of the bench")
@@ -133,8 +134,26 @@ def traffic_from(a):
     print(json.dumps(doc))
 
 
-def cpu_baseline(w, rho):
-    """The oracle as it stands on one head of the workload (the same inputs)."""
+def cpu_baseline(w, rho, pairs_head0):
+    """The oracle as it stands, timed stage by stage on head 0 of the workload.
+
+    A whole 720p head takes the oracle over ten minutes, so each stage runs on
+    a bounded sample and its time is scaled to the full head (the stage costs
+    follow the sample sizes linearly):
+      S1   RoPE of Q and K: the whole head;
+      S2a  k-means++: the first SEED_DRAWS draws of each of the four
+           clusterings (every draw is one pass over the N points), x C / draws;
+      S2bc Lloyd: one assignment of LLOYD_PTS points of each clustering,
+           x (N / points) x (iters + 1), and one centroid mean over all N
+           points (seeded labels), x iters;
+      S3-5 lookup tables, Eq. (6) proxy logits and the hybrid selection of
+           SEL_CLUSTERS query clusters, x Cq / clusters;
+      S6   exact attention of ATT_CLUSTERS clusters of N / Cq queries over
+           r keys each, r the head's mean selected-key count, x Cq / clusters.
+    The inputs of S3-S6 (centroids, codes, labels, key sets) only need the
+    right shapes, so they are taken from the head's rows and a seeded
+    generator.  value = 4 d sum_c n_c r_c of head 0 (the GPU plan's selected
+    pairs, the flops the metric counts) / the scaled oracle time."""
     import workloads
     from oracle import scope_oracle as O
     try:
@@ -142,15 +161,60 @@ def cpu_baseline(w, rho):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
+    SEED_DRAWS, LLOYD_PTS, SEL_CLUSTERS, ATT_CLUSTERS = 8, 4096, 8, 4
     q, k, v = workloads.generate(w, [0])
+    q, k, v = q[0], k[0], v[0]
+    N, d, grid = w.N, w.d, (w.T, w.Hg, w.Wg)
+    rng = np.random.default_rng([w.index, 99])
+    st = {}
     t0 = time.perf_counter()
-    r = O.workload_head(w, 0, q[0], k[0], v[0], rho=rho)
-    dt = time.perf_counter() - t0
-    flops = 4.0 * w.d * float(np.sum(r["n"] * r["r"]))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"head 0 of {w.BH} ({w.name}), full pipeline, {dt:.1f} s; effective TFLOP/s "
-                      f"on that head's selected keys",
-            "seconds": dt, "host_cpus": os.cpu_count(),
+    qr = O.round_storage(O.rope_3d(q, grid, w.split, w.rope_base), w.dtype)
+    kr = O.round_storage(O.rope_3d(k, grid, w.split, w.rope_base), w.dtype)
+    st["S1"] = time.perf_counter() - t0
+    offs = O.subspace_offsets(w.split)
+    sets = [(qr, w.Cq)] + [(kr[:, o:o + dm], w.Cm) for o, dm in zip(offs, w.split)]
+    st["S2a"] = st["S2bc"] = 0.0
+    pts = min(N, LLOYD_PTS)
+    for m, (X, C) in enumerate(sets):
+        X = np.ascontiguousarray(X)
+        t0 = time.perf_counter()
+        O.kmeanspp_seeds(X, min(SEED_DRAWS, C), w.kmeans_seed, 0, m)
+        st["S2a"] += (time.perf_counter() - t0) * C / min(SEED_DRAWS, C)
+        M = X[rng.choice(N, C, replace=False)]
+        t0 = time.perf_counter()
+        O.assign(X[:pts], O.round_bf16(M) if w.dtype == "bf16" else M)
+        t1 = time.perf_counter()
+        O.centroid_means(X, rng.integers(0, C, N), M)
+        t2 = time.perf_counter()
+        st["S2bc"] += (t1 - t0) * (w.iters + 1) * N / pts + (t2 - t1) * w.iters
+    qc = qr[rng.choice(N, w.Cq, replace=False)]
+    kc = kr[rng.choice(N, w.Cm, replace=False)]
+    codes = rng.integers(0, w.Cm, (N, 3))
+    n_c = np.bincount(rng.integers(0, w.Cq, N), minlength=w.Cq)
+    nsel = min(SEL_CLUSTERS, w.Cq)
+    t0 = time.perf_counter()
+    P = O.lookup_tables(qc, kc, w.split)
+    s = O.proxy_logits(P[:, :nsel], codes, d)
+    O.hybrid_select(s, n_c[:nsel], rho, w.alpha)
+    st["S3-5"] = (time.perf_counter() - t0) * w.Cq / nsel
+    r_mean = int(round(pairs_head0 / N))
+    na = min(ATT_CLUSTERS, w.Cq)
+    nq = N // w.Cq
+    labels = np.full(N, na, dtype=np.int64)
+    labels[:na * nq] = np.repeat(np.arange(na), nq)
+    sel = [np.sort(rng.choice(N, r_mean, replace=False)) for _ in range(na)]
+    t0 = time.perf_counter()
+    O.sparse_attention(qr, kr, v, labels, sel)
+    st["S6"] = (time.perf_counter() - t0) * w.Cq / na
+    total = sum(st.values())
+    flops = 4.0 * w.d * pairs_head0
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"head 0 of {w.BH} ({w.name}), oracle stages on bounded samples scaled to the head: RoPE "
+                      f"whole; k-means++ {SEED_DRAWS} draws per clustering; Lloyd assignment {pts} points, means all; "
+                      f"LUT + proxy + "
+                      f"selection {nsel} clusters; attention {na} clusters of {nq} queries x {r_mean} keys",
+            "seconds_scaled": {k_: round(v_, 2) for k_, v_ in st.items()}, "seconds_head": round(total, 2),
+            "host_cpus": os.cpu_count(),
             "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
@@ -476,6 +540,7 @@ def main():
         except Exception:
             traffic = None
     achieved = flops / (att_ms * 1e-3) / 1e12
+    stages = stage_breakdown(w, p, sav, pl, qd, kd, vd, qr, kr, out, torch, pairs)
     line = {
         "metric": "SCOPE attention layer latency (ms) + effective TFLOP/s on selected keys, 1 GPU",
         "value": round(flops / (ms * 1e-3) / 1e12, 3),
@@ -488,6 +553,7 @@ def main():
                    "grid": [w.T, w.Hg, w.Wg], "head_dim": w.d, "rope_split": list(w.split), "Cq": w.Cq,
                    "Cm": w.Cm, "lloyd_iters": w.iters, "rho": rho, "alpha": w.alpha},
         "latency_ms": {"step": round(ms, 4), "plan": round(plan_ms, 4), "attend": round(att_ms, 4)},
+        "stages": stages,
         "attend_tflops": round(achieved, 2),
         "density": round(density, 4),
         "k_head": {"min": int(kh.min()), "mean": float(kh.mean()), "max": int(kh.max())},
@@ -499,8 +565,45 @@ def main():
     if a.warm_iters >= 0:
         line["warm_start"] = warm_start(a, w, rho, qd, kd, vd, sav, torch)
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, rho)
+        nh0 = (pl.q_off[1:w.Cq + 1] - pl.q_off[:w.Cq]).double()
+        line["cpu_baseline"] = cpu_baseline(w, rho, float((nh0 * pl.counts_r[:w.Cq].double()).sum()))
     print(json.dumps(line), flush=True)
+
+
+def stage_breakdown(w, p, sav, pl, qd, kd, vd, qr, kr, out, torch, pairs, reps=3):
+    """Per-stage times of the step (medians of `reps` extra plans with stage
+    events, scope_plan_timed, plus the attention launch) and, for the
+    bandwidth-bound stages, GB/s on their algorithmic bytes: S1 reads Q, K and
+    writes Q', K' (8 N d bytes per head in bf16); S4+S5 per head, with the
+    Cq x N fp32 score matrix written once and read once, 6 N bytes of key
+    codes, the three Cq x Cm LUTs and 4 bytes per selected index:
+    8 Cq N + 6 N + 12 Cq Cm + 4 sum_c r_c (this build recomputes the scores
+    from the codes and never stores them, so it moves fewer bytes)."""
+    runs = []
+    for _ in range(reps):
+        ms = sav.plan_timed(p, qd, kd, pl, qr, kr)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sav.attend(p, pl, qr, kr, vd, out)
+        e1.record()
+        e1.synchronize()
+        ms["attend"] = e0.elapsed_time(e1)
+        runs.append(ms)
+    med = {k: float(np.median([r[k] for r in runs])) for k in runs[0]}
+    names = {"rope": "S1_rope", "kmeanspp": "S2a_kmeanspp", "lloyd": "S2bc_lloyd", "perm_lut": "S3_perm_lut",
+             "score_select": "S4S5_score_select", "attend": "S6_attend"}
+    out_ms = {names[k]: round(v, 4) for k, v in med.items()}
+    esz = 2 if w.dtype == "bf16" else 4
+    sum_r = float(pl.counts_r.double().sum())
+    b_rope = 4.0 * esz * w.BH * w.N * w.d
+    b_sel = w.BH * (8.0 * w.Cq * w.N + 6.0 * w.N + 12.0 * w.Cq * w.Cm) + 4.0 * sum_r
+    gbs = lambda b, ms: round(b / (ms * 1e-3) / 1e9, 1)
+    return {"ms": out_ms,
+            "S1_rope": {"bound": "hbm", "bytes": b_rope, "GB/s": gbs(b_rope, med["rope"]),
+                        "frac": round(b_rope / (med["rope"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "S4S5_score_select": {"bound": "hbm", "bytes": b_sel, "GB/s": gbs(b_sel, med["score_select"]),
+                                  "frac": round(b_sel / (med["score_select"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "S6_attend": {"bound": "mfma", "TFLOP/s": round(4.0 * w.d * pairs / (med["attend"] * 1e-3) / 1e12, 2)}}
 
 
 def _attend_sha():

@@ -118,7 +118,13 @@ typedef struct {
                             [2] set if the workgroups that share one k-means++
                             clustering (large N, bf16) stopped waiting on each other
                             (not expected: they are launched cooperatively; the
-                            plan's clusters are then not valid) */
+                            plan's clusters are then not valid),
+                            [3] bf16 runs: set if some element of q_rope / k_rope is
+                            neither 0 nor of magnitude in [2^-47, 2^9); inside that
+                            range the centroid sums of the Lloyd updates are exact
+                            (the centroids are then the exact means rounded once to
+                            fp32, independent of scheduling); outside it they are
+                            ordinary fp64 sums (the plan is still valid) */
   float* q_centroids;    /* [B*H][Cq][d] final query centroids (fp32) */
   float* k_centroids;    /* [B*H][Cm][d] key centroids, row z = (mu^T_z | mu^H_z | mu^W_z) */
   int32_t* q_labels;     /* [B*H][N] query cluster of each token */
@@ -149,6 +155,20 @@ scope_status scope_workspace_size(const scope_params* p, size_t* ws_bytes,
 scope_status scope_plan(const scope_params* p, const void* q, const void* k, void* q_rope,
                         void* k_rope, scope_plan_t* plan, void* ws, size_t ws_bytes,
                         hipStream_t stream);
+
+/* scope_plan, recording stage_events[i] (caller-created HIP events, i <
+ * n_events, 1 <= n_events <= 5) on `stream` right after stage i has been
+ * enqueued: 0 RoPE (S1), 1 k-means++ seeding (S2a), 2 Lloyd assignments and
+ * centroid updates (S2b, S2c), 3 query-cluster permutation and lookup tables
+ * (S3), 4 proxy scoring, Top-p, k_head, final selection and the attention work
+ * list (S4, S5; scoring is fused into the selection passes).  An event
+ * recorded before the call marks the start; elapsed times between the events
+ * are the stage times.  Results are identical to scope_plan's.
+ * SCOPE_ERR_INVALID also for a null event array or event, or n_events out of
+ * range. */
+scope_status scope_plan_timed(const scope_params* p, const void* q, const void* k, void* q_rope,
+                              void* k_rope, scope_plan_t* plan, void* ws, size_t ws_bytes,
+                              const hipEvent_t* stage_events, int n_events, hipStream_t stream);
 
 /* Rebuilds plan->work and plan->status[0] from perm_q/q_off/counts_r/sel_off
  * for a plan whose CSR was written by the caller (for instance copied from

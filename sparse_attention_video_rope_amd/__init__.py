@@ -6,7 +6,8 @@ the HIP library libscope.so behind the C ABI of include/scope.h; this package
 is its Python binding.
 """
 from ._lib import (SCOPE_BF16, SCOPE_F32, SCOPE_FIXED_TOPK_ONLY, SCOPE_PERMUTE_CHANNELS, SCOPE_USE_INIT_CENTROIDS, Params, Plan, ScopeError,
-                   attend, load, make_params, params_for, plan, plan_finalize, sizes)
+                   STAGES, attend, load, make_params, params_for, plan, plan_finalize, plan_timed, sizes)
 
 __all__ = ["SCOPE_BF16", "SCOPE_F32", "SCOPE_FIXED_TOPK_ONLY", "SCOPE_PERMUTE_CHANNELS", "SCOPE_USE_INIT_CENTROIDS", "Params", "Plan",
-           "ScopeError", "attend", "load", "make_params", "params_for", "plan", "plan_finalize", "sizes"]
+           "STAGES", "ScopeError", "attend", "load", "make_params", "params_for", "plan", "plan_finalize", "plan_timed",
+           "sizes"]

@@ -71,6 +71,9 @@ def load():
         lib.scope_workspace_size.restype = c_int32
         lib.scope_plan.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, PL, c_void_p, c_size_t, c_void_p]
         lib.scope_plan.restype = c_int32
+        lib.scope_plan_timed.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, PL, c_void_p, c_size_t,
+                                         ctypes.POINTER(c_void_p), c_int32, c_void_p]
+        lib.scope_plan_timed.restype = c_int32
         lib.scope_plan_finalize.argtypes = [P, PL, c_void_p]
         lib.scope_plan_finalize.restype = c_int32
         lib.scope_attend.argtypes = [P, PL, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
@@ -199,6 +202,30 @@ def plan(p: Params, q, k, pl: Optional[Plan] = None, q_rope=None, k_rope=None):
     if st:
         raise ScopeError(st, "scope_plan")
     return q_rope, k_rope, pl
+
+
+STAGES = ("rope", "kmeanspp", "lloyd", "perm_lut", "score_select")
+
+
+def plan_timed(p: Params, q, k, pl: Plan, q_rope, k_rope):
+    """scope_plan_timed: the same plan, with HIP events after each stage.
+
+    Returns {stage: ms} (synchronises the stream to read the events)."""
+    import torch
+    _check_tensor(q, p, "q")
+    _check_tensor(k, p, "k")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+    for e in ev:
+        e.record()          # creates the HIP event behind each torch event
+    ev[0].record()
+    arr = (c_void_p * len(STAGES))(*[e.cuda_event for e in ev[1:]])
+    st = load().scope_plan_timed(ctypes.byref(p), q.data_ptr(), k.data_ptr(), q_rope.data_ptr(), k_rope.data_ptr(),
+                                 ctypes.byref(pl.struct), pl.workspace.data_ptr(), pl.workspace.numel(), arr,
+                                 len(STAGES), _stream())
+    if st:
+        raise ScopeError(st, "scope_plan_timed")
+    ev[-1].synchronize()
+    return {name: ev[i].elapsed_time(ev[i + 1]) for i, name in enumerate(STAGES)}
 
 
 def plan_finalize(p: Params, pl: Plan):

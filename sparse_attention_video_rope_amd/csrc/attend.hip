@@ -1,6 +1,6 @@
 // Stage 6: exact attention of every query over its cluster's selected keys,
-// with the original post-RoPE keys and values ("sparse attention is then
-// computed over the selected original keys and values", SCOPE abstract):
+// on the post-RoPE keys and original values themselves rather than their
+// proxies (SCOPE abstract):
 //   o_i = sum_{j in S_c(i)} softmax_j(<q'_i, k'_j> / sqrt(d)) v_j.
 //
 // bf16 path (gfx950, wave64): one workgroup of 4 waves per (cluster, 128-query
@@ -27,9 +27,16 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Work item of this workgroup, or -1 (items past the device-side count exit).
+// Workgroups are dispatched to the 8 XCDs round-robin by block index, and
+// each XCD has its own L2.  Block b takes item (b mod 8) * per + b / 8, so
+// every XCD works through one contiguous eighth of the work list in list
+// order: the items of one cluster (adjacent in the list, same key set) run
+// at the same time on one XCD and share its L2 for their K / V gathers.
+// The grid is a multiple of 8 and covers 8 * per (per = ceil(n_work / 8)).
 __device__ __forceinline__ int att_item(int n_work) {
-  const int item = blockIdx.x;
-  return item < n_work ? item : -1;
+  const int b = blockIdx.x, per = (n_work + 7) >> 3;
+  const int item = (b & 7) * per + (b >> 3);
+  return (b >> 3) < per && item < n_work ? item : -1;
 }
 
 struct AttArgs {
@@ -414,7 +421,7 @@ hipError_t launch_attend(const Geo& g, const scope_plan_t& plan, const void* qr,
   a.scale = (float)(1.0 / sqrt((double)g.d));
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   if (plan.work_capacity == 0) return hipSuccess;
-  const unsigned grid = (unsigned)plan.work_capacity;
+  const unsigned grid = (unsigned)((plan.work_capacity + 7) / 8 * 8);
 #define SCOPE_ATT_ARGS \
   a, plan.work, plan.status, plan.perm_q, plan.q_off, plan.counts_r, plan.sel_off, plan.sel_idx, plan.k_norm_max
   if (g.bf16) {

@@ -5,10 +5,15 @@
 // Procedure: seeded k-means++ followed by Lloyd rounds
 //   labels_0 = assign(init); for it in 1..iters: mu = mean(labels); labels = assign(mu).
 //
-// Exactness.  bf16 data makes every k-means++ squared distance and every
-// centroid sum exactly representable in fp64 for data of ordinary range, so
-// the fp64 arithmetic below is order-independent; the MFMA assignment is a
-// filter whose near-ties are re-decided with exact fp64 distances.
+// Reproducibility.  The centroid sums of bf16 data are exact (split by
+// magnitude, see accum_kernel), so the order of their atomics does not matter
+// and each mean is the exact sum / n rounded once.  The k-means++ squared
+// distances and their running sums are ordinary fp64 arithmetic evaluated in
+// a fixed order (no floating-point atomics), so every run gives the same
+// draws; a draw can differ from an index-order scan in exact arithmetic only
+// where the target lies within the sums' rounding error of a running-sum
+// boundary (a near tie).  The MFMA assignment is a filter whose near-ties are
+// re-decided with fp64 distances.
 #include <float.h>
 #include <type_traits>
 
@@ -38,9 +43,8 @@ __device__ __forceinline__ double sqdist_row(const T* __restrict__ x, const doub
 // k-means++ seeding (Arthur and Vassilvitskii 2007): one workgroup of 1024
 // threads per (head, clustering).  Centre 0 = floor(u_0 N); centre s = the
 // smallest i whose running sum of D^2 (index order) exceeds u_s * sum(D^2),
-// D^2 being the squared distance to the nearest centre chosen so far (fp64;
-// exact for bf16 data of ordinary range, so the summation order is
-// immaterial there).
+// D^2 being the squared distance to the nearest centre chosen so far (fp64,
+// summed in a fixed order).
 // The points form groups of 8192; inside a group, wave w owns the 512
 // consecutive points starting at 512 w, one 64-point round per step of its
 // 8 rounds (lane = point mod 64).  So (group, wave, round, lane) is the index
@@ -103,7 +107,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 // Exchange area of one clustering when W workgroups share its points
 // (SeedSync::Wq or Wk > 1, a cooperative launch: all of them are resident at once).
 // Each workgroup owns a contiguous run of groups; per draw it publishes the
-// exact sum of its D^2, waits for the others, and the workgroup holding the
+// sum of its D^2, waits for the others, and the workgroup holding the
 // crossing publishes the drawn index, tagged with the draw, which the others
 // poll for.
 static_assert(SEED_SYNC_BYTES == 8 + 2 * 8 * SEED_MAX_GROUPS + 4 * MAX_C, "exchange area layout");
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
       }
       chain_wait(false);
       if (wv == 0) {
-        // every workgroup: the same exact sums in the same order, so the same owner
+        // every workgroup: the same sums in the same order, so the same owner
         const double v = lane < W ? __longlong_as_double((long long)__hip_atomic_load(
                                         x_part + (s & 1) * SEED_MAX_GROUPS + lane, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT))
@@ -864,20 +868,20 @@ __global__ __launch_bounds__(SR_NT) void seedr_kernel(const T* __restrict__ qr, 
 // ---------------------------------------------------------------------------
 // k-means++ seeding for bf16 data with the point state in LDS (1024 threads).
 // Same draw rule as seed_kernel.  Thread t owns the P consecutive points
-// t P .. t P + P - 1 ((thread, slot) is the index order).  The exact fp64 D^2
-// of every point lives in global memory; LDS holds, per point, one 32-bit word
+// t P .. t P + P - 1 ((thread, slot) is the index order).  The fp64 D^2 of
+// every point lives in global memory; LDS holds, per point, one 32-bit word
 // with D^2 rounded up to bf16 (high half) and ||x|| rounded to bf16 (low half)
-// for the pruning tests, the 16-bit nearest centre ids, and each thread's exact
+// for the pruning tests, the 16-bit nearest centre ids, and each thread's fp64
 // D^2 sum.  Per draw: a block scan of the per-thread sums finds the crossing
-// thread, which reads its exact values to find the point; the centre's
+// thread, which reads its fp64 values to find the point; the centre's
 // distances to the earlier centres are computed by all waves; the points that
 // neither the Elkan test (||c_s - a||^2 >= 4 D^2, a the nearest centre) nor the
 // norm test ((||x|| - ||c_s||)^2 >= D^2) rules out are listed in index order (a
-// scan of per-thread counts) and all threads compute their exact distances;
-// the thread that computes a distance applies it: it replaces the exact D^2
-// (global) when smaller, refreshes the LDS copies and adds the exact
-// difference to the owner's sum (fp64 LDS atomics; sums of bf16-derived D^2
-// are exact, so their order does not matter).
+// scan of per-thread counts) and all threads compute their fp64 distances;
+// the thread that computes a distance applies it: it replaces the fp64 D^2
+// (global) when smaller, refreshes the LDS copies and flags the owner, which
+// then sums its P values afresh in slot order (no floating-point atomics, so
+// the sums do not depend on timing).
 // ---------------------------------------------------------------------------
 constexpr int SL_NT = 1024;
 
@@ -922,7 +926,7 @@ constexpr int SL_U = 8;          // rows in flight per lane group in the distanc
 constexpr int SL_LDS_LIMIT = 160 * 1024;
 
 struct SeedLLayout {
-  size_t d2s, nrs, list, tsum, cc, chosen, cache, bytes;
+  size_t d2s, nrs, list, tsum, tflag, cc, chosen, cache, bytes;
   bool cached;
 };
 __host__ __device__ inline SeedLLayout seedl_layout(int N, int C, int dm) {
@@ -934,6 +938,7 @@ __host__ __device__ inline SeedLLayout seedl_layout(int N, int C, int dm) {
   L.nrs = take((size_t)2 * SL_NT * P);
   L.list = take((size_t)4 * (SL_LIST + 1));
   L.tsum = take((size_t)8 * SL_NT);
+  L.tflag = take((size_t)SL_NT);
   L.cc = take((size_t)8 * C);
   L.chosen = take((size_t)4 * C);
   const size_t base = o;
@@ -982,6 +987,7 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
   uint16_t* nrs = reinterpret_cast<uint16_t*>(seedl_smem + L.nrs);     // [P][NT]
   int32_t* list = reinterpret_cast<int32_t*>(seedl_smem + L.list);     // [SL_LIST + 1]
   double* tsum = reinterpret_cast<double*>(seedl_smem + L.tsum);       // [NT]
+  uint8_t* tflag = reinterpret_cast<uint8_t*>(seedl_smem + L.tflag);   // [NT] a point of the thread changed
   double* cc = reinterpret_cast<double*>(seedl_smem + L.cc);           // [C]
   int32_t* chosen = reinterpret_cast<int32_t*>(seedl_smem + L.chosen); // [C]
   uint16_t* cache = reinterpret_cast<uint16_t*>(seedl_smem + L.cache); // [C][cld]
@@ -1001,6 +1007,7 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
 
   for (int i = threadIdx.x; i < SL_NT * P; i += SL_NT) { d2s[i] = 0u; nrs[i] = (uint16_t)NR_MARK; }
   tsum[threadIdx.x] = 0.0;
+  tflag[threadIdx.x] = 0;
   __syncthreads();
 
   int nwait = 0;
@@ -1046,14 +1053,14 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
     } else if (W > 1) {
       // ---- the workgroups of the clustering together ------------------------------
       const double loc = tsum[tid];
-      double total;   // this workgroup's (exact)
+      double total;   // this workgroup's
       const double incl = block_incl_scan_dpp<double, SL_NT>(loc, dtmp, &total);
       if (tid == 0)
         __hip_atomic_store(x_part + (s & 1) * SEED_MAX_GROUPS + wg, (unsigned long long)__double_as_longlong(total),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       chain_wait(false);
       if (wv == 0) {
-        // every workgroup: the same exact sums in the same order, so the same owner
+        // every workgroup: the same sums in the same order, so the same owner
         const double v = lane < W ? __longlong_as_double((long long)__hip_atomic_load(
                                         x_part + (s & 1) * SEED_MAX_GROUPS + lane, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT))
@@ -1155,7 +1162,7 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
       __syncthreads();
       if (total > 0.0) {
         const double excl = incl - loc;
-        // the crossing thread's wave reads its P exact values (one per lane) and scans them
+        // the crossing thread's wave reads its P fp64 values (one per lane) and scans them
         const uint64_t cross = __ballot(excl <= target && incl > target);
         if (cross) {
           const int L = __ffsll((unsigned long long)cross) - 1;
@@ -1327,12 +1334,21 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
               D2g[p] = dist;
               d2s[li] = (bf16_up_bits(dist) << 16) | (s == 0 ? bf16_rn_bits(xn) : (d2s[li] & 0xFFFFu));
               nrs[li] = s == 0 ? (uint16_t)0 : (uint16_t)(s | (nrs[li] & NR_MARK));
-              atomicAdd(&tsum[t], dist - old[u]);
+              tflag[t] = 1;
             }
           }
         }
       }
       __syncthreads();
+    }
+    // the D^2 sum of each thread whose points changed, afresh in slot order
+    // (a fixed order, so the sums, and with them every draw, are the same on
+    // every run)
+    if (tflag[tid]) {
+      double acc = 0.0;
+      for (int k = 0; k < nk; ++k) acc += D2g[p0 + k];
+      tsum[tid] = acc;
+      tflag[tid] = 0;
     }
     if (tid == 0 && ci - pbase >= 0 && ci - pbase < N) {
       const int lc = ci - pbase;
@@ -1487,16 +1503,29 @@ __global__ __launch_bounds__(1024) void sort_kernel(Geo g, const int32_t* __rest
 //  finalize_kernel: one wave per centroid adds the partials in a fixed order,
 //    divides by the count, rounds to fp32 (an empty cluster keeps its
 //    centroid), and refreshes the bf16 copy and its squared norm.
-// bf16 values are exactly representable in fp64 and their sums over at most
-// 2^18 points stay exact for data of ordinary range, so the LDS atomic order
-// does not change the result: the mean equals exact sum / n rounded once.
+// For bf16 data the sums are exact (split by magnitude, below), so the LDS
+// atomic order does not change the result: the mean equals exact sum / n
+// rounded once.  fp32 data is summed in rounded fp64 (no delta updates).
 // ---------------------------------------------------------------------------
 constexpr int ACC_NT = 512;
+
+// Centroid sums of bf16 data are kept in two parts, split by magnitude at
+// 2^-19.  A bf16 value of magnitude >= 2^-19 is a multiple of 2^-26, so while
+// every |x| < 2^9 and N <= 2^18 any sum of such values is below 2^27, a
+// multiple of 2^-26, and exact in fp64 (53 bits).  The smaller nonzero values
+// (rare: about 1.6e-6 of unit-variance data) are added with fp64 atomics to a
+// global table; each is a multiple of 2^-54 when |x| >= 2^-47, and their sums
+// stay below 2^-1, so these sums are exact as well.  Both parts are therefore
+// independent of the order of the atomics, and big + small, rounded once, is
+// the correctly rounded exact sum.  The RoPE kernel flags data outside
+// {0} u [2^-47, 2^9) (plan status[3]).
+__device__ __forceinline__ bool is_small_value(float v) { return v != 0.f && fabsf(v) < 0x1p-19f; }
 
 template <typename T, int SW>
 __global__ __launch_bounds__(ACC_NT) void accum_kernel(const T* __restrict__ qr, const T* __restrict__ kr, Geo g,
                                                        const int32_t* __restrict__ labels, double* __restrict__ psum,
-                                                       int32_t* __restrict__ pcnt, int nslices, int parts) {
+                                                       int32_t* __restrict__ pcnt, int nslices, int parts,
+                                                       double* __restrict__ ssm) {
   const int part = blockIdx.x, bh = blockIdx.z;
   // blockIdx.y enumerates the (clustering, slice) pairs
   int m = 0, sl = blockIdx.y;
@@ -1543,8 +1572,12 @@ __global__ __launch_bounds__(ACC_NT) void accum_kernel(const T* __restrict__ qr,
     for (int k = 0; k < ST; ++k) {
       const int q = k + sub * ST;
       const int lk = __shfl(L, q, 64);
+      const bool in = chv && q < np;
+      // bf16: values below the split go to the global small-value sums (rare)
+      const bool sm = sizeof(T) == 2 && in && is_small_value(v[k]);
       // lanes without a point add -0.0, which leaves every sum unchanged
-      atomicAdd(&S[lk * SW + ch], (chv && q < np) ? (double)v[k] : -0.0);
+      atomicAdd(&S[lk * SW + ch], (in && !sm) ? (double)v[k] : -0.0);
+      if (sm) atomicAdd(&ssm[(((size_t)bh * 4 + m) * g.Cmax + lk) * d + s0 + ch], (double)v[k]);
     }
   }
   __syncthreads();
@@ -1571,7 +1604,7 @@ __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ labels,
                                                              const int32_t* __restrict__ prev,
                                                              double* __restrict__ stot, int32_t* __restrict__ ntot,
-                                                             int parts) {
+                                                             int parts, double* __restrict__ ssm) {
   const int part = blockIdx.x, bh = blockIdx.z;
   int m = 0, sl = blockIdx.y;
   while (m < 3 && sl >= (g.dm[m] + SW - 1) / SW) { sl -= (g.dm[m] + SW - 1) / SW; ++m; }
@@ -1626,8 +1659,14 @@ __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __r
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (vv[u] && chv) {
-          atomicAdd(&S[ln[u] * SW + ch], (double)xv[u]);
-          atomicAdd(&S[lo[u] * SW + ch], -(double)xv[u]);
+          if (!is_small_value(xv[u])) {
+            atomicAdd(&S[ln[u] * SW + ch], (double)xv[u]);
+            atomicAdd(&S[lo[u] * SW + ch], -(double)xv[u]);
+          } else {
+            double* sr = ssm + ((size_t)bh * 4 + m) * g.Cmax * d + s0 + ch;
+            atomicAdd(&sr[(size_t)ln[u] * d], (double)xv[u]);
+            atomicAdd(&sr[(size_t)lo[u] * d], -(double)xv[u]);
+          }
         }
         if (vv[u] && sl == 0 && ch == 0) {
           atomicAdd(&cnt[ln[u]], 1);
@@ -1656,6 +1695,7 @@ __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __r
 __global__ __launch_bounds__(256) void finalize_kernel(Geo g, const double* __restrict__ psum,
                                                        const int32_t* __restrict__ pcnt, int SW, int nslices,
                                                        int parts, int delta, double* __restrict__ stot,
+                                                       const double* __restrict__ ssm,
                                                        int32_t* __restrict__ ntot, float* __restrict__ qcent,
                                                        float* __restrict__ kcent, uint16_t* __restrict__ cbf,
                                                        float* __restrict__ cnorm) {
@@ -1685,7 +1725,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(Geo g, const double* __re
       for (int q = 0; q < parts; ++q) sum += ps[(size_t)q * g.Cmax * SW];
       st[ch] = sum;
     }
-    if (n > 0) row[ch] = (float)(sum / (double)n);
+    // big + small part: one rounding of the exact sum (bf16; ssm is zero for fp32)
+    if (n > 0) row[ch] = (float)((sum + ssm[(((size_t)bh * 4 + m) * g.Cmax + c) * d + ch]) / (double)n);
   }
   if (lane == 0 && !delta) *nt = n;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1741,7 +1782,7 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
 // <= 2^-23 (M^2 + 2 |x| M); the packed bits move a value v by < 2^-19 |v|.
 // EPS covers twice the first two; the packing is charged on the two values
 // compared.  A point whose best two candidates lie within that window is
-// re-decided with exact fp64 distances (ties to the lowest index), so the
+// re-decided with fp64 distances (ties to the lowest index), so the
 // labels equal the fp64 argmin.
 // ---------------------------------------------------------------------------
 constexpr int ASG_NT = 256;
@@ -2036,8 +2077,9 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int chains = g.BH * 4;
   const int G = ((g.N + SEED_NT - 1) / SEED_NT + SEED_RG - 1) / SEED_RG;
-  // bf16 data only: there every sum of D^2 is exact, so splitting the running
-  // sum at workgroup boundaries cannot change a draw
+  // bf16 data only (fp32 data keeps one workgroup per clustering): the running
+  // sum then adds the workgroups' partial sums in range order, a fixed order,
+  // so the draws are reproducible; only the rounding of the sums changes
   // The slots left after every clustering has Wk go to the query clusterings
   // (the widest rows).
   int Wq = 1, Wk = 1, dev = 0, ncu = 0, coop = 0, per_cu = 0;
@@ -2167,15 +2209,20 @@ hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Wor
   dim3 grid(parts, ypairs, g.BH);
   auto go = [&](auto kern, const auto* q, const auto* k) {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kern<<<grid, ACC_NT, lds, s>>>(q, k, g, cur, w.psum, w.pcnt, ns, parts);
+    kern<<<grid, ACC_NT, lds, s>>>(q, k, g, cur, w.psum, w.pcnt, ns, parts, w.ssm);
   };
   auto god = [&](auto kern) {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     kern<<<grid, ACC_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, cur, labels_of(g, w, it - 2), w.stot,
-                                  w.ntot, parts);
+                                  w.ntot, parts, w.ssm);
   };
   const uint16_t *qb = (const uint16_t*)qr, *kb = (const uint16_t*)kr;
   const float *qf = (const float*)qr, *kf = (const float*)kr;
+  if (it == 1) {
+    // small-value sums start at zero (a fill kernel: no memset node in a captured graph)
+    const hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(w.ssm), 0, ssm_elems(g) * 2, s);
+    if (e != hipSuccess) return e;
+  }
   if (delta) {
     if (SW == 32) god(accum_delta_kernel<32>); else god(accum_delta_kernel<16>);
   } else if (g.bf16) {
@@ -2184,7 +2231,7 @@ hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Wor
     if (SW == 32) go(accum_kernel<float, 32>, qf, kf); else go(accum_kernel<float, 16>, qf, kf);
   }
   finalize_kernel<<<dim3((g.Cmax + 3) / 4, 4, g.BH), 256, 0, s>>>(g, w.psum, w.pcnt, SW, ns, parts, delta ? 1 : 0,
-                                                                  w.stot, w.ntot, w.qcent, w.kcent, w.cbf, w.cnorm);
+                                                                  w.stot, w.ssm, w.ntot, w.qcent, w.kcent, w.cbf, w.cnorm);
   return hipGetLastError();
 }
 

@@ -19,8 +19,9 @@ struct RopeArgs {
 };
 
 __global__ void rope_table_kernel(double2* tab, int n0, int n1, int n2, int dm0, int dm1, int dm2,
-                                  double base) {
+                                  double base, int32_t* range_flag) {
   int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx == 0) *range_flag = 0;   // set again below by rope_kernel if needed
   if (idx >= n0 + n1 + n2) return;
   int r = idx, dm = dm0;
   if (r >= n0) { r -= n0; dm = dm1; if (r >= n1) { r -= n1; dm = dm2; } }
@@ -87,7 +88,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    T* __restrict__ qo, T* __restrict__ ko,
                                                    const double2* __restrict__ tab, RopeArgs a,
-                                                   uint32_t* __restrict__ knm) {
+                                                   uint32_t* __restrict__ knm, int32_t* __restrict__ range_flag) {
   __shared__ float red[256 / 64];
   const int cshift = a.d == 128 ? 4 : 3;
   const int sel = blockIdx.z, bh = blockIdx.y;
@@ -141,6 +142,17 @@ __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, cons
     }
     store_rounded(x[kk], y);
     if (valid) x[kk].store((sel ? ko : qo) + base[kk]);
+    if constexpr (sizeof(T) == 2) {
+      // exact-sum range of the clustering: every stored value 0 or of
+      // magnitude in [2^-47, 2^9) (bf16 bit patterns 0x2800 .. 0x43FF)
+      bool out = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t mag = (uint32_t)x[kk].v[i] & 0x7FFFu;
+        out |= valid && mag != 0u && (mag < 0x2800u || mag >= 0x4400u);
+      }
+      if (__ballot(out) && (threadIdx.x & 63) == 0) atomicOr(range_flag, 1);
+    }
     if (sel && knm) {
       // squared norm of the token: its d/8 threads are consecutive lanes
       float ss = 0.f;
@@ -157,10 +169,10 @@ __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, cons
 }
 
 hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const void* k, void* qo,
-                       void* ko, const Workspace& w, float* k_norm_max, hipStream_t s) {
+                       void* ko, const Workspace& w, float* k_norm_max, int32_t* range_flag, hipStream_t s) {
   const int n0 = g.T * g.dm[1] / 2, n1 = g.Hg * g.dm[2] / 2, n2 = g.Wg * g.dm[3] / 2;
   rope_table_kernel<<<(n0 + n1 + n2 + 255) / 256, 256, 0, s>>>(w.rope_tab, n0, n1, n2, g.dm[1], g.dm[2],
-                                                               g.dm[3], p.rope_base);
+                                                               g.dm[3], p.rope_base, range_flag);
   RopeArgs a;
   a.BH = g.BH; a.N = g.N; a.d = g.d; a.Hg = g.Hg; a.Wg = g.Wg;
   a.off1 = g.off[2]; a.off2 = g.off[3];
@@ -178,10 +190,10 @@ hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const
   }
   if (g.bf16)
     rope_kernel<uint16_t><<<blocks, 256, 0, s>>>((const uint16_t*)q, (const uint16_t*)k, (uint16_t*)qo,
-                                                 (uint16_t*)ko, w.rope_tab, a, knm);
+                                                 (uint16_t*)ko, w.rope_tab, a, knm, range_flag);
   else
     rope_kernel<float><<<blocks, 256, 0, s>>>((const float*)q, (const float*)k, (float*)qo, (float*)ko,
-                                              w.rope_tab, a, knm);
+                                              w.rope_tab, a, knm, range_flag);
   return hipGetLastError();
 }
 

@@ -61,6 +61,7 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
   w.psum = (double*)take(8 * BH * 4 * (size_t)acc_slices(g) * acc_parts(g) * g.Cmax * acc_sw(g));
   w.pcnt = (int32_t*)take(4 * BH * 4 * (size_t)acc_parts(g) * g.Cmax);
   w.stot = (double*)take(8 * BH * 4 * (size_t)g.Cmax * g.d);
+  w.ssm = (double*)take(8 * ssm_elems(g));
   w.ntot = (int32_t*)take(4 * BH * 4 * (size_t)g.Cmax);
   w.codes = (uint16_t*)take(8 * BH * N);
   w.qlab = (int32_t*)take(4 * BH * N);
@@ -164,8 +165,16 @@ scope_status scope_workspace_size(const scope_params* p, size_t* ws_bytes, int64
   return SCOPE_OK;
 }
 
-scope_status scope_plan(const scope_params* p, const void* q, const void* k, void* q_rope, void* k_rope,
-                        scope_plan_t* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace scope {
+
+// scope_plan with optional stage events: ev[i] (if ev and i < nev) is
+// recorded on the stream after stage i: 0 RoPE, 1 k-means++, 2 Lloyd,
+// 3 cluster permutation + LUT, 4 scoring + selection + work list.
+static scope_status plan_impl(const scope_params* p, const void* q, const void* k, void* q_rope, void* k_rope,
+                              scope_plan_t* plan, void* ws, size_t ws_bytes, const hipEvent_t* ev, int nev,
+                              hipStream_t stream) {
   scope_status st = validate(p);
   if (st != SCOPE_OK) return st;
   st = check_plan_core(plan);
@@ -183,9 +192,14 @@ scope_status scope_plan(const scope_params* p, const void* q, const void* k, voi
   const Workspace w = carve(g, plan, (char*)ws);
   if (ws_bytes < w.bytes) return SCOPE_ERR_WORKSPACE;
 
+  if (ev && nev > 0)
+    for (int i = 0; i < nev && i < 5; ++i)
+      if (!ev[i]) return SCOPE_ERR_INVALID;
   hipError_t e = hipSuccess;
 #define STEP(x) do { e = (x); if (e != hipSuccess) return hip_status(e); } while (0)
-  STEP(launch_rope(g, *p, q, k, q_rope, k_rope, w, plan->k_norm_max, stream));
+  auto mark = [&](int i) -> hipError_t { return (ev && i < nev) ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  STEP(launch_rope(g, *p, q, k, q_rope, k_rope, w, plan->k_norm_max, plan->status + 3, stream));
+  STEP(mark(0));
   // the clustering reads the rows in proxy channel order
   const void* qc = q_rope;
   const void* kc = k_rope;
@@ -197,21 +211,41 @@ scope_status scope_plan(const scope_params* p, const void* q, const void* k, voi
     kc = w.kperm;
   }
   if (!(p->flags & SCOPE_USE_INIT_CENTROIDS)) STEP(launch_seed(g, qc, kc, w, plan->status, stream));
+  STEP(mark(1));
   STEP(launch_prep(g, w, stream));
   STEP(launch_assign(g, qc, kc, w, 0, stream));
   for (int it = 1; it <= g.iters; ++it) {
     STEP(launch_update(g, qc, kc, w, it, stream));
     STEP(launch_assign(g, qc, kc, w, it, stream));
   }
+  STEP(mark(2));
   STEP(launch_pack(g, w, plan->q_labels, stream));
   STEP(launch_perm(g, w, plan->perm_q, plan->q_off, stream));
   STEP(launch_lut(g, w, stream));
+  STEP(mark(3));
   STEP(launch_topp(g, *p, w, plan->counts_t, plan->counts_b, stream));
   STEP(launch_khead(g, *plan, w, stream));
   STEP(launch_final_select(g, *p, w, *plan, stream));
   STEP(launch_worklist(g, *plan, stream));
+  STEP(mark(4));
 #undef STEP
   return SCOPE_OK;
+}
+
+}  // namespace scope
+
+extern "C" {
+
+scope_status scope_plan(const scope_params* p, const void* q, const void* k, void* q_rope, void* k_rope,
+                        scope_plan_t* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return plan_impl(p, q, k, q_rope, k_rope, plan, ws, ws_bytes, nullptr, 0, stream);
+}
+
+scope_status scope_plan_timed(const scope_params* p, const void* q, const void* k, void* q_rope, void* k_rope,
+                              scope_plan_t* plan, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
+                              int n_events, hipStream_t stream) {
+  if (!stage_events || n_events < 1 || n_events > 5) return SCOPE_ERR_INVALID;
+  return plan_impl(p, q, k, q_rope, k_rope, plan, ws, ws_bytes, stage_events, n_events, stream);
 }
 
 scope_status scope_plan_finalize(const scope_params* p, scope_plan_t* plan, hipStream_t stream) {

@@ -62,7 +62,8 @@ struct Workspace {
   int32_t* labels_alt;          // [BH][4][N] (assignments alternate between the two arrays)
   double* psum;                 // [BH][4][acc_slices][acc_parts][Cmax][acc_sw] partial centroid sums
   int32_t* pcnt;                // [BH][4][acc_parts][Cmax] partial cluster sizes
-  double* stot;                 // [BH][4][Cmax][d] exact per-cluster sums of the last update
+  double* stot;                 // [BH][4][Cmax][d] per-cluster sums of the values of magnitude >= 2^-19
+  double* ssm;                  // [BH][4][Cmax][d] per-cluster sums of the smaller nonzero values (bf16 data)
   int32_t* ntot;                // [BH][4][Cmax] cluster sizes of the last update
   uint16_t* codes;              // [BH][N][4]
   int32_t* qlab;                // [BH][N] (final query labels)
@@ -88,13 +89,16 @@ inline int acc_parts(const Geo& g) {
   return p < 1 ? 1 : (p > 8 ? 8 : p);
 }
 
+// Elements of the small-value centroid sums (Workspace::ssm).
+inline size_t ssm_elems(const Geo& g) { return (size_t)g.BH * 4 * g.Cmax * g.d; }
+
 Geo make_geo(const scope_params& p);
 // Lays the workspace out from `base` (nullptr: only computes .bytes).
 Workspace carve(const Geo& g, const scope_plan_t* plan, char* base);
 
 // ---- launchers (return hipGetLastError()) ---------------------------------
 hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const void* k, void* qo,
-                       void* ko, const Workspace& w, float* k_norm_max, hipStream_t s);
+                       void* ko, const Workspace& w, float* k_norm_max, int32_t* range_flag, hipStream_t s);
 hipError_t launch_permute(const Geo& g, const ChanPerm& perm, const void* qr, const void* kr, const Workspace& w,
                           hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);

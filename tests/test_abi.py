@@ -22,7 +22,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = sav.load()
     names = declared_symbols()
-    assert names == ["scope_attend", "scope_plan", "scope_plan_finalize", "scope_status_string",
+    assert names == ["scope_attend", "scope_plan", "scope_plan_finalize", "scope_plan_timed", "scope_status_string",
                      "scope_workspace_size"]
     for n in names:
         assert hasattr(lib, n), n
@@ -149,3 +149,25 @@ def test_plan_rejects_misaligned_and_small_workspace():
     plan.work_capacity = work
     st = lib.scope_plan(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(plan), fake, 1 << 40, None)
     assert st == 1                      # init centroids requested but not given
+
+
+def test_plan_timed_rejects_bad_event_arrays_before_launch():
+    lib = sav.load()
+    p = good()
+    plan = _lib.PlanStruct()
+    fake = 1 << 20                     # never dereferenced: validation fails first
+    for name in ("perm_q", "q_off", "counts_t", "counts_b", "counts_r", "k_head", "sel_off", "sel_idx", "work",
+                 "status"):
+        setattr(plan, name, fake)
+    _, _, work = sav.sizes(p)
+    plan.work_capacity = work
+    ev = (ctypes.c_void_p * 5)(*([fake] * 5))
+    for arr, n in ((None, 5), (ev, 0), (ev, 6)):
+        st = lib.scope_plan_timed(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(plan), fake, 1 << 40,
+                                  arr, n, None)
+        assert st == 1
+    ev[2] = None                       # a null event
+    st = lib.scope_plan_timed(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(plan), fake, 1 << 40, ev, 5, None)
+    assert st == 1
+    st = lib.scope_plan_timed(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(plan), fake, 16, ev, 5, None)
+    assert st == 3                     # the workspace check comes first, as in scope_plan

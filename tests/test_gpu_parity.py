@@ -2,6 +2,9 @@
 seconds.  The shapes span several tiles of each kernel with ragged tails
 (128-query attention chunks, 64-key gather chunks, 32-centroid MFMA blocks,
 256-point assignment tiles)."""
+import math
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -333,3 +336,49 @@ def test_kmeanspp_seeds_all_points_coincide():
     g = run_gpu(w, inputs=(q, k, k))
     assert g["status"][2] == 0
     _seeds_vs_oracle(w, q, k, g)
+
+
+def _assert_all_ties(w, g, rho):
+    """Every key of every cluster has the same proxy logit: t_c = ceil(rho N)
+    (the Cm = 1 closed form) and S_c the lowest-index keys."""
+    t_want = math.ceil(Fraction(rho) * w.N)
+    for bh in range(w.BH):
+        assert g["t"][bh].tolist() == [t_want] * w.Cq, f"head {bh}: t_c {sorted(set(g['t'][bh].tolist()))}"
+        for c, s in enumerate(gpu_sel(g, bh, w.Cq)):
+            assert np.array_equal(s, np.arange(g["r"][bh, c])), f"head {bh} cluster {c}"
+
+
+@pytest.mark.parametrize("rho", [0.9, 0.5])
+def test_tie_walk_all_queries_at_the_origin(rho):
+    """Queries all zero: every LUT row is 0 and all N = 36783 logits of every
+    cluster tie, far more than the 1024 boundary candidates the selection
+    sorts, so the Top-p pass and the final selection resolve the boundary by
+    their walk over distinct logits.  Plan and attention against the oracle."""
+    w = workloads.small("tieZ", 9, 61, 67, 64, (16, 24, 24), "bf16", 30, 12, index=111, H=1, rhos=(rho,))
+    say("tie walk, zero queries", w.N, rho)
+    q, k, v = workloads.generate(w)
+    q = np.zeros_like(q)
+    heads = [O.workload_head(w, 0, q[0], k[0], v[0])]
+    g = run_gpu(w, inputs=(q, k, v))
+    assert g["status"][1] == 0 and g["status"][2] == 0
+    _assert_all_ties(w, g, rho)
+    assert_plan_equal(w, g, heads)
+    mx, mn = assert_attention(g["out"][0], heads[0]["out"], w.dtype, "zero queries")
+    say(f"  max {mx:.2e} mean {mn:.2e}")
+
+
+@pytest.mark.parametrize("rho", [0.9, 0.5])
+def test_tie_walk_one_key_centroid(rho):
+    """Cm = 1: every key has the same code triple, so inside each query
+    cluster all N = 4991 logits are equal (the closed form t_c = ceil(rho N),
+    S_c = the lowest indices), with 20 distinct query clusters."""
+    w = workloads.small("tieC1", 7, 23, 31, 128, (44, 42, 42), "bf16", 20, 1, index=113, H=2, rhos=(rho,))
+    say("tie walk, Cm = 1", w.N, rho)
+    heads = oracle_heads(w)
+    g = run_gpu(w)
+    assert g["status"][1] == 0
+    _assert_all_ties(w, g, rho)
+    assert_plan_equal(w, g, heads)
+    for bh, o in enumerate(heads):
+        mx, mn = assert_attention(g["out"][bh], o["out"], w.dtype, f"Cm = 1 head {bh}")
+        say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")

@@ -243,3 +243,28 @@ def test_tiny_end_to_end_invariants():
         p = np.exp(logit - logit.max(1, keepdims=True))
         dense = (p @ v[bh]) / p.sum(1, keepdims=True)
         np.testing.assert_allclose(d["out"], dense, atol=1e-12)
+
+
+# --- queries grouped by cluster (the attention work order) ---------------------
+
+def test_cluster_permutation_hand_built_example():
+    """Labels worked by hand: members of each cluster listed in ascending token
+    order, clusters in ascending label order, empty clusters give equal offsets,
+    and the offsets start at 0 and end at N."""
+    labels = np.array([2, 0, 2, 3, 0, 2, 0, 3, 2, 0])
+    perm, off = O.cluster_permutation(labels, 5)
+    #           cluster 0       cluster 2        cluster 3   (1 and 4 empty)
+    assert perm.tolist() == [1, 4, 6, 9, 0, 2, 5, 8, 3, 7]
+    assert off.tolist() == [0, 4, 4, 8, 10, 10]
+
+
+def test_cluster_permutation_is_stable_inside_each_cluster():
+    """Against a brute-force grouping: for every cluster c the slice
+    perm[off[c]:off[c+1]] is exactly the ascending list of tokens with label c."""
+    rng = np.random.default_rng(12)
+    for Cq, N in ((1, 7), (5, 64), (40, 33)):
+        labels = rng.integers(0, Cq, N)
+        perm, off = O.cluster_permutation(labels, Cq)
+        assert len(off) == Cq + 1 and off[0] == 0 and off[-1] == N
+        for c in range(Cq):
+            assert perm[off[c]:off[c + 1]].tolist() == [i for i in range(N) if labels[i] == c]
