@@ -50,11 +50,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fidelity", action="store_true", help="run the proxy-fidelity sweep instead of the bench")
     ap.add_argument("--fidelity-rows", type=int, default=32, help="sampled query rows per head for --fidelity")
-    ap.add_argument("--partition", choices=("rope", "random"), default="rope",
-                    help="--fidelity: proxy subspaces from the 3D-RoPE ranges or from a seeded random channel order")
+    ap.add_argument("--partition", choices=("rope", "random", "full"), default="rope",
+                    help="--fidelity: proxy subspaces from the 3D-RoPE ranges, from a seeded random channel order, "
+                         "or no partition: one key codebook over all d channels (the cluster-level proxy) with "
+                         "--full-cm centroids")
+    ap.add_argument("--full-cm", type=int, default=None,
+                    help="--partition full: key centroids of the one codebook (default 3 Cm, the centroid budget "
+                         "of the three subspace codebooks, at most 1024)")
+    ap.add_argument("--heads", type=int, default=None,
+                    help="--fidelity: run only the first H heads of the workload (sampled heads at the 720p sizes)")
     ap.add_argument("--selection", choices=("scope", "fixed-topk"), default="scope",
                     help="--fidelity: the full selection, or Top-p / fixed Top-k without the online per-head Top-k "
                          "at a rho matched to the full selection's density")
+    ap.add_argument("--layers", type=int, default=40,
+                    help="attention layers per denoising step of the dense-prefix schedule (the pages fix only "
+                         "that the first layer is dense at every step; the count is a stand-in)")
+    ap.add_argument("--dense-steps", type=float, default=None,
+                    help="fraction of denoising steps run dense (default: 0.2 for the Wan-like workloads, "
+                         "0.1 otherwise, as the pages give for Wan and HunyuanVideo)")
     ap.add_argument("--warm-iters", type=int, default=2,
                     help="Lloyd iterations of the warm-started plan (negative: skip the warm-start measurement)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attend_traffic.json"),
@@ -400,7 +413,7 @@ def _fidelity_of_plan(a, w, p, pl, qd, kd, vd, rng):
     return res
 
 
-def _matched_rho(w, sav, qd, kd, pl, target, lo, perm, steps=14):
+def _matched_rho(w, sav, qd, kd, pl, target, lo, perm, extra=None, steps=14):
     """rho of the fixed-Top-k-only selection whose realised density is closest to target (bisection;
     the density is nondecreasing in rho)."""
     import torch
@@ -408,7 +421,7 @@ def _matched_rho(w, sav, qd, kd, pl, target, lo, perm, steps=14):
     hi = 1.0
     for _ in range(steps):
         mid = 0.5 * (lo + hi)
-        p = sav.params_for(w, rho=mid, channel_perm=perm, online_khead=False)
+        p = sav.params_for(w, rho=mid, channel_perm=perm, online_khead=False, **(extra or {}))
         sav.plan(p, qd, kd, pl)
         torch.cuda.synchronize()
         dens = _density(w, pl)
@@ -434,6 +447,12 @@ def fidelity(a):
     dt = torch.bfloat16 if w0.dtype == "bf16" else torch.float32
     keys = ("recall", "mass", "spearman", "density", "err", "rho_used")
     res = {rho: {k: [] for k in keys} for rho in FID_RHOS}
+    extra = {}
+    if a.partition == "full":
+        w0 = w0.with_(Cm=a.full_cm or min(1024, 3 * w0.Cm))
+        extra = {"full_dim_keys": True}
+    if a.heads:
+        w0 = w0.with_(H=min(a.heads, w0.H))
     for rep in range(FID_REPS):
         w = w0.with_(index=w0.index + 1000 * rep, alpha=FID_ALPHA)
         q, k, v = workloads.generate(w)
@@ -442,16 +461,16 @@ def fidelity(a):
         perm = None
         if a.partition == "random":
             perm = np.random.default_rng([w.index, 11]).permutation(w.d).tolist()
-        pl = sav.Plan(sav.params_for(w, channel_perm=perm), device=dev, debug=True)
+        pl = sav.Plan(sav.params_for(w, channel_perm=perm, **extra), device=dev, debug=True)
         for rho in FID_RHOS:
             rng = np.random.default_rng([w.index, 77])     # the same sampled rows at every rho
-            p = sav.params_for(w, rho=rho, channel_perm=perm)
+            p = sav.params_for(w, rho=rho, channel_perm=perm, **extra)
             rho_used = rho
             if a.selection == "fixed-topk":
                 sav.plan(p, qd, kd, pl)
                 torch.cuda.synchronize()
-                rho_used = _matched_rho(w, sav, qd, kd, pl, _density(w, pl), rho, perm)
-                p = sav.params_for(w, rho=rho_used, channel_perm=perm, online_khead=False)
+                rho_used = _matched_rho(w, sav, qd, kd, pl, _density(w, pl), rho, perm, extra)
+                p = sav.params_for(w, rho=rho_used, channel_perm=perm, online_khead=False, **extra)
             r = _fidelity_of_plan(a, w, p, pl, qd, kd, vd, rng)
             r["rho_used"] = rho_used
             for key in keys:
@@ -460,7 +479,8 @@ def fidelity(a):
         del pl
     summary = {rho: {key: {"mean": float(np.mean(vals)), "std": float(np.std(vals, ddof=1))}
                      for key, vals in e.items()} for rho, e in res.items()}
-    print(json.dumps({"fidelity": w0.name, "partition": a.partition, "selection": a.selection, "alpha": FID_ALPHA,
+    print(json.dumps({"fidelity": w0.name, "partition": a.partition, "key_centroids": w0.Cm, "heads": w0.BH,
+                      "selection": a.selection, "alpha": FID_ALPHA,
                       "reps": FID_REPS, "rows_per_head": a.fidelity_rows, "top_frac": 0.1,
                       "by_rho": {str(r): v for r, v in summary.items()}}), flush=True)
 
@@ -562,6 +582,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "wall_s": round(wall, 3),
     }
+    line["dense_prefix"] = dense_prefix(a, w, qd, kd, vd, sav, torch, ms)
     if a.warm_iters >= 0:
         line["warm_start"] = warm_start(a, w, rho, qd, kd, vd, sav, torch)
     if not a.no_cpu_baseline:
@@ -604,6 +625,37 @@ def stage_breakdown(w, p, sav, pl, qd, kd, vd, qr, kr, out, torch, pairs, reps=3
             "S4S5_score_select": {"bound": "hbm", "bytes": b_sel, "GB/s": gbs(b_sel, med["score_select"]),
                                   "frac": round(b_sel / (med["score_select"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
             "S6_attend": {"bound": "mfma", "TFLOP/s": round(4.0 * w.d * pairs / (med["attend"] * 1e-3) / 1e12, 2)}}
+
+
+def dense_prefix(a, w, qd, kd, vd, sav, torch, scope_ms):
+    """The dense-prefix schedule of the SCOPE paper (referee report, major
+    comment 3): the first attention layer is dense at every denoising step and
+    the first 20% (Wan) or 10% (HunyuanVideo) of the steps are dense
+    throughout.  Measures one dense layer (SCOPE_DENSE: RoPE, the all-keys
+    plan and the same attention kernel) and blends it with the sparse step:
+    share of dense layer-steps f = 1/L + (1 - 1/L) p, blended = f t_dense +
+    (1 - f) t_scope per layer-step."""
+    p_dense = sav.params_for(w, dense=True)
+    pl = sav.Plan(p_dense, device=qd.device, debug=False)
+    qr, kr, out = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(a.warmup + a.steps)]
+    for e0, e1 in ev:
+        e0.record()
+        sav.plan(p_dense, qd, kd, pl, qr, kr)
+        sav.attend(p_dense, pl, qr, kr, vd, out)
+        e1.record()
+    torch.cuda.synchronize()
+    dense_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev[a.warmup:]]))
+    frac = a.dense_steps if a.dense_steps is not None else (0.2 if w.name.startswith("wan") else 0.1)
+    L = max(1, a.layers)
+    f = 1.0 / L + (1.0 - 1.0 / L) * frac
+    blended = f * dense_ms + (1.0 - f) * scope_ms
+    dense_flops = 4.0 * w.d * float(w.N) ** 2 * w.BH
+    return {"dense_step_ms": round(dense_ms, 4), "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+            "layers": L, "dense_step_fraction": frac, "dense_share": round(f, 5),
+            "blended_ms_per_layer_step": round(blended, 4),
+            "attention_speedup_vs_all_dense": round(dense_ms / blended, 4)}
 
 
 def _attend_sha():

@@ -70,6 +70,22 @@ typedef enum { SCOPE_F32 = 0, SCOPE_BF16 = 1 } scope_dtype;
                                          Top-p / fixed Top-k selection without the online
                                          per-head Top-k extension of Eq. (10) (the Fig. 7
                                          ablation); k_head is still computed and written */
+#define SCOPE_FULL_DIM_KEYS 0x10u     /* the cluster-level ablation proxy (forward implications of
+                                         the SCOPE review: clustering whole key vectors instead of
+                                         the 3D-RoPE subspaces): one key codebook of Cm centroids
+                                         over all d channels (k-means++ draws of clustering 1), the
+                                         proxy P[c][z_j] / sqrt(d) with a one-term table; the other
+                                         two codes are 0 and their table rows zero.  Not with
+                                         SCOPE_PERMUTE_CHANNELS or SCOPE_DENSE */
+#define SCOPE_DENSE 0x8u              /* dense attention (the dense prefix of the SCOPE paper's
+                                         schedule: the first layer at every step and the first
+                                         denoising steps run dense): scope_plan applies RoPE and
+                                         writes a plan in which every query attends to all N keys
+                                         (cluster 0 holds all queries in token order, r_0 = t_0 =
+                                         b_0 = k_head = N, S_0 = 0..N-1, the other clusters are
+                                         empty); no k-means, scoring or selection runs, and the
+                                         optional debug buffers are not written.  Not combinable
+                                         with the other flags. */
 
 typedef struct {
   int32_t B, H;            /* batch and heads; every (b, h) is independent; B*H <= 65535 */
@@ -84,7 +100,8 @@ typedef struct {
   double alpha;            /* fixed Top-k floor of Eq. (8) as a fraction of N, 0..1 */
   uint64_t seed;           /* k-means++ draws: SplitMix64 outputs */
   int32_t dtype;           /* scope_dtype */
-  uint32_t flags;          /* SCOPE_USE_INIT_CENTROIDS | SCOPE_PERMUTE_CHANNELS | SCOPE_FIXED_TOPK_ONLY */
+  uint32_t flags;          /* SCOPE_USE_INIT_CENTROIDS | SCOPE_PERMUTE_CHANNELS | SCOPE_FIXED_TOPK_ONLY |
+                              SCOPE_FULL_DIM_KEYS, or SCOPE_DENSE alone */
   /* With SCOPE_PERMUTE_CHANNELS: entries 0..d-1 are a permutation of
    * 0..d-1 (else SCOPE_ERR_INVALID); the query clustering, the three key
    * codebooks, the centroids and the LUT then work on the RoPE'd rows with
@@ -126,7 +143,8 @@ typedef struct {
                             fp32, independent of scheduling); outside it they are
                             ordinary fp64 sums (the plan is still valid) */
   float* q_centroids;    /* [B*H][Cq][d] final query centroids (fp32) */
-  float* k_centroids;    /* [B*H][Cm][d] key centroids, row z = (mu^T_z | mu^H_z | mu^W_z) */
+  float* k_centroids;    /* [B*H][Cm][d] key centroids, row z = (mu^T_z | mu^H_z | mu^W_z)
+                            (SCOPE_FULL_DIM_KEYS: mu_z over all d channels) */
   int32_t* q_labels;     /* [B*H][N] query cluster of each token */
   uint16_t* k_codes;     /* [B*H][N][4] (z^T, z^H, z^W, 0) key subspace codes */
   int32_t* seeds;        /* [B*H][4][max(Cq,Cm)] k-means++ centre indices (Q, T, H, W) */

@@ -108,9 +108,9 @@ def token_positions(T: int, Hg: int, Wg: int) -> np.ndarray:
 def rope_3d(x: np.ndarray, grid, split, base: float = 10000.0) -> np.ndarray:
     """3D rotary embedding of one head, x: [N, d] fp64, returned in fp64 (unrounded).
 
-    The channels are the concatenation [T | H | W] of three ranges (the
-    "temporal, height and width channel ranges of 3D RoPE" that SCOPE's key
-    subspaces follow).  Inside range m (offset o, width d_m) channel pairs
+    The channels are the concatenation [T | H | W] of the three 3D-RoPE
+    channel ranges (temporal, height, width), which are the key subspaces
+    of SCOPE (core discovery, pith.science page).  Inside range m (offset o, width d_m) channel pairs
     (o+2i, o+2i+1) rotate by angle p_m * base^(-2i/d_m), p_m being the
     token's t, h or w index (RoFormer's interleaved-pair form, applied per
     range; reading, the pages fix only the split).
@@ -236,6 +236,13 @@ def lookup_tables(q_centroids: np.ndarray, k_centroids: np.ndarray, split) -> np
     ])
 
 
+def lookup_table_full(q_centroids: np.ndarray, k_centroids: np.ndarray) -> np.ndarray:
+    """The cluster-level proxy of the ablation that clusters the keys in all d
+    channels at once (one codebook instead of the T/H/W product code):
+    P[c, z] = <qbar_c, mu_z> over every channel; [Cq, Cm]."""
+    return q_centroids @ k_centroids.T
+
+
 def proxy_logits(P: np.ndarray, codes: np.ndarray, d: int) -> np.ndarray:
     """Eq. (6): s[c, j] = (P^T[c, zT_j] + P^H[c, zH_j] + P^W[c, zW_j]) / sqrt(d); [Cq, N]."""
     return (P[0][:, codes[:, 0]] + P[1][:, codes[:, 1]] + P[2][:, codes[:, 2]]) / np.sqrt(d)
@@ -316,6 +323,19 @@ def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_labels: np.n
     return out
 
 
+def dense_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, grid, split, dtype: str,
+               rope_base: float = 10000.0) -> Dict[str, np.ndarray]:
+    """Dense attention of one head (the dense prefix of the SCOPE paper's
+    schedule, referee report of the pith.science page, major comment 3: the
+    first layer at every step and the first denoising steps skip the sparse
+    selection): RoPE, then o_i = softmax_j over all N keys (<q'_i, k'_j>/sqrt(d)) v_j."""
+    qr = round_storage(rope_3d(q, grid, split, rope_base), dtype)
+    kr = round_storage(rope_3d(k, grid, split, rope_base), dtype)
+    N = q.shape[0]
+    out = sparse_attention(qr, kr, v, np.zeros(N, dtype=np.int64), [np.arange(N)])
+    return {"q_rope": qr, "k_rope": kr, "out": out}
+
+
 def cluster_permutation(q_labels: np.ndarray, Cq: int):
     """Tokens grouped by cluster, ascending index inside a cluster; offsets [Cq+1]."""
     perm = np.argsort(q_labels, kind="stable")
@@ -332,7 +352,7 @@ def scope_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, grid, split, dtyp
                seed: int = 0, bh: int = 0, rope_base: float = 10000.0,
                init_q: Optional[np.ndarray] = None, init_k: Optional[np.ndarray] = None,
                with_attention: bool = True, channel_perm: Optional[np.ndarray] = None,
-               online_khead: bool = True) -> Dict[str, object]:
+               online_khead: bool = True, full_dim_keys: bool = False) -> Dict[str, object]:
     """The whole path for one head; inputs are fp64 arrays holding `dtype` values.
 
     init_q [Cq, d] / init_k [Cm, d] replace k-means++ when given.
@@ -342,6 +362,14 @@ def scope_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, grid, split, dtyp
     clustering, centroids, LUT and proxy use the RoPE'd rows with their
     channels reordered, row[:, channel_perm], so key subspace m is the m-th
     run of split[m] reordered channels; attention uses the rows as they are.
+
+    full_dim_keys (the other ablation of the pages' forward implications: a
+    cluster-level proxy over whole key vectors, as in SVG2, instead of the
+    subspace partition): the keys form one k-means clustering of Cm centroids
+    over all d channels (k-means++ draws of clustering 1), the proxy is
+    P[c, z_j] / sqrt(d) with the one-term table of lookup_table_full; the
+    codes of the two other terms are 0 and their tables are zero, so the
+    same three-term Eq. (6) sum gives that value exactly.
     """
     N, d = q.shape
     qr = round_storage(rope_3d(q, grid, split, rope_base), dtype)
@@ -357,14 +385,21 @@ def scope_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, grid, split, dtyp
     k_cent = np.zeros((Cm, d))
     codes = np.zeros((N, 3), dtype=np.int64)
     k_seeds = []
-    for m, (o, dm) in enumerate(zip(offs, split)):
-        init = None if init_k is None else init_k[:, o:o + dm]
-        km = kmeans(kc[:, o:o + dm], Cm, iters, dtype, seed, bh, 1 + m, init)
-        k_cent[:, o:o + dm] = km["centroids"]
-        codes[:, m] = km["labels"]
-        k_seeds.append(km["seeds"])
-
-    P = lookup_tables(kq["centroids"], k_cent, split)
+    if full_dim_keys:
+        assert channel_perm is None
+        km = kmeans(kc, Cm, iters, dtype, seed, bh, 1, init_k)
+        k_cent = km["centroids"]
+        codes[:, 0] = km["labels"]
+        k_seeds = [km["seeds"], None, None]
+        P = np.stack([lookup_table_full(kq["centroids"], k_cent), np.zeros((Cq, Cm)), np.zeros((Cq, Cm))])
+    else:
+        for m, (o, dm) in enumerate(zip(offs, split)):
+            init = None if init_k is None else init_k[:, o:o + dm]
+            km = kmeans(kc[:, o:o + dm], Cm, iters, dtype, seed, bh, 1 + m, init)
+            k_cent[:, o:o + dm] = km["centroids"]
+            codes[:, m] = km["labels"]
+            k_seeds.append(km["seeds"])
+        P = lookup_tables(kq["centroids"], k_cent, split)
     s = proxy_logits(P, codes, d)
     n = np.bincount(kq["labels"], minlength=Cq)
     t, b, kh, r, sel = hybrid_select(s, n, rho, alpha, online_khead)

@@ -19,6 +19,8 @@ SCOPE_BF16 = 1
 SCOPE_USE_INIT_CENTROIDS = 0x1
 SCOPE_PERMUTE_CHANNELS = 0x2
 SCOPE_FIXED_TOPK_ONLY = 0x4
+SCOPE_DENSE = 0x8
+SCOPE_FULL_DIM_KEYS = 0x10
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small",
           4: "plan buffer too small", 5: "HIP error"}
@@ -85,10 +87,14 @@ def load():
 
 
 def make_params(*, B, H, T, Hg, Wg, d, split, Cq, Cm, iters=10, rope_base=10000.0, rho=0.9, alpha=0.0,
-                seed=0, dtype="bf16", init_centroids=False, channel_perm=None, online_khead=True) -> Params:
+                seed=0, dtype="bf16", init_centroids=False, channel_perm=None, online_khead=True,
+                dense=False, full_dim_keys=False) -> Params:
     """channel_perm: None, or the channel order of the proxy subspaces (a
     permutation of 0..d-1; sets SCOPE_PERMUTE_CHANNELS); online_khead=False
-    sets SCOPE_FIXED_TOPK_ONLY (r_c = b_c)."""
+    sets SCOPE_FIXED_TOPK_ONLY (r_c = b_c); dense=True sets SCOPE_DENSE
+    (dense attention: RoPE and a plan of all keys for every query);
+    full_dim_keys=True sets SCOPE_FULL_DIM_KEYS (one key codebook over all d
+    channels instead of the T/H/W subspaces)."""
     p = Params()
     p.B, p.H, p.T, p.Hg, p.Wg, p.d = B, H, T, Hg, Wg, d
     p.d_t, p.d_h, p.d_w = split
@@ -98,6 +104,10 @@ def make_params(*, B, H, T, Hg, Wg, d, split, Cq, Cm, iters=10, rope_base=10000.
     p.flags = SCOPE_USE_INIT_CENTROIDS if init_centroids else 0
     if not online_khead:
         p.flags |= SCOPE_FIXED_TOPK_ONLY
+    if dense:
+        p.flags |= SCOPE_DENSE
+    if full_dim_keys:
+        p.flags |= SCOPE_FULL_DIM_KEYS
     if channel_perm is not None:
         cp = [int(c) for c in channel_perm]
         if len(cp) != d:

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
       m = 0; bh = b / sy.Wq; wg = b - bh * sy.Wq;
     } else {
       const int c = (b - nq) / sy.Wk;
-      wg = (b - nq) - c * sy.Wk; bh = c / 3; m = 1 + (c - bh * 3);
+      wg = (b - nq) - c * sy.Wk; bh = c / g.nk; m = 1 + (c - bh * g.nk);
     }
   }
   const int W = m == 0 ? sy.Wq : sy.Wk;
@@ -962,7 +962,7 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
       m = 0; bh = b / sy.Wq; wg = b - bh * sy.Wq;
     } else {
       const int c = (b - nq) / sy.Wk;
-      wg = (b - nq) - c * sy.Wk; bh = c / 3; m = 1 + (c - bh * 3);
+      wg = (b - nq) - c * sy.Wk; bh = c / g.nk; m = 1 + (c - bh * g.nk);
     }
   }
   // W workgroups share the clustering: this one owns the points
@@ -1754,8 +1754,10 @@ __global__ void pack_kernel(Geo g, const int32_t* __restrict__ labels, uint16_t*
   const int32_t* l = labels + (size_t)bh * 4 * g.N + n;
   ushort4 c;
   c.x = (uint16_t)l[g.N];
-  c.y = (uint16_t)l[2 * (size_t)g.N];
-  c.z = (uint16_t)l[3 * (size_t)g.N];
+  // one key codebook (SCOPE_FULL_DIM_KEYS): the other two codes are 0, and
+  // their lookup-table rows are all zero
+  c.y = g.nk > 1 ? (uint16_t)l[2 * (size_t)g.N] : (uint16_t)0;
+  c.z = g.nk > 2 ? (uint16_t)l[3 * (size_t)g.N] : (uint16_t)0;
   c.w = 0;
   reinterpret_cast<ushort4*>(codes)[i] = c;
   qlab[i] = l[0];
@@ -1785,7 +1787,7 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
 // re-decided with fp64 distances (ties to the lowest index), so the
 // labels equal the fp64 argmin.
 // ---------------------------------------------------------------------------
-constexpr int ASG_NT = 256;
+constexpr int ASG_WAVES = 12288;   // waves of one assignment, over all heads and clusterings
 
 __device__ __forceinline__ float pack_pos(float x, int v) {
   return __uint_as_float((__float_as_uint(x) & ~0xFu) | (uint32_t)v);
@@ -1925,8 +1927,11 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
 struct AsgSplit {
   int start[5];
 };
-template <int KBMAX>
-__global__ __launch_bounds__(ASG_NT) void assign2_kernel(const uint16_t* __restrict__ qr,
+// NT threads (NT / 64 waves) share one centroid table in LDS: a launch whose
+// table is large takes more waves per workgroup, so that the SIMDs still hold
+// two or three waves each.
+template <int KBMAX, int NT>
+__global__ __launch_bounds__(NT) void assign2_kernel(const uint16_t* __restrict__ qr,
                                                          const uint16_t* __restrict__ kr, Geo g,
                                                          const uint16_t* __restrict__ cbf,
                                                          const float* __restrict__ cnorm,
@@ -1941,11 +1946,11 @@ __global__ __launch_bounds__(ASG_NT) void assign2_kernel(const uint16_t* __restr
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* sc = reinterpret_cast<uint16_t*>(smem_raw);                               // [Cpad][ldc] -2 mu
   float* scn = reinterpret_cast<float*>(smem_raw + (size_t)Cpad * ldc * 2);           // [Cpad] ||mu||^2
-  double* xsh = reinterpret_cast<double*>(smem_raw + (size_t)Cpad * ldc * 2 + (size_t)Cpad * 4);   // [4][128]
-  __shared__ float red[8];
+  double* xsh = reinterpret_cast<double*>(smem_raw + (size_t)Cpad * ldc * 2 + (size_t)Cpad * 4);   // [NT/64][128]
+  __shared__ float red[NT / 64];
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint16_t* gc = cbf + ((size_t)bh * 4 + m) * g.CmaxPad * g.DPmax;
-  for (int idx = tid; idx < Cpad * (dpad / 2); idx += ASG_NT) {
+  for (int idx = tid; idx < Cpad * (dpad / 2); idx += NT) {
     const int r = idx / (dpad / 2), c2 = idx % (dpad / 2);
     const uint32_t u = *reinterpret_cast<const uint32_t*>(gc + (size_t)r * g.DPmax + 2 * c2);
     const float f0 = -2.f * __uint_as_float(u << 16), f1 = -2.f * __uint_as_float(u & 0xFFFF0000u);
@@ -1954,17 +1959,17 @@ __global__ __launch_bounds__(ASG_NT) void assign2_kernel(const uint16_t* __restr
   }
   const float* gcn = cnorm + ((size_t)bh * 4 + m) * g.CmaxPad;
   float mx = 0.f;
-  for (int idx = tid; idx < Cpad; idx += ASG_NT) {
+  for (int idx = tid; idx < Cpad; idx += NT) {
     const float v = gcn[idx];
     scn[idx] = v;
     if (idx < C) mx = fmaxf(mx, v);
   }
-  mx = block_max<float, ASG_NT>(mx, red);   // also orders the LDS fills above
+  mx = block_max<float, NT>(mx, red);   // also orders the LDS fills above
   const float M = sqrtf(mx) * 1.0001f;
   const uint16_t* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + off;
   const bool vec16 = ((off * 2) % 16 == 0) && ((d * 2) % 16 == 0);
   int32_t* lab = labels + ((size_t)bh * 4 + m) * N;
-  const int gw = part * (ASG_NT / 64) + wv, gstride = nparts * (ASG_NT / 64);
+  const int gw = part * (NT / 64) + wv, gstride = nparts * (NT / 64);
   double* xs = xsh + wv * 128;
   const int kbn = dpad / 16;
   auto run = [&](auto kb) {
@@ -1991,28 +1996,29 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {
 
 template <typename T>
 static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace& w, int32_t* status, hipStream_t s) {
-  dim3 grid(g.BH, 4);
+  const int ncl = 1 + g.nk;   // active clusterings
+  dim3 grid(g.BH, ncl);
   size_t cache = 0;
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < ncl; ++m) {
     const size_t b = (size_t)g.C[m] * (g.dm[m] + 2) * sizeof(T);
     if (b <= (size_t)SEED_CACHE_BYTES && b > cache) cache = b;
   }
   if (sizeof(T) == 2) {
     size_t need = 0;
     bool fits = (g.N + SL_NT - 1) / SL_NT <= 32;
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < ncl; ++m) {
       const SeedLLayout L = seedl_layout(g.N, g.C[m], g.dm[m]);
       need = L.bytes > need ? L.bytes : need;
     }
     fits = fits && need + 2048 <= (size_t)SL_LDS_LIMIT;
     if (fits) {
       bool vec = g.d % 8 == 0;
-      for (int m = 0; m < 4; ++m) vec = vec && g.off[m] % 8 == 0 && g.dm[m] % 8 == 0;
+      for (int m = 0; m < ncl; ++m) vec = vec && g.off[m] % 8 == 0 && g.dm[m] % 8 == 0;
       const void* fn = vec ? (const void*)seedl_kernel<true> : (const void*)seedl_kernel<false>;
       (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)need);
       // Resident slots left over after one workgroup per clustering go to the
       // query clusterings (the widest rows), at least 4 points per thread each.
-      const int chains = g.BH * 4;
+      const int chains = g.BH * ncl;
       const int wmax = max(1, g.N / (4 * SL_NT));
       int Wq = 1, Wk = 1, dev = 0, ncu = 0, coop = 0, per_cu = 0;
       if (hipGetDevice(&dev) == hipSuccess &&
@@ -2021,9 +2027,9 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
           hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, SL_NT, need) == hipSuccess) {
         const int cap = ncu * per_cu;
         Wk = max(1, min(wmax, cap / chains));
-        Wq = max(Wk, min(wmax, (cap - 3 * g.BH * Wk) / g.BH));
+        Wq = max(Wk, min(wmax, (cap - g.nk * g.BH * Wk) / g.BH));
       }
-      seed_sync_init_kernel<<<chains, 256, 0, s>>>(w.seed_sync, chains, status + 2);
+      seed_sync_init_kernel<<<g.BH * 4, 256, 0, s>>>(w.seed_sync, g.BH * 4, status + 2);   // areas (bh, m) for all 4 m
       SeedSync sy;
       sy.base = w.seed_sync;
       sy.abort = status + 2;
@@ -2039,7 +2045,7 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
       if (Wq > 1 || Wk > 1) {
         void* args[] = {(void*)&q16, (void*)&k16, (void*)&g, (void*)&d2, (void*)&sd, (void*)&qc, (void*)&kc,
                         (void*)&sy};
-        const unsigned nblk = (unsigned)(g.BH * Wq + 3 * g.BH * Wk);
+        const unsigned nblk = (unsigned)(g.BH * Wq + g.nk * g.BH * Wk);
         if (hipLaunchCooperativeKernel(fn, dim3(nblk), dim3(SL_NT), args, (unsigned)need, s) == hipSuccess) return;
         (void)hipGetLastError();
       }
@@ -2055,7 +2061,7 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
   const int P = (g.N + SR_NT - 1) / SR_NT;
   if (P <= SR_PMAX) {
     size_t rcache = 0;
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < ncl; ++m) {
       const size_t b = (size_t)g.C[m] * (g.dm[m] + 2) * sizeof(T);
       if (b <= (size_t)SR_CACHE_BYTES && b > rcache) rcache = b;
     }
@@ -2075,7 +2081,7 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
   // (a cooperative launch guarantees that, or fails and one is used).
   const auto kern = seed_kernel<T, false>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  const int chains = g.BH * 4;
+  const int chains = g.BH * ncl;
   const int G = ((g.N + SEED_NT - 1) / SEED_NT + SEED_RG - 1) / SEED_RG;
   // bf16 data only (fp32 data keeps one workgroup per clustering): the running
   // sum then adds the workgroups' partial sums in range order, a fixed order,
@@ -2089,9 +2095,9 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, SEED_NT, lds) == hipSuccess) {
     const int cap = ncu * per_cu;
     Wk = max(1, min(G, cap / chains));
-    Wq = max(Wk, min(G, (cap - 3 * g.BH * Wk) / g.BH));
+    Wq = max(Wk, min(G, (cap - g.nk * g.BH * Wk) / g.BH));
   }
-  seed_sync_init_kernel<<<chains, 256, 0, s>>>(w.seed_sync, chains, status + 2);
+  seed_sync_init_kernel<<<g.BH * 4, 256, 0, s>>>(w.seed_sync, g.BH * 4, status + 2);   // areas (bh, m) for all 4 m
   SeedSync sy;
   sy.base = w.seed_sync;
   sy.abort = status + 2;
@@ -2106,7 +2112,7 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
   if (Wq > 1 || Wk > 1) {
     void* args[] = {(void*)&qr, (void*)&kr, (void*)&g, (void*)&d2, (void*)&nr, (void*)&sd, (void*)&qc, (void*)&kc,
                     (void*)&sy};
-    const unsigned nblk = (unsigned)(g.BH * Wq + 3 * g.BH * Wk);
+    const unsigned nblk = (unsigned)(g.BH * Wq + g.nk * g.BH * Wk);
     if (hipLaunchCooperativeKernel((const void*)kern, dim3(nblk), dim3(SEED_NT), args, (unsigned)lds, s) ==
         hipSuccess)
       return;
@@ -2125,7 +2131,7 @@ hipError_t launch_seed(const Geo& g, const void* qr, const void* kr, const Works
 }
 
 hipError_t launch_prep(const Geo& g, const Workspace& w, hipStream_t s) {
-  centroid_kernel<<<dim3(4, g.BH), 256, 0, s>>>(g, w.qcent, w.kcent, w.cbf, w.cnorm);
+  centroid_kernel<<<dim3(1 + g.nk, g.BH), 256, 0, s>>>(g, w.qcent, w.kcent, w.cbf, w.cnorm);
   return hipGetLastError();
 }
 
@@ -2139,57 +2145,71 @@ hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Wor
                          hipStream_t s) {
   int32_t* out = labels_of(g, w, iter);
   if (g.bf16) {
-    int lds = 0;
-    for (int m = 0; m < 4; ++m) lds = max(lds, g.Cpad[m] * (g.dpad[m] + 8) * 2 + g.Cpad[m] * 4 + 4 * 128 * 8);
-    // about 3072 workgroups in all, shared among the four clusterings of a
-    // head in proportion to Cpad (dpad / 16 + 1) (MFMA blocks plus the
-    // per-candidate selection work; equal shares left the query clustering,
-    // with the widest rows, as the last to finish), at most one wave per
-    // 64-point tile
+    // ASG_WAVES waves in all, shared among the clusterings of a head in
+    // proportion to Cpad (dpad / 16 + 1) (MFMA blocks plus the per-candidate
+    // selection work; equal shares left the query clustering, with the widest
+    // rows, as the last to finish), at most one wave per 64-point tile
     const int ntiles = (g.N + 63) / 64;
     double wsum = 0.0, wm[4];
     for (int m = 0; m < 4; ++m) { wm[m] = (double)g.Cpad[m] * (g.dpad[m] / 16 + 1); wsum += wm[m]; }
-    const double per_head = (double)(3072 + g.BH - 1) / g.BH;
-    AsgSplit split;
-    split.start[0] = 0;
+    const double per_head = (double)(ASG_WAVES + g.BH - 1) / g.BH;
+    int waves[4];
     for (int m = 0; m < 4; ++m) {
-      int pm = (int)(per_head * wm[m] / wsum + 0.5);
-      pm = max(1, min(pm, (ntiles + 3) / 4));
-      split.start[m + 1] = split.start[m] + pm;
+      const int wv = (int)(per_head * wm[m] / wsum + 0.5);
+      waves[m] = m <= g.nk ? max(1, min(wv, ntiles)) : 0;   // inactive clusterings get no waves
     }
-    auto lds_of = [&](int m) { return g.Cpad[m] * (g.dpad[m] + 8) * 2 + g.Cpad[m] * 4 + 4 * 128 * 8; };
-    auto launch = [&](const AsgSplit& sp, int lo_m, int hi_m) {
-      int bytes = 0, kb = 1;
-      for (int m = lo_m; m < hi_m; ++m) { bytes = max(bytes, lds_of(m)); kb = max(kb, g.dpad[m] / 16); }
-      const dim3 grid(sp.start[hi_m] - sp.start[lo_m], 1, g.BH);
+    auto table_of = [&](int m) { return g.Cpad[m] * (g.dpad[m] + 8) * 2 + g.Cpad[m] * 4; };
+    constexpr int kLdsCU = 160 * 1024;   // LDS of one CU
+    // one launch for clusterings [lo_m, hi_m): the workgroup size that gives
+    // the most waves per SIMD (LDS per CU and the kernel's registers), the
+    // smaller one on ties
+    auto launch = [&](int lo_m, int hi_m) {
+      int table = 0, kb = 1;
+      for (int m = lo_m; m < hi_m; ++m) { table = max(table, table_of(m)); kb = max(kb, g.dpad[m] / 16); }
+      const int kbmax = kb <= 2 ? 2 : (kb <= 4 ? 4 : 8);
+      const int vgpr_waves = kbmax <= 4 ? 4 : 3;   // waves per SIMD the kernel's registers allow
+      int nt = 256, best = 0;
+      for (int cand = 256; cand <= 768; cand += 256) {
+        const int bytes = table + (cand / 64) * 128 * 8;
+        const int per_simd = min((kLdsCU / bytes) * (cand / 256), vgpr_waves);
+        if (per_simd > best) { best = per_simd; nt = cand; }
+      }
+      const int bytes = table + (nt / 64) * 128 * 8;
+      AsgSplit sp;
+      sp.start[0] = 0;
+      for (int m = 0; m < 4; ++m) {
+        const int wg = (m >= lo_m && m < hi_m) ? max(1, (waves[m] + nt / 64 - 1) / (nt / 64)) : 0;
+        sp.start[m + 1] = sp.start[m] + wg;
+      }
+      const dim3 grid(sp.start[4], 1, g.BH);
       auto go = [&](auto kern) {
         if (bytes > 64 * 1024)
           (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-        kern<<<grid, ASG_NT, bytes, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, out, sp);
+        kern<<<grid, nt, bytes, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, out, sp);
       };
-      if (kb <= 2) go(assign2_kernel<2>);
-      else if (kb <= 4) go(assign2_kernel<4>);
-      else go(assign2_kernel<8>);
+      if (kbmax == 2) {
+        if (nt == 256) go(assign2_kernel<2, 256>); else if (nt == 512) go(assign2_kernel<2, 512>);
+        else go(assign2_kernel<2, 768>);
+      } else if (kbmax == 4) {
+        if (nt == 256) go(assign2_kernel<4, 256>); else if (nt == 512) go(assign2_kernel<4, 512>);
+        else go(assign2_kernel<4, 768>);
+      } else {
+        if (nt == 256) go(assign2_kernel<8, 256>); else if (nt == 512) go(assign2_kernel<8, 512>);
+        else go(assign2_kernel<8, 768>);
+      }
     };
-    int lds_k = 0;
-    for (int m = 1; m < 4; ++m) lds_k = max(lds_k, lds_of(m));
-    constexpr int kLdsCU = 160 * 1024;   // LDS of one CU
-    if (lds_of(0) > 64 * 1024 && kLdsCU / lds_k > kLdsCU / lds_of(0)) {
-      // The query clustering's centroid table alone limits a CU to one
-      // workgroup: the key clusterings get a launch of their own with their
-      // smaller tables (several workgroups per CU).
-      AsgSplit q = split, k = split;
-      for (int m = 2; m <= 4; ++m) q.start[m] = q.start[1];
-      const int b = split.start[1];
-      k.start[0] = k.start[1] = 0;
-      for (int m = 2; m <= 4; ++m) k.start[m] = split.start[m] - b;
-      launch(q, 0, 1);
-      launch(k, 1, 4);
+    int table_k = 0;
+    for (int m = 1; m <= g.nk; ++m) table_k = max(table_k, table_of(m));
+    if (table_of(0) > 64 * 1024 && table_k < table_of(0)) {
+      // The query clustering's centroid table is large: the key clusterings
+      // get a launch of their own with their smaller tables.
+      launch(0, 1);
+      launch(1, 1 + g.nk);
     } else {
-      launch(split, 0, 4);
+      launch(0, 1 + g.nk);
     }
   } else {
-    dim3 grid((g.N + 255) / 256, 4, g.BH);
+    dim3 grid((g.N + 255) / 256, 1 + g.nk, g.BH);
     assign_exact_f32_kernel<<<grid, 256, 0, s>>>((const float*)qr, (const float*)kr, g, w.qcent, w.kcent, out);
   }
   return hipGetLastError();
@@ -2204,7 +2224,7 @@ hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Wor
   const bool delta = g.bf16 && it >= 2;
   const int parts = acc_parts(g);
   int ypairs = 0;
-  for (int m = 0; m < 4; ++m) ypairs += (g.dm[m] + SW - 1) / SW;
+  for (int m = 0; m <= g.nk; ++m) ypairs += (g.dm[m] + SW - 1) / SW;
   const size_t lds = (size_t)g.Cmax * SW * 8 + (size_t)g.Cmax * 4;
   dim3 grid(parts, ypairs, g.BH);
   auto go = [&](auto kern, const auto* q, const auto* k) {
@@ -2230,7 +2250,7 @@ hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Wor
   } else {
     if (SW == 32) go(accum_kernel<float, 32>, qf, kf); else go(accum_kernel<float, 16>, qf, kf);
   }
-  finalize_kernel<<<dim3((g.Cmax + 3) / 4, 4, g.BH), 256, 0, s>>>(g, w.psum, w.pcnt, SW, ns, parts, delta ? 1 : 0,
+  finalize_kernel<<<dim3((g.Cmax + 3) / 4, 1 + g.nk, g.BH), 256, 0, s>>>(g, w.psum, w.pcnt, SW, ns, parts, delta ? 1 : 0,
                                                                   w.stot, w.ssm, w.ntot, w.qcent, w.kcent, w.cbf, w.cnorm);
   return hipGetLastError();
 }

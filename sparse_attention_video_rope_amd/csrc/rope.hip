@@ -170,13 +170,14 @@ __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ q, cons
 
 hipError_t launch_rope(const Geo& g, const scope_params& p, const void* q, const void* k, void* qo,
                        void* ko, const Workspace& w, float* k_norm_max, int32_t* range_flag, hipStream_t s) {
-  const int n0 = g.T * g.dm[1] / 2, n1 = g.Hg * g.dm[2] / 2, n2 = g.Wg * g.dm[3] / 2;
-  rope_table_kernel<<<(n0 + n1 + n2 + 255) / 256, 256, 0, s>>>(w.rope_tab, n0, n1, n2, g.dm[1], g.dm[2],
-                                                               g.dm[3], p.rope_base, range_flag);
+  // the rotation follows the 3D-RoPE ranges (g.rdm), not the clustering geometry
+  const int n0 = g.T * g.rdm[0] / 2, n1 = g.Hg * g.rdm[1] / 2, n2 = g.Wg * g.rdm[2] / 2;
+  rope_table_kernel<<<(n0 + n1 + n2 + 255) / 256, 256, 0, s>>>(w.rope_tab, n0, n1, n2, g.rdm[0], g.rdm[1],
+                                                               g.rdm[2], p.rope_base, range_flag);
   RopeArgs a;
   a.BH = g.BH; a.N = g.N; a.d = g.d; a.Hg = g.Hg; a.Wg = g.Wg;
-  a.off1 = g.off[2]; a.off2 = g.off[3];
-  a.dm[0] = g.dm[1]; a.dm[1] = g.dm[2]; a.dm[2] = g.dm[3];
+  a.off1 = g.rdm[0]; a.off2 = g.rdm[0] + g.rdm[1];
+  a.dm[0] = g.rdm[0]; a.dm[1] = g.rdm[1]; a.dm[2] = g.rdm[2];
   a.toff[0] = 0; a.toff[1] = n0; a.toff[2] = n0 + n1;
   const uint64_t hw = (uint64_t)g.Hg * g.Wg;
   a.mhw = ((1ull << 32) + hw - 1) / hw;

@@ -21,10 +21,19 @@ Geo make_geo(const scope_params& p) {
   g.off[1] = 0; g.dm[1] = p.d_t;
   g.off[2] = p.d_t; g.dm[2] = p.d_h;
   g.off[3] = p.d_t + p.d_h; g.dm[3] = p.d_w;
+  g.rdm[0] = p.d_t; g.rdm[1] = p.d_h; g.rdm[2] = p.d_w;
+  g.nk = 3;
+  if (p.flags & SCOPE_FULL_DIM_KEYS) {
+    // one key codebook over all d channels; clusterings 2 and 3 unused
+    g.nk = 1;
+    g.dm[1] = p.d;
+    g.off[2] = g.off[3] = 0;
+    g.dm[2] = g.dm[3] = 0;
+  }
   g.Cmax = p.Cq > p.Cm ? p.Cq : p.Cm;
   g.DPmax = 0; g.CmaxPad = 0;
   for (int m = 0; m < 4; ++m) {
-    if (m > 0) g.C[m] = p.Cm;
+    if (m > 0) g.C[m] = m <= g.nk ? p.Cm : 0;
     g.Cpad[m] = round_up(g.C[m], 32);
     g.dpad[m] = round_up(g.dm[m], 16);
     if (g.dpad[m] > g.DPmax) g.DPmax = g.dpad[m];
@@ -47,7 +56,7 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
     return p;
   };
   const size_t BH = g.BH, N = g.N;
-  const int nrope = g.T * g.dm[1] / 2 + g.Hg * g.dm[2] / 2 + g.Wg * g.dm[3] / 2;
+  const int nrope = g.T * g.rdm[0] / 2 + g.Hg * g.rdm[1] / 2 + g.Wg * g.rdm[2] / 2;
   w.rope_tab = (double2*)take(sizeof(double2) * nrope);
   w.d2 = (double*)take(8 * BH * 4 * N);
   w.nearest = (int32_t*)take(4 * BH * 4 * N);
@@ -104,7 +113,11 @@ static scope_status validate(const scope_params* p) {
   if (!(p->rho > 0.0 && p->rho <= 1.0)) return SCOPE_ERR_INVALID;
   if (!(p->alpha >= 0.0 && p->alpha <= 1.0)) return SCOPE_ERR_INVALID;
   if (p->dtype != SCOPE_F32 && p->dtype != SCOPE_BF16) return SCOPE_ERR_INVALID;
-  if (p->flags & ~(SCOPE_USE_INIT_CENTROIDS | SCOPE_PERMUTE_CHANNELS | SCOPE_FIXED_TOPK_ONLY)) return SCOPE_ERR_INVALID;
+  if (p->flags &
+      ~(SCOPE_USE_INIT_CENTROIDS | SCOPE_PERMUTE_CHANNELS | SCOPE_FIXED_TOPK_ONLY | SCOPE_DENSE | SCOPE_FULL_DIM_KEYS))
+    return SCOPE_ERR_INVALID;
+  if ((p->flags & SCOPE_DENSE) && p->flags != SCOPE_DENSE) return SCOPE_ERR_INVALID;
+  if ((p->flags & SCOPE_FULL_DIM_KEYS) && (p->flags & SCOPE_PERMUTE_CHANNELS)) return SCOPE_ERR_INVALID;
   if (p->flags & SCOPE_PERMUTE_CHANNELS) {
     bool seen[128] = {};
     for (int i = 0; i < p->d; ++i) {
@@ -200,6 +213,13 @@ static scope_status plan_impl(const scope_params* p, const void* q, const void* 
   auto mark = [&](int i) -> hipError_t { return (ev && i < nev) ? hipEventRecord(ev[i], stream) : hipSuccess; };
   STEP(launch_rope(g, *p, q, k, q_rope, k_rope, w, plan->k_norm_max, plan->status + 3, stream));
   STEP(mark(0));
+  if (p->flags & SCOPE_DENSE) {
+    // dense attention: every query of a head attends to all of its keys
+    STEP(launch_dense_plan(g, *plan, stream));
+    STEP(launch_worklist(g, *plan, stream));
+    for (int i = 1; i < 5; ++i) STEP(mark(i));
+    return SCOPE_OK;
+  }
   // the clustering reads the rows in proxy channel order
   const void* qc = q_rope;
   const void* kc = k_rope;

@@ -23,8 +23,11 @@ constexpr int MAX_N = 1 << 18;  // largest token count supported (16 groups of 1
 struct Geo {
   int BH, N, d, T, Hg, Wg;
   int Cq, Cm, iters;
-  int off[4], dm[4], C[4], Cpad[4], dpad[4];
+  int off[4], dm[4], C[4], Cpad[4], dpad[4];   // channel offset / width, centroids, padded sizes per clustering
+  int rdm[3];                   // 3D-RoPE channel ranges (d_t, d_h, d_w), whatever the clustering geometry
   int Cmax, CmaxPad, DPmax;
+  int nk;                       // key clusterings: 3 (T, H, W subspaces) or 1 (all d channels,
+                                // SCOPE_FULL_DIM_KEYS); clusterings 0 .. nk are active
   int bf16;                     // 1: bf16 storage, 0: fp32
   int permute;                  // 1: clustering on channel-reordered copies of q_rope / k_rope
   int online_khead;             // 1: r_c = max(b_c, k_head) (Eq. 10); 0: r_c = b_c
@@ -118,6 +121,8 @@ hipError_t launch_khead(const Geo& g, const scope_plan_t& plan, const Workspace&
 hipError_t launch_final_select(const Geo& g, const scope_params& p, const Workspace& w,
                                const scope_plan_t& plan, hipStream_t s);
 hipError_t launch_worklist(const Geo& g, const scope_plan_t& plan, hipStream_t s);
+// The plan of dense attention (SCOPE_DENSE): cluster 0 holds every query and all N keys.
+hipError_t launch_dense_plan(const Geo& g, const scope_plan_t& plan, hipStream_t s);
 hipError_t launch_attend(const Geo& g, const scope_plan_t& plan, const void* qr, const void* kr,
                          const void* v, void* out, hipStream_t s);
 

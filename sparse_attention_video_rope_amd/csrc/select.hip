@@ -731,7 +731,53 @@ __global__ __launch_bounds__(1024) void worklist_kernel(int BH, int Cq, int chun
   if (tid == 0) status[0] = (int32_t)(base < cap ? base : cap);
 }
 
+// ---------------------------------------------------------------------------
+// Dense attention (SCOPE_DENSE): the plan in which every query attends to all
+// keys of its head.  Cluster 0 of each head holds the N queries in token
+// order and the key set 0..N-1 (r_0 = t_0 = b_0 = k_head = N); the other
+// clusters are empty.  Grid (ceil(N / 256), BH).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dense_plan_kernel(int BH, int N, int Cq, int32_t* __restrict__ perm_q,
+                                                         int32_t* __restrict__ q_off, int32_t* __restrict__ ct,
+                                                         int32_t* __restrict__ cb, int32_t* __restrict__ cr,
+                                                         int32_t* __restrict__ khead, int64_t* __restrict__ sel_off,
+                                                         int32_t* __restrict__ sel_idx, int64_t capacity,
+                                                         int32_t* __restrict__ status) {
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const bool fits = (int64_t)BH * N <= capacity;
+  if (i < N) {
+    perm_q[(size_t)bh * N + i] = i;
+    if (fits) sel_idx[(size_t)bh * N + i] = i;
+  }
+  if (blockIdx.x == 0) {
+    for (int c = threadIdx.x; c <= Cq; c += 256) q_off[(size_t)bh * (Cq + 1) + c] = c == 0 ? 0 : N;
+    for (int c = threadIdx.x; c < Cq; c += 256) {
+      const int v = c == 0 ? N : 0;
+      ct[(size_t)bh * Cq + c] = v;
+      cb[(size_t)bh * Cq + c] = v;
+      cr[(size_t)bh * Cq + c] = v;
+      sel_off[(size_t)bh * Cq + c] = (int64_t)bh * N + (c == 0 ? 0 : N);
+    }
+    if (threadIdx.x == 0) {
+      khead[bh] = N;
+      if (bh == BH - 1) {
+        sel_off[(size_t)BH * Cq] = (int64_t)BH * N;
+        status[1] = fits ? 0 : 1;
+        status[2] = 0;
+      }
+    }
+  }
+}
+
 // ---- launchers ----------------------------------------------------------------
+
+hipError_t launch_dense_plan(const Geo& g, const scope_plan_t& plan, hipStream_t s) {
+  dense_plan_kernel<<<dim3((g.N + 255) / 256, g.BH), 256, 0, s>>>(
+      g.BH, g.N, g.Cq, plan.perm_q, plan.q_off, plan.counts_t, plan.counts_b, plan.counts_r, plan.k_head,
+      plan.sel_off, plan.sel_idx, plan.sel_capacity, plan.status);
+  return hipGetLastError();
+}
 
 static SelArgs sel_args(const Geo& g, const scope_params& p) {
   SelArgs a;

@@ -22,8 +22,8 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = sav.load()
     names = declared_symbols()
-    assert names == ["scope_attend", "scope_plan", "scope_plan_finalize", "scope_plan_timed", "scope_status_string",
-                     "scope_workspace_size"]
+    assert names == ["scope_attend", "scope_plan", "scope_plan_finalize", "scope_plan_timed",
+                     "scope_status_string", "scope_workspace_size"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -94,8 +94,18 @@ def test_channel_permutation_validation():
         assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 1
     q = good(online_khead=False)
     assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 0
-    q.flags = 0x8                                           # unknown flag
+    q.flags = _lib.SCOPE_FULL_DIM_KEYS | _lib.SCOPE_FIXED_TOPK_ONLY   # one key codebook
+    assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 0
+    q.flags = _lib.SCOPE_FULL_DIM_KEYS | _lib.SCOPE_PERMUTE_CHANNELS   # not combinable
     assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 1
+    q.flags = 0x20                                          # unknown flag
+    assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 1
+    q.flags = _lib.SCOPE_DENSE                              # dense attention alone
+    assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 0
+    for other in (_lib.SCOPE_FIXED_TOPK_ONLY, _lib.SCOPE_USE_INIT_CENTROIDS, _lib.SCOPE_PERMUTE_CHANNELS,
+                  _lib.SCOPE_FULL_DIM_KEYS):
+        q.flags = _lib.SCOPE_DENSE | other                  # not combinable
+        assert lib.scope_workspace_size(ctypes.byref(q), None, None, None) == 1
     # entries beyond d are not read; the reordered copies of q_rope / k_rope (bf16) enlarge the workspace
     p.channel_perm[100] = 200
     ws_p, _, _ = sav.sizes(p)
@@ -171,3 +181,4 @@ def test_plan_timed_rejects_bad_event_arrays_before_launch():
     assert st == 1
     st = lib.scope_plan_timed(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(plan), fake, 16, ev, 5, None)
     assert st == 3                     # the workspace check comes first, as in scope_plan
+

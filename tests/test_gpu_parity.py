@@ -382,3 +382,48 @@ def test_tie_walk_one_key_centroid(rho):
     for bh, o in enumerate(heads):
         mx, mn = assert_attention(g["out"][bh], o["out"], w.dtype, f"Cm = 1 head {bh}")
         say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
+
+
+@pytest.mark.parametrize("w", SMALL + [workloads.CONFIGS["tiny"]], ids=IDS + ["tiny"])
+def test_dense_mode_matches_oracle_dense_attention(w):
+    """SCOPE_DENSE (the dense prefix of the schedule): RoPE and a plan of all
+    N keys for every query, then the same attention kernel; output against the
+    oracle's dense softmax attention, plan structure exact."""
+    say("dense", w.name)
+    q, k, v = workloads.generate(w)
+    p = sav.params_for(w, dense=True)
+    pl = sav.Plan(p, debug=False)
+    qr, kr, _ = sav.plan(p, to_dev(q, w.dtype), to_dev(k, w.dtype), pl)
+    out = to_np(sav.attend(p, pl, qr, kr, to_dev(v, w.dtype))).reshape(w.BH, w.N, w.d)
+    BH, N, Cq = w.BH, w.N, w.Cq
+    assert to_np(pl.status)[1] == 0
+    assert np.array_equal(to_np(pl.perm_q).reshape(BH, N), np.tile(np.arange(N), (BH, 1)))
+    assert np.array_equal(to_np(pl.q_off).reshape(BH, Cq + 1), np.tile([0] + [N] * Cq, (BH, 1)))
+    for name in ("counts_t", "counts_b", "counts_r"):
+        assert np.array_equal(to_np(getattr(pl, name)).reshape(BH, Cq), np.tile([N] + [0] * (Cq - 1), (BH, 1)))
+    assert to_np(pl.k_head).tolist() == [N] * BH
+    so = to_np(pl.sel_off)
+    assert so[-1] == BH * N
+    assert np.array_equal(to_np(pl.sel_idx[:BH * N]).reshape(BH, N), np.tile(np.arange(N), (BH, 1)))
+    grid = (w.T, w.Hg, w.Wg)
+    for bh in range(BH):
+        o = O.dense_head(q[bh], k[bh], v[bh], grid=grid, split=w.split, dtype=w.dtype, rope_base=w.rope_base)
+        mx, mn = assert_attention(out[bh], o["out"], w.dtype, f"{w.name} dense head {bh}")
+        say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
+
+
+@pytest.mark.parametrize("w", SMALL + LARGE[:2], ids=IDS + LARGE_IDS[:2])
+def test_full_dim_key_codebook_end_to_end(w):
+    """The cluster-level ablation proxy (SCOPE_FULL_DIM_KEYS): one key
+    codebook over all d channels; plan and attention against the oracle."""
+    say("full-dim keys", w.name)
+    heads = oracle_heads(w, full_dim_keys=True)
+    g = run_gpu(w, full_dim_keys=True)
+    assert g["status"][1] == 0 and g["status"][2] == 0
+    for bh, o in enumerate(heads):
+        assert g["seeds"][bh, 1, :w.Cm].tolist() == list(o["k_seeds"][0]), f"head {bh} key seeds"
+        assert not g["k_codes"][bh][:, 1:].any()
+    assert_plan_equal(w, g, heads)
+    for bh, o in enumerate(heads):
+        mx, mn = assert_attention(g["out"][bh], o["out"], w.dtype, f"{w.name} head {bh}")
+        say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")

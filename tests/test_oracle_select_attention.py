@@ -268,3 +268,49 @@ def test_cluster_permutation_is_stable_inside_each_cluster():
         assert len(off) == Cq + 1 and off[0] == 0 and off[-1] == N
         for c in range(Cq):
             assert perm[off[c]:off[c + 1]].tolist() == [i for i in range(N) if labels[i] == c]
+
+
+def test_dense_head_is_softmax_attention_over_all_keys():
+    """The dense-prefix oracle: RoPE'd rows (the same rounding as the sparse
+    path) and full softmax attention, against torch's fp64 attention on those
+    rows, and equal to the sparse path at rho = 1 (every key kept)."""
+    w = workloads.small("dn", 3, 4, 5, 64, (16, 24, 24), "bf16", 4, 5, H=1, iters=2)
+    q, k, v = workloads.generate(w)
+    d = O.dense_head(q[0], k[0], v[0], grid=(w.T, w.Hg, w.Wg), split=w.split, dtype=w.dtype)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(d["q_rope"])[None], torch.from_numpy(d["k_rope"])[None], torch.from_numpy(v[0])[None])
+    np.testing.assert_allclose(d["out"], ref[0].numpy(), rtol=1e-12, atol=1e-12)
+    full = O.workload_head(w, 0, q[0], k[0], v[0], rho=1.0)
+    np.testing.assert_array_equal(full["q_rope"], d["q_rope"])
+    np.testing.assert_allclose(full["out"], d["out"], rtol=0, atol=1e-13)
+
+
+# --- the full-dimensional key codebook (the cluster-level ablation proxy) ---
+
+def test_full_dim_proxy_is_exact_logit_when_every_key_is_its_own_centroid():
+    """Check (a) for the one-codebook proxy: with Cq = Cm = N every query and
+    key is its own centroid, so P[c, z_j] / sqrt(d) is the exact logit."""
+    w = workloads.small("fa", 2, 3, 4, 64, (16, 24, 24), "f32", 24, 24, H=1, iters=3)
+    q, k, v = workloads.generate(w)
+    r = O.workload_head(w, 0, q[0], k[0], v[0], full_dim_keys=True)
+    np.testing.assert_array_equal(np.sort(r["q_labels"]), np.arange(24))
+    np.testing.assert_array_equal(np.sort(r["k_codes"][:, 0]), np.arange(24))
+    assert not r["k_codes"][:, 1:].any() and not r["lut"][1:].any()
+    np.testing.assert_array_equal(r["k_centroids"][r["k_codes"][:, 0]], r["k_rope"])
+    exact = r["q_rope"] @ r["k_rope"].T / 8.0
+    np.testing.assert_allclose(r["scores"][r["q_labels"]], exact, rtol=1e-12, atol=1e-12)
+
+
+def test_full_dim_lut_is_the_inner_product_with_the_key_centroid():
+    """The one-term table: s[c, j] = <qbar_c, mu_{z_j}> / sqrt(d) computed
+    directly, and the key codebook is a k-means of whole key vectors (every
+    key nearest its own centroid over all d channels)."""
+    w = workloads.small("fb", 3, 4, 5, 128, (44, 42, 42), "bf16", 5, 7, H=1, iters=3)
+    q, k, v = workloads.generate(w)
+    r = O.workload_head(w, 0, q[0], k[0], v[0], full_dim_keys=True)
+    mu = r["k_centroids"][r["k_codes"][:, 0]]
+    direct = r["q_centroids"] @ mu.T / np.sqrt(128)
+    np.testing.assert_allclose(r["scores"], direct, rtol=1e-12, atol=1e-12)
+    Mr = O.round_bf16(r["k_centroids"])
+    dist = ((r["k_rope"][:, None, :] - Mr[None]) ** 2).sum(2)
+    np.testing.assert_array_equal(r["k_codes"][:, 0], np.argmin(dist, 1))
