@@ -188,6 +188,21 @@ scope_status scope_plan_timed(const scope_params* p, const void* q, const void* 
                               void* k_rope, scope_plan_t* plan, void* ws, size_t ws_bytes,
                               const hipEvent_t* stage_events, int n_events, hipStream_t stream);
 
+/* scope_plan without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Its scratch memory is one fixed array of
+ * SCOPE_NOALLOC_MAX_WORKSPACE bytes inside the library, one per GPU (each GPU
+ * the library runs on holds it until the process ends); no call allocates or
+ * frees memory.  Same arguments, results and errors as scope_plan, plus
+ * SCOPE_ERR_WORKSPACE (before any launch) when scope_workspace_size() of the
+ * parameters exceeds SCOPE_NOALLOC_MAX_WORKSPACE.  Every call on one GPU
+ * shares that GPU's array, so calls that overlap in time on one GPU (other
+ * streams, other threads) race and must not be issued; calls in stream order
+ * are fine (each call initialises what it reads). */
+#define SCOPE_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+scope_status scope_plan_noalloc(const scope_params* p, const void* q, const void* k, void* q_rope,
+                                void* k_rope, scope_plan_t* plan, hipStream_t stream);
+
 /* Rebuilds plan->work and plan->status[0] from perm_q/q_off/counts_r/sel_off
  * for a plan whose CSR was written by the caller (for instance copied from
  * another implementation).  scope_plan already does this. */

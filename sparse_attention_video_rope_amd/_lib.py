@@ -73,6 +73,8 @@ def load():
         lib.scope_workspace_size.restype = c_int32
         lib.scope_plan.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, PL, c_void_p, c_size_t, c_void_p]
         lib.scope_plan.restype = c_int32
+        lib.scope_plan_noalloc.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, PL, c_void_p]
+        lib.scope_plan_noalloc.restype = c_int32
         lib.scope_plan_timed.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, PL, c_void_p, c_size_t,
                                          ctypes.POINTER(c_void_p), c_int32, c_void_p]
         lib.scope_plan_timed.restype = c_int32
@@ -143,10 +145,11 @@ class Plan:
     """Caller-owned device buffers of one plan (torch tensors) plus the C struct."""
 
     def __init__(self, p: Params, device="cuda", debug: bool = True, sel_capacity: Optional[int] = None,
-                 norm_bound: bool = True, centroids: Optional[bool] = None):
+                 norm_bound: bool = True, centroids: Optional[bool] = None, workspace: bool = True):
         """debug: also keep labels, codes, seeds and LUT; centroids (default:
         debug): keep the final centroids, which a later plan can start from
-        with SCOPE_USE_INIT_CENTROIDS."""
+        with SCOPE_USE_INIT_CENTROIDS; workspace=False: no workspace (for
+        plan_noalloc only)."""
         import torch
         ws, sel_worst, work_cap = sizes(p)
         BH, N, Cq, Cm, d = p.BH, p.N, p.Cq, p.Cm, p.d
@@ -165,7 +168,7 @@ class Plan:
         self.status = torch.zeros(4, **i32)
         # per-head bound of ||k'|| (lets scope_attend drop the running softmax maximum); None: not provided
         self.k_norm_max = torch.zeros(BH, dtype=torch.float32, device=device) if norm_bound else None
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(ws if workspace else 0, dtype=torch.uint8, device=device)
         self.debug = debug
         self.q_centroids = self.k_centroids = None
         if debug if centroids is None else centroids:
@@ -211,6 +214,21 @@ def plan(p: Params, q, k, pl: Optional[Plan] = None, q_rope=None, k_rope=None):
                            ctypes.byref(pl.struct), pl.workspace.data_ptr(), pl.workspace.numel(), _stream())
     if st:
         raise ScopeError(st, "scope_plan")
+    return q_rope, k_rope, pl
+
+
+NOALLOC_MAX_WORKSPACE = 64 << 20       # SCOPE_NOALLOC_MAX_WORKSPACE of include/scope.h
+
+
+def plan_noalloc(p: Params, q, k, pl: Plan, q_rope, k_rope):
+    """scope_plan_noalloc: the plan in the library's fixed per-GPU scratch
+    array (no workspace; the caller still passes every input and output)."""
+    _check_tensor(q, p, "q")
+    _check_tensor(k, p, "k")
+    st = load().scope_plan_noalloc(ctypes.byref(p), q.data_ptr(), k.data_ptr(), q_rope.data_ptr(),
+                                   k_rope.data_ptr(), ctypes.byref(pl.struct), _stream())
+    if st:
+        raise ScopeError(st, "scope_plan_noalloc")
     return q_rope, k_rope, pl
 
 

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "scope_internal.hpp"
 
 namespace scope {
@@ -252,9 +254,46 @@ static scope_status plan_impl(const scope_params* p, const void* q, const void* 
   return SCOPE_OK;
 }
 
+// ---- workspace of the no-allocation entry point ------------------------------
+// One fixed array per GPU, in the library's code object (each device that
+// loads the library holds its own copy until the process ends).  Host code
+// never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static_assert(SCOPE_NOALLOC_MAX_WORKSPACE % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[SCOPE_NOALLOC_MAX_WORKSPACE];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static scope_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SCOPE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SCOPE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SCOPE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SCOPE_OK;
+}
+
 }  // namespace scope
 
 extern "C" {
+
+scope_status scope_plan_noalloc(const scope_params* p, const void* q, const void* k, void* q_rope, void* k_rope,
+                                scope_plan_t* plan, hipStream_t stream) {
+  const scope_status st = validate(p);
+  if (st != SCOPE_OK) return st;
+  if (carve(make_geo(*p), nullptr, nullptr).bytes > SCOPE_NOALLOC_MAX_WORKSPACE) return SCOPE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const scope_status sst = scratch_of_current_device(&ws);
+  if (sst != SCOPE_OK) return sst;
+  return plan_impl(p, q, k, q_rope, k_rope, plan, ws, SCOPE_NOALLOC_MAX_WORKSPACE, nullptr, 0, stream);
+}
 
 scope_status scope_plan(const scope_params* p, const void* q, const void* k, void* q_rope, void* k_rope,
                         scope_plan_t* plan, void* ws, size_t ws_bytes, hipStream_t stream) {

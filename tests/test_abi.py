@@ -22,7 +22,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = sav.load()
     names = declared_symbols()
-    assert names == ["scope_attend", "scope_plan", "scope_plan_finalize", "scope_plan_timed",
+    assert names == ["scope_attend", "scope_plan", "scope_plan_finalize", "scope_plan_noalloc", "scope_plan_timed",
                      "scope_status_string", "scope_workspace_size"]
     for n in names:
         assert hasattr(lib, n), n
@@ -182,3 +182,15 @@ def test_plan_timed_rejects_bad_event_arrays_before_launch():
     st = lib.scope_plan_timed(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(plan), fake, 16, ev, 5, None)
     assert st == 3                     # the workspace check comes first, as in scope_plan
 
+
+def test_plan_noalloc_rejects_parameters_beyond_its_scratch_before_launch():
+    """The no-allocation entry point: a parameter set whose workspace exceeds
+    the fixed scratch array is refused with SCOPE_ERR_WORKSPACE before any HIP
+    call; invalid parameters still give SCOPE_ERR_INVALID."""
+    lib = sav.load()
+    big = good(H=40, T=21, Hg=45, Wg=80, d=128, split=(44, 42, 42), Cq=300, Cm=333)
+    assert sav.sizes(big)[0] > _lib.NOALLOC_MAX_WORKSPACE
+    plan = _lib.PlanStruct()
+    assert lib.scope_plan_noalloc(ctypes.byref(big), None, None, None, None, ctypes.byref(plan), None) == 3
+    assert lib.scope_plan_noalloc(ctypes.byref(good(rho=0.0)), None, None, None, None, ctypes.byref(plan), None) == 1
+    assert sav.sizes(good())[0] <= _lib.NOALLOC_MAX_WORKSPACE
