@@ -56,7 +56,8 @@ def parse():
                          "--full-cm centroids")
     ap.add_argument("--full-cm", type=int, default=None,
                     help="--partition full: key centroids of the one codebook (default 3 Cm, the centroid budget "
-                         "of the three subspace codebooks, at most 1024)")
+                         "of the three subspace codebooks, lowered to the largest the library supports: its "
+                         "bf16 table must fit in one CU's LDS)")
     ap.add_argument("--heads", type=int, default=None,
                     help="--fidelity: run only the first H heads of the workload (sampled heads at the 720p sizes)")
     ap.add_argument("--selection", choices=("scope", "fixed-topk"), default="scope",
@@ -449,8 +450,15 @@ def fidelity(a):
     res = {rho: {k: [] for k in keys} for rho in FID_RHOS}
     extra = {}
     if a.partition == "full":
-        w0 = w0.with_(Cm=a.full_cm or min(1024, 3 * w0.Cm))
         extra = {"full_dim_keys": True}
+        cm = a.full_cm or min(1024, 3 * w0.Cm)
+        while cm > 32:     # the largest supported codebook up to the request (LDS holds its table)
+            try:
+                sav.sizes(sav.params_for(w0.with_(Cm=cm), **extra))
+                break
+            except sav.ScopeError:
+                cm -= 32 if cm % 32 == 0 else cm % 32
+        w0 = w0.with_(Cm=cm)
     if a.heads:
         w0 = w0.with_(H=min(a.heads, w0.H))
     for rep in range(FID_REPS):

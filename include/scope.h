@@ -35,7 +35,11 @@
  *     iters outside 0..1000, rope_base <= 1, rho outside (0, 1], alpha
  *     outside [0, 1], an unknown dtype or flag, a null or misaligned pointer.
  *     SCOPE_ERR_UNSUPPORTED: d not in {64, 128}, N > 262144, Cq or Cm above
- *     1024, B*H > 65535.
+ *     1024, B*H > 65535, and in bf16 runs a centroid table larger than the
+ *     160 KB LDS of a CU: ceil32(C) * (ceil16(d_m) + 8) * 2 + ceil32(C) * 4
+ *     + 4096 bytes for any clustering (C = Cq with d_m = d for the queries,
+ *     C = Cm with the subspace width, or d with SCOPE_FULL_DIM_KEYS, for the
+ *     keys); at d = 128 that allows up to 576 centroids.
  *   - Calls that overlap in time must use distinct workspaces and plans.
  */
 #ifndef SCOPE_H

@@ -13,6 +13,8 @@
 // O^T += V^T P^T, whose V^T operand comes from transposing LDS reads.
 #include <float.h>
 
+#include <type_traits>
+
 #include "scope_device.hpp"
 #include "scope_internal.hpp"
 
@@ -221,8 +223,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   // fixed (wave-uniform): the softmax reference mref is final, no running
   // maximum is kept; see the switch after the first chunk below
   bool fixed = false;
-  auto step = [&](int kc, lds_u16* Kc, lds_u16* Vc, lds_u16* Kn, lds_u16* Vn) {
-    if (kc + 1 < nchunks) {
+  // FAST: a chunk that is neither the first nor the last, on a wave whose
+  // softmax reference is fixed: no key mask, no running maximum, the next
+  // chunk exists.  Without the branches of the general step, the compiler can
+  // interleave the exponentials of one 32-key subtile with the QK^T MFMAs of
+  // the other.
+  auto step = [&](auto fast_c, int kc, lds_u16* Kc, lds_u16* Vc, lds_u16* Kn, lds_u16* Vn) {
+    constexpr bool FAST = decltype(fast_c)::value;
+    if (FAST || kc + 1 < nchunks) {
       gather(Kn, Vn);                              // rows of chunk kc+1
       load_idx(min(kc + 2, nchunks - 1));          // indices of chunk kc+2
     }
@@ -233,12 +241,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         bf16x8_t ak[D / 16];
 #pragma unroll
         for (int kb = 0; kb < D / 16; ++kb) ak[kb] = *(const lds_bf16x8*)(Kc + kro[kb] + st * 32 * D);
+        // keep the subtile's K reads above its MFMA chain: issued together,
+        // only the first read's latency is waited for
+        __builtin_amdgcn_sched_barrier(0);
         s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], qb[0], cneg, 0, 0, 0);
 #pragma unroll
         for (int kb = 1; kb < D / 16; ++kb) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kb], qb[kb], s[st], 0, 0, 0);
       }
       const int kleft = r - kc * BN;
-      if (kleft < BN) {
+      if (!FAST && kleft < BN) {
         // key offset of this lane's rows, made opaque here so that the 32 key
         // positions are formed in this (last-chunk) branch instead of being
         // kept live in registers across the loop
@@ -250,7 +261,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           for (int v = 0; v < 16; ++v)
             if (st * 32 + 8 * (v >> 2) + (v & 3) + k4 >= kleft) s[st][v] = -__builtin_inff();
       }
-      if (!fixed) {
+      if (!FAST && !fixed) {
         // running maximum: s holds logits minus mref; the first chunk sets
         // the reference to its maximum, a later one raises it when its
         // maximum exceeds it by more than RESCALE_LOG2
@@ -350,10 +361,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       for (int v = 0; v < 16; ++v) cneg[v] = -mref;
     }
   };
-  for (int kc = 0; kc < nchunks; kc += 2) {
-    step(kc, K0, V0, K1, V1);
-    if (kc == 0) decide();
-    if (kc + 1 < nchunks) step(kc + 1, K1, V1, K0, V0);
+  const std::false_type general{};
+  const std::true_type fast{};
+  int kc = 1;
+  if (nchunks > 0) {
+    step(general, 0, K0, V0, K1, V1);
+    decide();
+    // middle chunks (two per iteration: chunk kc reads buffer 1, kc + 1
+    // buffer 0); a wave-uniform choice of the loop, made once
+    if (fixed && __builtin_amdgcn_readfirstlane((int)fixed)) {
+      for (; kc + 2 < nchunks; kc += 2) {
+        step(fast, kc, K1, V1, K0, V0);
+        step(fast, kc + 1, K0, V0, K1, V1);
+      }
+    } else {
+      for (; kc + 2 < nchunks; kc += 2) {
+        step(general, kc, K1, V1, K0, V0);
+        step(general, kc + 1, K0, V0, K1, V1);
+      }
+    }
+    // the last one or two chunks (the last may be partial)
+    for (; kc < nchunks; ++kc) {
+      if (kc & 1) step(general, kc, K1, V1, K0, V0);
+      else step(general, kc, K0, V0, K1, V1);
+    }
   }
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (!qvalid) return;

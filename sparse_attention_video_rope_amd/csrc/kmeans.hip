@@ -116,8 +116,10 @@ struct SeedSync {
   char* base;        // [BH][4] areas of SEED_SYNC_BYTES: counter, drawn index, part[2][32], lowest[MAX_C]
   int32_t* abort;    // set when a wait ran out (every later wait is then skipped)
   int Wq, Wk;        // workgroups per query / key clustering (1 and 1: no exchange)
-  int flat;          // 1: blockIdx.x enumerates the BH*Wq query workgroups, then the
-                     // 3*BH*Wk key workgroups; 0: grid (BH, 4) with one each
+  int flat;          // 1: blockIdx.x enumerates the nbh*Wq query workgroups, then the
+                     // nk*nbh*Wk key workgroups of heads bh0 .. bh0+nbh-1; 0: grid (BH, 1+nk)
+                     // with one each
+  int bh0, nbh;      // heads of this launch (flat)
 };
 
 __global__ void seed_sync_init_kernel(char* base, int chains, int32_t* abort) {
@@ -136,13 +138,14 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
                                                        float* __restrict__ kcent, SeedSync sy) {
   int m = blockIdx.y, bh = blockIdx.x, wg = 0;
   if (sy.flat) {
-    const int b = blockIdx.x, nq = g.BH * sy.Wq;
+    const int b = blockIdx.x, nq = sy.nbh * sy.Wq;
     if (b < nq) {
       m = 0; bh = b / sy.Wq; wg = b - bh * sy.Wq;
     } else {
       const int c = (b - nq) / sy.Wk;
       wg = (b - nq) - c * sy.Wk; bh = c / g.nk; m = 1 + (c - bh * g.nk);
     }
+    bh += sy.bh0;
   }
   const int W = m == 0 ? sy.Wq : sy.Wk;
   const int N = g.N, d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m];
@@ -957,13 +960,14 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
                                                       float* __restrict__ qcent, float* __restrict__ kcent, SeedSync sy) {
   int m = blockIdx.y, bh = blockIdx.x, wg = 0;
   if (sy.flat) {
-    const int b = blockIdx.x, nq = g.BH * sy.Wq;
+    const int b = blockIdx.x, nq = sy.nbh * sy.Wq;
     if (b < nq) {
       m = 0; bh = b / sy.Wq; wg = b - bh * sy.Wq;
     } else {
       const int c = (b - nq) / sy.Wk;
       wg = (b - nq) - c * sy.Wk; bh = c / g.nk; m = 1 + (c - bh * g.nk);
     }
+    bh += sy.bh0;
   }
   // W workgroups share the clustering: this one owns the points
   // [pbase, pbase + N) (local indices below; drawn centres are global)
@@ -2036,6 +2040,8 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
       sy.Wq = Wq;
       sy.Wk = Wk;
       sy.flat = 1;
+      sy.bh0 = 0;
+      sy.nbh = g.BH;
       const uint16_t* q16 = (const uint16_t*)qr;
       const uint16_t* k16 = (const uint16_t*)kr;
       double* d2 = w.d2;
@@ -2077,38 +2083,46 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
     return;
   }
   const size_t lds = (size_t)SEED_NW * SEED_LIST * 12 + cache;
-  // Several workgroups per clustering when the chip holds them all at once
-  // (a cooperative launch guarantees that, or fails and one is used).
-  const auto kern = seed_kernel<T, false>;
-  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int chains = g.BH * ncl;
   const int G = ((g.N + SEED_NT - 1) / SEED_NT + SEED_RG - 1) / SEED_RG;
-  // bf16 data only (fp32 data keeps one workgroup per clustering): the running
-  // sum then adds the workgroups' partial sums in range order, a fixed order,
-  // so the draws are reproducible; only the rounding of the sums changes
-  // The slots left after every clustering has Wk go to the query clusterings
-  // (the widest rows).
-  int Wq = 1, Wk = 1, dev = 0, ncu = 0, coop = 0, per_cu = 0;
-  if (sizeof(T) == 2 && hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-      hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, SEED_NT, lds) == hipSuccess) {
-    const int cap = ncu * per_cu;
-    Wk = max(1, min(G, cap / chains));
-    Wq = max(Wk, min(G, (cap - g.nk * g.BH * Wk) / g.BH));
-  }
   seed_sync_init_kernel<<<g.BH * 4, 256, 0, s>>>(w.seed_sync, g.BH * 4, status + 2);   // areas (bh, m) for all 4 m
-  SeedSync sy;
-  sy.base = w.seed_sync;
-  sy.abort = status + 2;
-  sy.Wq = Wq;
-  sy.Wk = Wk;
-  sy.flat = 1;
   double* d2 = w.d2;
   uint16_t* nr = reinterpret_cast<uint16_t*>(w.nearest);
   int32_t* sd = w.seeds;
   float* qc = w.qcent;
   float* kc = w.kcent;
+  int dev = 0, ncu = 0, coop = 0;
+  const bool can_coop = sizeof(T) == 2 && hipGetDevice(&dev) == hipSuccess &&
+                        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop;
+  SeedSync sy;
+  sy.base = w.seed_sync;
+  sy.abort = status + 2;
+  // bf16 data only (fp32 data keeps one workgroup per clustering): the running
+  // sum then adds the workgroups' partial sums in range order, a fixed order,
+  // so the draws are reproducible; only the rounding of the sums changes.
+  //
+  // Several workgroups per clustering when the chip holds them all at once
+  // (a cooperative launch guarantees that, or fails and one is used), with
+  // the point state in global memory.  The slots left after every clustering
+  // has Wk go to the query clusterings (the widest rows).  (One workgroup per
+  // 8192-point group with the state in registers, in launches of a few heads
+  // whose rows stay in the Infinity Cache, measured 103.7 ms instead of
+  // 56.8 ms at the Hunyuan-like size: the exchange among 15 workgroups per
+  // draw and the six sequential launches cost more than the state traffic.)
+  const auto kern = seed_kernel<T, false>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  int Wq = 1, Wk = 1, per_cu = 0;
+  if (can_coop && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, SEED_NT, lds) == hipSuccess) {
+    const int cap = ncu * per_cu;
+    Wk = max(1, min(G, cap / chains));
+    Wq = max(Wk, min(G, (cap - g.nk * g.BH * Wk) / g.BH));
+  }
+  sy.Wq = Wq;
+  sy.Wk = Wk;
+  sy.flat = 1;
+  sy.bh0 = 0;
+  sy.nbh = g.BH;
   if (Wq > 1 || Wk > 1) {
     void* args[] = {(void*)&qr, (void*)&kr, (void*)&g, (void*)&d2, (void*)&nr, (void*)&sd, (void*)&qc, (void*)&kc,
                     (void*)&sy};

@@ -120,6 +120,15 @@ static scope_status validate(const scope_params* p) {
     return SCOPE_ERR_INVALID;
   if ((p->flags & SCOPE_DENSE) && p->flags != SCOPE_DENSE) return SCOPE_ERR_INVALID;
   if ((p->flags & SCOPE_FULL_DIM_KEYS) && (p->flags & SCOPE_PERMUTE_CHANNELS)) return SCOPE_ERR_INVALID;
+  if (p->dtype == SCOPE_BF16 && !(p->flags & SCOPE_DENSE)) {
+    // the bf16 assignment keeps a clustering's whole centroid table in the
+    // LDS of one CU (bf16 rows padded to 16 channels + 8, fp32 norms, and at
+    // least 4 waves' 1 KB refinement rows)
+    const Geo g = make_geo(*p);
+    for (int m = 0; m <= g.nk; ++m)
+      if ((size_t)g.Cpad[m] * (g.dpad[m] + 8) * 2 + (size_t)g.Cpad[m] * 4 + 4 * 1024 > MAX_ASSIGN_LDS)
+        return SCOPE_ERR_UNSUPPORTED;
+  }
   if (p->flags & SCOPE_PERMUTE_CHANNELS) {
     bool seen[128] = {};
     for (int i = 0; i < p->d; ++i) {

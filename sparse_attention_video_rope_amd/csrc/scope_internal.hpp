@@ -16,6 +16,7 @@ constexpr int MAX_C = 1024;     // largest Cq / Cm supported
 // per-clustering exchange area of the k-means++ kernel when one clustering
 // spans several workgroups: counter, drawn index, 2 x 32 partial sums, MAX_C minima
 constexpr int SEED_SYNC_BYTES = 8 + 2 * 8 * 32 + 4 * MAX_C;
+constexpr size_t MAX_ASSIGN_LDS = 160 * 1024;   // LDS of one CU: holds a clustering's bf16 centroid table
 constexpr int MAX_N = 1 << 18;  // largest token count supported (16 groups of 16 rounds of 1024)
 
 // Geometry of the four clusterings of a head: 0 = queries (full d),

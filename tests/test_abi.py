@@ -72,6 +72,8 @@ def good(**kw):
     (dict(d=96, split=(32, 32, 32)), 2),      # unsupported head dim
     (dict(Cq=0), 1), (dict(Cm=257), 1),       # Cm > N
     (dict(Cq=300, T=8, Hg=16, Wg=16, Cm=2000), 2),   # beyond the supported cluster count
+    (dict(Cq=600, T=8, Hg=16, Wg=16, d=128, split=(44, 42, 42)), 2),   # query table beyond one CU's LDS
+    (dict(Cq=8, Cm=999, T=8, Hg=16, Wg=16, d=128, split=(44, 42, 42), full_dim_keys=True), 2),
     (dict(rho=0.0), 1), (dict(rho=1.5), 1), (dict(alpha=-0.1), 1),
     (dict(iters=-1), 1), (dict(rope_base=1.0), 1),
 ])
@@ -194,3 +196,19 @@ def test_plan_noalloc_rejects_parameters_beyond_its_scratch_before_launch():
     assert lib.scope_plan_noalloc(ctypes.byref(big), None, None, None, None, ctypes.byref(plan), None) == 3
     assert lib.scope_plan_noalloc(ctypes.byref(good(rho=0.0)), None, None, None, None, ctypes.byref(plan), None) == 1
     assert sav.sizes(good())[0] <= _lib.NOALLOC_MAX_WORKSPACE
+
+
+def test_largest_supported_centroid_tables():
+    """The bf16 centroid table of a clustering must fit in one CU's LDS: 576
+    centroids of 128 channels do, 577 do not; fp32 runs take no table."""
+    lib = sav.load()
+    kw = dict(T=8, Hg=16, Wg=16, d=128, split=(44, 42, 42))
+    for cq, code in ((576, 0), (577, 2)):
+        p = good(Cq=cq, **kw)
+        assert lib.scope_workspace_size(ctypes.byref(p), None, None, None) == code
+        p = good(Cq=8, Cm=cq, full_dim_keys=True, **kw)
+        assert lib.scope_workspace_size(ctypes.byref(p), None, None, None) == code
+    p = good(Cq=1000, dtype="f32", **kw)
+    assert lib.scope_workspace_size(ctypes.byref(p), None, None, None) == 0
+    p = good(Cq=1024, Cm=1024, T=16, Hg=16, Wg=16)        # d = 64: 1024-centroid tables fit
+    assert lib.scope_workspace_size(ctypes.byref(p), None, None, None) == 0
