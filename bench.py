@@ -69,6 +69,7 @@ def parse():
     ap.add_argument("--dense-steps", type=float, default=None,
                     help="fraction of denoising steps run dense (default: 0.2 for the Wan-like workloads, "
                          "0.1 otherwise, as the pages give for Wan and HunyuanVideo)")
+    ap.add_argument("--no-dense-prefix", action="store_true", help="leave out the dense-prefix measurement")
     ap.add_argument("--warm-iters", type=int, default=2,
                     help="Lloyd iterations of the warm-started plan (negative: skip the warm-start measurement)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attend_traffic.json"),
@@ -590,7 +591,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "wall_s": round(wall, 3),
     }
-    line["dense_prefix"] = dense_prefix(a, w, qd, kd, vd, sav, torch, ms)
+    if not a.no_dense_prefix:
+        line["dense_prefix"] = dense_prefix(a, w, qd, kd, vd, sav, torch, ms)
     if a.warm_iters >= 0:
         line["warm_start"] = warm_start(a, w, rho, qd, kd, vd, sav, torch)
     if not a.no_cpu_baseline:

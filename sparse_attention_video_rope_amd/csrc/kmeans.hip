@@ -1350,7 +1350,13 @@ __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict
     // every run)
     if (tflag[tid]) {
       double acc = 0.0;
-      for (int k = 0; k < nk; ++k) acc += D2g[p0 + k];
+      for (int k0 = 0; k0 < nk; k0 += 8) {
+        double v[8];   // eight loads in flight, added in slot order
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = k0 + u < nk ? D2g[p0 + k0 + u] : 0.0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+      }
       tsum[tid] = acc;
       tflag[tid] = 0;
     }
@@ -1598,10 +1604,14 @@ __global__ __launch_bounds__(ACC_NT) void accum_kernel(const T* __restrict__ qr,
 // subtracts them from its old one; the sizes change by one each.  Same grid
 // and LDS table as accum_kernel; the nonzero entries of the table are then
 // added to the totals in global memory (fp64 atomics; exact, so in any
-// order).  A wave takes 64 points at a time (their labels loaded one step
-// ahead), lists the changed ones (lane numbers, in LDS) and loads their rows
-// in batches of 8 instructions (64 / SW points each: lanes = channels) before
-// adding them.
+// order).  The workgroup takes its points in segments of DELTA_PPT per thread
+// (all labels of a segment in flight at once), lists the changed ones in LDS and
+// then loads their rows in batches of 8 instructions per wave (64 / SW points
+// each: lanes = channels) before adding them (the previous version took 64
+// points per wave and step, with the labels one step ahead: 454 us per pass
+// at the Hunyuan-like size, bound by that chain of label loads).
+constexpr int DELTA_PPT = 4;                   // points per thread and segment of accum_delta_kernel
+constexpr int DELTA_SEG = ACC_NT * DELTA_PPT;   // 16 KB of LDS lists (the LDS table's limit counts them)
 template <int SW>
 __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __restrict__ qr,
                                                              const uint16_t* __restrict__ kr, Geo g,
@@ -1618,7 +1628,9 @@ __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __r
   extern __shared__ __align__(16) unsigned char acc_smem[];
   double* S = reinterpret_cast<double*>(acc_smem);                         // [C][SW]
   int32_t* cnt = reinterpret_cast<int32_t*>(acc_smem + (size_t)C * SW * 8);  // [C]
-  __shared__ int32_t wlist[ACC_NT / 64][64];
+  __shared__ int32_t dpt[DELTA_SEG];    // changed points of a segment
+  __shared__ int32_t dlab[DELTA_SEG];   // their new label | old label << 16
+  __shared__ int32_t dcount;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i < C * SW; i += ACC_NT) S[i] = 0.0;
   for (int i = tid; i < C; i += ACC_NT) cnt[i] = 0;
@@ -1631,23 +1643,40 @@ __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __r
   constexpr int G = 64 / SW, U = 8;
   const int j = lane / SW, ch = lane % SW;
   const bool chv = ch < sw;
-  int Ln_ = lab[min(p0 + wv * 64 + lane, N - 1)], Lp_ = prv[min(p0 + wv * 64 + lane, N - 1)];
-  for (int c0 = p0 + wv * 64; c0 < p1; c0 += ACC_NT) {
-    const int p = c0 + lane;
-    const bool ok = p < p1;
-    const int L = min(max(Ln_, 0), C - 1), Lp = min(max(Lp_, 0), C - 1);
-    // labels of the next 64 points, in flight during this step
-    Ln_ = lab[min(c0 + ACC_NT + lane, N - 1)];
-    Lp_ = prv[min(c0 + ACC_NT + lane, N - 1)];
-    const bool c = ok && L != Lp;
-    const uint64_t mk = __ballot(c);
-    const int nchg = (int)__popcll(mk);
-    if (nchg == 0) continue;
-    if (c) wlist[wv][__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = lane;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int b = 0; b < nchg; b += U * G) {
+  // Segments of DELTA_PPT points per thread: every thread loads its labels at
+  // once, the changed points go to an LDS list (point, new | old << 16), and
+  // then all waves add their rows (G points per instruction, U instructions
+  // in flight).  The list order depends on timing, but the sums are exact.
+  for (int seg = p0; seg < p1; seg += DELTA_SEG) {
+    if (tid == 0) dcount = 0;
+    __syncthreads();
+    int Ln[DELTA_PPT], Lp[DELTA_PPT];
+#pragma unroll
+    for (int u = 0; u < DELTA_PPT; ++u) {
+      const int p = seg + u * ACC_NT + tid;
+      const bool ok = p < p1;
+      Ln[u] = ok ? lab[p] : 0;
+      Lp[u] = ok ? prv[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < DELTA_PPT; ++u) {
+      const int p = seg + u * ACC_NT + tid;
+      const bool c = p < p1 && Ln[u] != Lp[u];
+      const uint64_t mk = __ballot(c);
+      if (mk == 0) continue;
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&dcount, (int)__popcll(mk));
+      base = __shfl(base, 0);
+      if (c) {
+        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+        dpt[pos] = p;
+        dlab[pos] = min(max(Ln[u], 0), C - 1) | (min(max(Lp[u], 0), C - 1) << 16);
+      }
+    }
+    __syncthreads();
+    const int nchg = dcount;
+    for (int b = wv * U * G; b < nchg; b += (ACC_NT / 64) * U * G) {
       float xv[U];
       int ln[U], lo[U];
       bool vv[U];
@@ -1655,10 +1684,11 @@ __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __r
       for (int u = 0; u < U; ++u) {
         const int idx = b + u * G + j;
         vv[u] = idx < nchg;
-        const int q = vv[u] ? wlist[wv][idx] : 0;
-        ln[u] = __shfl(L, q);
-        lo[u] = __shfl(Lp, q);
-        xv[u] = (vv[u] && chv) ? bf16_to_f32(X[(size_t)(c0 + q) * d + ch]) : 0.f;
+        const int pt = vv[u] ? dpt[idx] : 0;
+        const int lb = vv[u] ? dlab[idx] : 0;
+        ln[u] = lb & 0xFFFF;
+        lo[u] = lb >> 16;
+        xv[u] = (vv[u] && chv) ? bf16_to_f32(X[(size_t)pt * d + ch]) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -1678,10 +1708,7 @@ __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __r
         }
       }
     }
-    // the list is rewritten for the next 64 points
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __syncthreads();   // the list is rewritten by the next segment
   }
   __syncthreads();
   double* st = stot + ((size_t)bh * 4 + m) * g.Cmax * d + s0;

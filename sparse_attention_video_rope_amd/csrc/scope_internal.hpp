@@ -85,8 +85,9 @@ struct Workspace {
 inline int att_chunk(const Geo&) { return ATT_BM; }
 // Lloyd update layout: channel slices of acc_sw channels, acc_parts point
 // ranges per (head, clustering).  Slices are 32 channels wide unless the
-// per-cluster sums of that width would not fit in LDS.
-inline int acc_sw(const Geo& g) { return g.Cmax <= 600 ? 32 : 16; }
+// per-cluster sums of that width (Cmax x 32 fp64 plus the counts, beside the
+// 16 KB of lists of the delta update) would not fit in the 160 KB LDS.
+inline int acc_sw(const Geo& g) { return g.Cmax <= 544 ? 32 : 16; }
 inline int acc_slices(const Geo& g) { return (g.d + acc_sw(g) - 1) / acc_sw(g); }
 inline int acc_parts(const Geo& g) {
   const int p = (g.N + 4095) / 4096;

@@ -26,6 +26,8 @@ SMALL = [
     # 300 query clusters at d = 128: the query assignment's centroid table
     # fills a CU's LDS, so the key clusterings are assigned in a launch of their own
     workloads.small("s128c", 3, 10, 12, 128, (44, 42, 42), "bf16", 300, 60, index=112),
+    # 600 query clusters: the centroid updates take 16-channel slices
+    workloads.small("s64c", 4, 20, 24, 64, (16, 24, 24), "bf16", 600, 40, H=1, index=114),
 ]
 IDS = [w.name for w in SMALL]
 
