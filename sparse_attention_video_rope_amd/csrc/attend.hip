@@ -3,9 +3,9 @@
 // proxies (SCOPE abstract):
 //   o_i = sum_{j in S_c(i)} softmax_j(<q'_i, k'_j> / sqrt(d)) v_j.
 //
-// bf16 path (gfx950, wave64): one workgroup of 4 waves per (cluster, 128-query
-// chunk) work item; each wave owns 32 queries whose Q rows stay in registers
-// as MFMA operands.  The selected keys' K and V rows are gathered 64 at a time
+// bf16 path (gfx950, wave64): one workgroup of NW waves per (cluster, 32 NW-query
+// chunk) work item (NW = 8 at head dim 128, 4 at 64); each wave owns 32 queries
+// whose Q rows stay in registers as MFMA operands.  The selected keys' K and V rows are gathered 64 at a time
 // straight into LDS (row-major, double buffered).  Per 32-key subtile the wave
 // computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so each lane holds 16
 // logits of one query: the online-softmax max and sum need one cross-lane
@@ -29,16 +29,23 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Work item of this workgroup, or -1 (items past the device-side count exit).
-// Workgroups are dispatched to the 8 XCDs round-robin by block index, and
-// each XCD has its own L2.  Block b takes item (b mod 8) * per + b / 8, so
-// every XCD works through one contiguous eighth of the work list in list
-// order: the items of one cluster (adjacent in the list, same key set) run
-// at the same time on one XCD and share its L2 for their K / V gathers.
-// The grid is a multiple of 8 and covers 8 * per (per = ceil(n_work / 8)).
+// Workgroups are dispatched to the 8 XCDs round-robin by block index; each
+// XCD has its own L2, and the 256 MB Infinity Cache behind them is shared.
+// The work list runs in (head, cluster, chunk) order and is cut into runs of
+// ATT_RUN consecutive items; the runs go to the XCDs in turn, and XCD x takes
+// its runs in list order (block b: k = b / 8 on XCD b mod 8, item
+// (k / ATT_RUN * 8 + x) * ATT_RUN + k mod ATT_RUN).  So all XCDs work on the
+// same stretch of the list, whose K / V rows (one head, 61 MB at the
+// Hunyuan-like size) stay in the Infinity Cache, and the items of one cluster
+// (same key set, adjacent in the list) mostly start together on one XCD and
+// share its L2.  Giving each XCD one contiguous eighth of the list instead
+// puts eight heads' K / V in flight at once; at the Hunyuan-like size that
+// launch took 149 ms instead of 136 ms.  The grid is a multiple of 8 ATT_RUN.
+constexpr int ATT_RUN = 8;
 __device__ __forceinline__ int att_item(int n_work) {
-  const int b = blockIdx.x, per = (n_work + 7) >> 3;
-  const int item = (b & 7) * per + (b >> 3);
-  return (b >> 3) < per && item < n_work ? item : -1;
+  const int b = blockIdx.x, x = b & 7, k = b >> 3;
+  const int item = ((k / ATT_RUN) * 8 + x) * ATT_RUN + k % ATT_RUN;
+  return item < n_work ? item : -1;
 }
 
 struct AttArgs {
@@ -78,16 +85,14 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const lds_u16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 
-template <int D, int WPE, int BN = 64>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void attend_bf16_lds_kernel(
+template <int D, int WPE, int NW, int BN = 64>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) void attend_bf16_lds_kernel(
     AttArgs a, const int32_t* __restrict__ work, const int32_t* __restrict__ status,
     const int32_t* __restrict__ perm_q, const int32_t* __restrict__ q_off, const int32_t* __restrict__ cr,
     const int64_t* __restrict__ sel_off, const int32_t* __restrict__ sel_idx, const float* __restrict__ knm,
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vv,
     uint16_t* __restrict__ out) {
-  constexpr int NW = 4;
-  constexpr int BM = 32 * NW;
-  static_assert(BM == ATT_BM, "queries per workgroup must equal the work-list chunk");
+  constexpr int BM = 32 * NW;                // queries per work item (the work-list chunk)
   constexpr int NST = BN / 32;               // 32-key MFMA row blocks per chunk
   constexpr int PR = D / 8;                  // 16-byte pieces per row
   constexpr int TILE = BN * D;               // elements per tile
@@ -452,17 +457,20 @@ hipError_t launch_attend(const Geo& g, const scope_plan_t& plan, const void* qr,
   a.scale = (float)(1.0 / sqrt((double)g.d));
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   if (plan.work_capacity == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((plan.work_capacity + 7) / 8 * 8);
+  const unsigned grid = (unsigned)((plan.work_capacity + 8 * ATT_RUN - 1) / (8 * ATT_RUN) * (8 * ATT_RUN));
 #define SCOPE_ATT_ARGS \
   a, plan.work, plan.status, plan.perm_q, plan.q_off, plan.counts_r, plan.sel_off, plan.sel_idx, plan.k_norm_max
   if (g.bf16) {
-    // 4 waves x 32 queries; 3 (d = 64) or 2 (d = 128) waves per SIMD
+    // d = 64: 4 waves x 32 queries, 3 waves per SIMD (three workgroups per
+    // CU); d = 128: 8 waves x 32 queries, 2 waves per SIMD (one workgroup per
+    // CU), so that each K / V chunk gathered into LDS serves 256 queries
+    static_assert(32 * ATT_NW64 == ATT_BM && 32 * ATT_NW128 == ATT_BM128, "work-list chunks");
     if (g.d == 64)
-      attend_bf16_lds_kernel<64, 3><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
-                                                         (const uint16_t*)v, (uint16_t*)out);
+      attend_bf16_lds_kernel<64, 3, ATT_NW64><<<grid, 64 * ATT_NW64, 0, s>>>(
+          SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr, (const uint16_t*)v, (uint16_t*)out);
     else
-      attend_bf16_lds_kernel<128, 2><<<grid, 256, 0, s>>>(SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr,
-                                                          (const uint16_t*)v, (uint16_t*)out);
+      attend_bf16_lds_kernel<128, 2, ATT_NW128><<<grid, 64 * ATT_NW128, 0, s>>>(
+          SCOPE_ATT_ARGS, (const uint16_t*)qr, (const uint16_t*)kr, (const uint16_t*)v, (uint16_t*)out);
   } else {
     if (g.d == 64)
       attend_f32_kernel<64><<<grid, ATT_BM, 0, s>>>(SCOPE_ATT_ARGS, (const float*)qr, (const float*)kr,

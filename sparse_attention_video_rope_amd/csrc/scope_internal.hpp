@@ -9,7 +9,10 @@
 
 namespace scope {
 
-constexpr int ATT_BM = 128;     // queries per attention work item (4 waves x 32)
+constexpr int ATT_BM = 128;     // queries per attention work item (fp32 storage; bf16 with d = 64: 4 waves x 32)
+constexpr int ATT_BM128 = 256;  // queries per attention work item, bf16 with d = 128 (8 waves x 32)
+constexpr int ATT_NW64 = 4;     // waves per attention workgroup, bf16 with d = 64
+constexpr int ATT_NW128 = 8;    // waves per attention workgroup, bf16 with d = 128
 constexpr int SEL_NB = 2048;    // histogram bins per level in the selection kernels
 constexpr int SEL_CAP = 1024;   // boundary candidates sorted in LDS (more fall back to a walk over distinct logits)
 constexpr int MAX_C = 1024;     // largest Cq / Cm supported
@@ -82,7 +85,7 @@ struct Workspace {
 };
 
 // Queries per attention work item (every kernel: 128).
-inline int att_chunk(const Geo&) { return ATT_BM; }
+inline int att_chunk(const Geo& g) { return g.bf16 && g.d == 128 ? ATT_BM128 : ATT_BM; }
 // Lloyd update layout: channel slices of acc_sw channels, acc_parts point
 // ranges per (head, clustering).  Slices are 32 channels wide unless the
 // per-cluster sums of that width (Cmax x 32 fp64 plus the counts, beside the

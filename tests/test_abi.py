@@ -118,10 +118,11 @@ def test_channel_permutation_validation():
 def test_workspace_size_and_capacities():
     p = good()
     ws, sel, work = sav.sizes(p)
-    # work items: BH * (Cq + ceil(N / 128))
+    # work items: BH * (Cq + ceil(N / chunk)); chunk = 128 queries, 256 for bf16 with d = 128
     assert ws > 0 and sel == 2 * 8 * 256 and work == 2 * (8 + 2)
     assert sav.sizes(good(dtype="f32"))[2] == 2 * (8 + 2)
-    assert sav.sizes(good(d=128, split=(44, 42, 42)))[2] == 2 * (8 + 2)
+    assert sav.sizes(good(d=128, split=(44, 42, 42)))[2] == 2 * (8 + 1)
+    assert sav.sizes(good(d=128, split=(44, 42, 42), dtype="f32"))[2] == 2 * (8 + 2)
     # monotone in the token count
     ws2, _, _ = sav.sizes(good(T=8))
     assert ws2 > ws

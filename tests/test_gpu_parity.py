@@ -1,6 +1,6 @@
 """GPU parity of every stage against the oracle, at sizes the oracle finishes in
 seconds.  The shapes span several tiles of each kernel with ragged tails
-(128-query attention chunks, 64-key gather chunks, 32-centroid MFMA blocks,
+(128- and 256-query attention chunks, 64-key gather chunks, 32-centroid MFMA blocks,
 256-point assignment tiles)."""
 import math
 from fractions import Fraction
@@ -429,3 +429,51 @@ def test_full_dim_key_codebook_end_to_end(w):
     for bh, o in enumerate(heads):
         mx, mn = assert_attention(g["out"][bh], o["out"], w.dtype, f"{w.name} head {bh}")
         say(f"  head {bh}: max {mx:.2e} mean {mn:.2e}")
+
+
+# cluster sizes around the 32-query wave groups and the 128- / 256-query work
+# items (one empty cluster), and key-set sizes around the 32-key subtiles and the
+# 64-key chunks of the attention kernel
+ITEM_SIZES = [1, 2, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 191, 192, 193, 0, 256, 257, 255, 445]
+KEY_SIZES = [1, 7, 31, 32, 33, 63, 64, 65, 97, 128, 129, 255, 300, 1000, 2560]
+
+
+@pytest.mark.parametrize("shift", [0, 4, 9])
+@pytest.mark.parametrize("d", [64, 128])
+def test_attend_item_shapes(d, shift):
+    """Hand-built plans: every query count around the wave groups and work items
+    paired with key sets of every size around the subtiles and chunks (shifted
+    per case), with and without the logit bound; output against the oracle's
+    attention over the same sets."""
+    split = (16, 24, 24) if d == 64 else (44, 42, 42)
+    w = workloads.small("shapes", 4, 16, 40, d, split, "bf16", len(ITEM_SIZES), 8, H=1, index=115)
+    N, Cq = w.N, w.Cq
+    assert sum(ITEM_SIZES) == N
+    say("item shapes", d, shift)
+    q, k, v = workloads.generate(w)
+    rng = np.random.default_rng(1000 + shift)
+    tokens = rng.permutation(N)
+    labels = np.empty(N, dtype=np.int64)
+    labels[tokens] = np.repeat(np.arange(Cq), ITEM_SIZES)
+    sel = [np.sort(rng.choice(N, size=KEY_SIZES[(c + shift) % len(KEY_SIZES)], replace=False)) for c in range(Cq)]
+    r = np.array([len(s) if ITEM_SIZES[c] else 0 for c, s in enumerate(sel)])
+    sel = [s if ITEM_SIZES[c] else s[:0] for c, s in enumerate(sel)]
+    perm, off = O.cluster_permutation(labels, Cq)
+    head = {"perm_q": perm, "q_off": off, "t": r, "b": r, "r": r, "k_head": int(r.max()), "sel": sel}
+    p = sav.params_for(w)
+    pl = sav.Plan(p, debug=False)
+    upload_oracle_plan(w, [head], pl)
+    sav.plan_finalize(p, pl)
+    want = O.sparse_attention(q[0], k[0], v[0], labels, sel)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    kn = float(np.sqrt((k[0] ** 2).sum(1)).max()) * (1 + 2**-10)
+    for name, bound in (("bound", kn), ("no bound", 0.0)):
+        pl.k_norm_max.fill_(bound)
+        out = to_np(sav.attend(p, pl, qd, kd, vd)).reshape(N, d)
+        for c in range(Cq):
+            rows = labels == c
+            if rows.any():
+                assert_attention(out[rows], want[rows], "bf16",
+                                 f"{name}: cluster {c} n {ITEM_SIZES[c]} r {r[c]}")
+        mx, mn = assert_attention(out, want, "bf16", name)
+        say(f"  {name}: max {mx:.2e} mean {mn:.2e}")
