@@ -81,6 +81,10 @@ typedef __attribute__((address_space(1))) const char gbl_char;
 __device__ __forceinline__ void lds_load16(gbl_char* src, lds_u16* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
+// s_waitcnt immediate that waits until at most n vector memory operations are
+// outstanding and leaves the other counters alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 __device__ __forceinline__ s16x4_t lds_read_tr16(const lds_u16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
@@ -101,10 +105,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   constexpr int RPB = 64 / PR;               // rows per block
   static_assert(IPW * NW == BLK, "gather split");
   constexpr float RESCALE_LOG2 = 8.f;
+  // three buffers per tile: chunk c lives in buffer c mod 3, and its rows are
+  // gathered two chunks ahead
   __shared__ __align__(1024) uint16_t Ks0[TILE];
   __shared__ __align__(1024) uint16_t Ks1[TILE];
+  __shared__ __align__(1024) uint16_t Ks2[TILE];
   __shared__ __align__(1024) uint16_t Vs0[TILE];
   __shared__ __align__(1024) uint16_t Vs1[TILE];
+  __shared__ __align__(1024) uint16_t Vs2[TILE];
+  // key indices of chunk c in slot c mod 3 (one row of 64 per wave), loaded
+  // four chunks ahead
+  __shared__ __align__(256) int32_t Is0[NW * BN];
+  __shared__ __align__(256) int32_t Is1[NW * BN];
+  __shared__ __align__(256) int32_t Is2[NW * BN];
+  static_assert(BN == 64, "one 64-lane dword load per chunk of indices");
 
   if (status[1]) return;
   const int item = att_item(status[0]);
@@ -194,12 +208,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
     koff[i] = (uint32_t)((slot ^ kswz(row)) * 16);
     voff[i] = (uint32_t)((slot ^ vswz(row)) * 16);
   }
-  // raw key indices of the next chunk's rows (loaded a chunk ahead)
+  // Key indices travel through LDS: each wave copies the 64 indices of a
+  // chunk into its own row of the chunk's slot with one dword load to LDS
+  // (lane l: key c BN + l, clamped to the last one) and reads its rows'
+  // indices from there.  No register is loaded from global memory inside the
+  // loop, so the compiler inserts no vector-memory wait of its own for them,
+  // and the rows gathered ahead stay in flight until the explicit wait at the
+  // end of each step.  The three slots are separate arrays, so that the
+  // compiler can see that a slot being read is not the one being loaded.
+  typedef __attribute__((address_space(3))) int32_t lds_i32;
+  lds_i32* I0 = (lds_i32*)&Is0[0];
+  lds_i32* I1 = (lds_i32*)&Is1[0];
+  lds_i32* I2 = (lds_i32*)&Is2[0];
+  auto islot = [&](int c) { const int m = c % 3; return m == 0 ? I0 : (m == 1 ? I1 : I2); };
   int kidx[IPW];
-  auto load_idx = [&](int kc) {
+  auto load_idx = [&](int c, lds_i32* slot) {
+    __builtin_amdgcn_global_load_lds((gbl_char*)(keyb + (uint32_t)min(c * BN + lane, r - 1) * 4u),
+                                     (__attribute__((address_space(3))) void*)(slot + wv * BN), 4, 0, 0);
+  };
+  auto take_idx = [&](const lds_i32* slot) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i)
-      kidx[i] = *reinterpret_cast<const int*>(keyb + (uint32_t)min(kc * BN + grow(i), r - 1) * 4u);
+    for (int i = 0; i < IPW; ++i) kidx[i] = slot[wv * BN + grow(i)];
   };
   auto gather = [&](lds_u16* Kd, lds_u16* Vd) {
 #pragma unroll
@@ -233,11 +262,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   // chunk exists.  Without the branches of the general step, the compiler can
   // interleave the exponentials of one 32-key subtile with the QK^T MFMAs of
   // the other.
-  auto step = [&](auto fast_c, int kc, lds_u16* Kc, lds_u16* Vc, lds_u16* Kn, lds_u16* Vn) {
+  // Step of chunk kc (rows in Kc / Vc): gathers chunk kc + 2 into Kg / Vg
+  // (the buffer of chunk kc - 1, free since the last barrier) with the
+  // indices in slot It, and loads the indices of chunk kc + 4 into slot Il
+  // (the slot of chunk kc + 1, whose indices were used in the last step).
+  auto step = [&](auto fast_c, int kc, lds_u16* Kc, lds_u16* Vc, lds_u16* Kg, lds_u16* Vg, lds_i32* It,
+                  lds_i32* Il) {
     constexpr bool FAST = decltype(fast_c)::value;
-    if (FAST || kc + 1 < nchunks) {
-      gather(Kn, Vn);                              // rows of chunk kc+1
-      load_idx(min(kc + 2, nchunks - 1));          // indices of chunk kc+2
+    const bool more = FAST || kc + 2 < nchunks;
+    if (more) {
+      take_idx(It);                                // indices of chunk kc+2 (landed by the last step's wait)
+      load_idx(min(kc + 4, nchunks - 1), Il);      // indices of chunk kc+4
+      gather(Kg, Vg);                              // rows of chunk kc+2
     }
     if (active) {
       f32x16_t s[NST];
@@ -317,23 +353,43 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
         }
       }
     }
-    // this chunk's reads are done and the next chunk's rows have landed
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // this chunk's reads are done, and the next chunk's rows (gathered in the
+    // previous step) and the indices of chunk kc + 3 (loaded before them) have
+    // landed: only this step's loads (one index load and 2 IPW row loads) may
+    // still be in flight
+    if (more) __builtin_amdgcn_s_waitcnt(waitcnt_vm(1 + 2 * IPW));
+    else __builtin_amdgcn_s_waitcnt(0);
+    // a bare barrier: __syncthreads() adds a workgroup fence, whose release
+    // waits for every outstanding load, the prefetched chunk's too.  Every LDS
+    // read of this step has completed (its values are MFMA operands) and the
+    // explicit wait above covers this wave's part of the next chunk; the
+    // memory clobber keeps the compiler from moving LDS accesses across it.
+    asm volatile("s_barrier" ::: "memory");
   };
 
   lds_u16* K0 = (lds_u16*)&Ks0[0];
   lds_u16* K1 = (lds_u16*)&Ks1[0];
+  lds_u16* K2 = (lds_u16*)&Ks2[0];
   lds_u16* V0 = (lds_u16*)&Vs0[0];
   lds_u16* V1 = (lds_u16*)&Vs1[0];
+  lds_u16* V2 = (lds_u16*)&Vs2[0];
   if (nchunks > 0) {
-    load_idx(0);
+    // indices of chunks 0 .. 3 (clamped to the last chunk), then rows of
+    // chunks 0 and 1
+    load_idx(0, I0);
+    load_idx(min(1, nchunks - 1), I1);
+    load_idx(min(2, nchunks - 1), I2);
     __builtin_amdgcn_s_waitcnt(0);
+    take_idx(I0);
     gather(K0, V0);
-    if (nchunks > 1) load_idx(1);
+    if (nchunks > 1) {
+      take_idx(I1);
+      gather(K1, V1);
+    }
+    load_idx(min(3, nchunks - 1), I0);
   }
-  // Q rows, the first chunk and the next indices are complete here on every
-  // path, so the loop starts with no loads outstanding
+  // Q rows, the first two chunks and the indices of chunks 2 and 3 are
+  // complete here on every path, so the loop starts with no loads outstanding
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // After the first chunk mref is its maximum m0 <= max_j t_j <= bound (t the
@@ -368,28 +424,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   };
   const std::false_type general{};
   const std::true_type fast{};
+  // buffer of chunk c, for the steps whose chunk is known only at run time
+  auto kbuf = [&](int c) { const int m = c % 3; return m == 0 ? K0 : (m == 1 ? K1 : K2); };
+  auto vbuf = [&](int c) { const int m = c % 3; return m == 0 ? V0 : (m == 1 ? V1 : V2); };
   int kc = 1;
   if (nchunks > 0) {
-    step(general, 0, K0, V0, K1, V1);
+    step(general, 0, K0, V0, K2, V2, I2, I1);
     decide();
-    // middle chunks (two per iteration: chunk kc reads buffer 1, kc + 1
-    // buffer 0); a wave-uniform choice of the loop, made once
+    // middle chunks, three per iteration (kc = 1 mod 3: chunk kc in buffer 1,
+    // kc + 1 in 2, kc + 2 in 0); each gathers the chunk two ahead, so the
+    // loop runs while kc + 4 < nchunks.  A wave-uniform choice, made once.
     if (fixed && __builtin_amdgcn_readfirstlane((int)fixed)) {
-      for (; kc + 2 < nchunks; kc += 2) {
-        step(fast, kc, K1, V1, K0, V0);
-        step(fast, kc + 1, K0, V0, K1, V1);
-      }
-    } else {
-      for (; kc + 2 < nchunks; kc += 2) {
-        step(general, kc, K1, V1, K0, V0);
-        step(general, kc + 1, K0, V0, K1, V1);
+      for (; kc + 4 < nchunks; kc += 3) {
+        step(fast, kc, K1, V1, K0, V0, I0, I2);
+        step(fast, kc + 1, K2, V2, K1, V1, I1, I0);
+        step(fast, kc + 2, K0, V0, K2, V2, I2, I1);
       }
     }
-    // the last one or two chunks (the last may be partial)
-    for (; kc < nchunks; ++kc) {
-      if (kc & 1) step(general, kc, K1, V1, K0, V0);
-      else step(general, kc, K0, V0, K1, V1);
-    }
+    // the rest (the last chunk may be partial), and every chunk of a wave
+    // that keeps the running maximum
+    for (; kc < nchunks; ++kc)
+      step(general, kc, kbuf(kc), vbuf(kc), kbuf(kc + 2), vbuf(kc + 2), islot(kc + 2), islot(kc + 1));
   }
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (!qvalid) return;
