@@ -1604,15 +1604,14 @@ __global__ __launch_bounds__(ACC_NT) void accum_kernel(const T* __restrict__ qr,
 // subtracts them from its old one; the sizes change by one each.  Same grid
 // and LDS table as accum_kernel; the nonzero entries of the table are then
 // added to the totals in global memory (fp64 atomics; exact, so in any
-// order).  The workgroup takes its points in segments of DELTA_PPT per thread
-// (all labels of a segment in flight at once), lists the changed ones in LDS and
-// then loads their rows in batches of 8 instructions per wave (64 / SW points
-// each: lanes = channels) before adding them (the previous version took 64
-// points per wave and step, with the labels one step ahead: 454 us per pass
-// at the Hunyuan-like size, bound by that chain of label loads).
-constexpr int DELTA_PPT = 4;                   // points per thread and segment of accum_delta_kernel
-constexpr int DELTA_SEG = ACC_NT * DELTA_PPT;   // 16 KB of LDS lists (the LDS table's limit counts them)
-template <int SW>
+// order).  The workgroup takes its points in segments of PPT per thread (all
+// labels of a segment in flight at once), lists the changed ones in LDS (after
+// the table: 8 PPT bytes per thread) and then loads their rows in batches of
+// 8 instructions per wave (64 / SW points each: lanes = channels) before
+// adding them.  The launch takes the largest PPT of 16, 8, 4 whose lists fit
+// next to the table: the segments of a workgroup are a chain of dependent
+// label loads.
+template <int SW, int PPT>
 __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __restrict__ qr,
                                                              const uint16_t* __restrict__ kr, Geo g,
                                                              const int32_t* __restrict__ labels,
@@ -1626,10 +1625,11 @@ __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __r
   const int s0 = sl * SW, sw = min(SW, dm - s0);
   if (sw <= 0) return;
   extern __shared__ __align__(16) unsigned char acc_smem[];
+  constexpr int SEG = ACC_NT * PPT;
   double* S = reinterpret_cast<double*>(acc_smem);                         // [C][SW]
   int32_t* cnt = reinterpret_cast<int32_t*>(acc_smem + (size_t)C * SW * 8);  // [C]
-  __shared__ int32_t dpt[DELTA_SEG];    // changed points of a segment
-  __shared__ int32_t dlab[DELTA_SEG];   // their new label | old label << 16
+  int32_t* dpt = cnt + ((g.Cmax + 3) & ~3);   // [SEG] changed points of a segment
+  int32_t* dlab = dpt + SEG;                  // [SEG] their new label | old label << 16
   __shared__ int32_t dcount;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i < C * SW; i += ACC_NT) S[i] = 0.0;
@@ -1643,23 +1643,23 @@ __global__ __launch_bounds__(ACC_NT) void accum_delta_kernel(const uint16_t* __r
   constexpr int G = 64 / SW, U = 8;
   const int j = lane / SW, ch = lane % SW;
   const bool chv = ch < sw;
-  // Segments of DELTA_PPT points per thread: every thread loads its labels at
+  // Segments of PPT points per thread: every thread loads its labels at
   // once, the changed points go to an LDS list (point, new | old << 16), and
   // then all waves add their rows (G points per instruction, U instructions
   // in flight).  The list order depends on timing, but the sums are exact.
-  for (int seg = p0; seg < p1; seg += DELTA_SEG) {
+  for (int seg = p0; seg < p1; seg += SEG) {
     if (tid == 0) dcount = 0;
     __syncthreads();
-    int Ln[DELTA_PPT], Lp[DELTA_PPT];
+    int Ln[PPT], Lp[PPT];
 #pragma unroll
-    for (int u = 0; u < DELTA_PPT; ++u) {
+    for (int u = 0; u < PPT; ++u) {
       const int p = seg + u * ACC_NT + tid;
       const bool ok = p < p1;
       Ln[u] = ok ? lab[p] : 0;
       Lp[u] = ok ? prv[p] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < DELTA_PPT; ++u) {
+    for (int u = 0; u < PPT; ++u) {
       const int p = seg + u * ACC_NT + tid;
       const bool c = p < p1 && Ln[u] != Lp[u];
       const uint64_t mk = __ballot(c);
@@ -2272,10 +2272,16 @@ hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Wor
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     kern<<<grid, ACC_NT, lds, s>>>(q, k, g, cur, w.psum, w.pcnt, ns, parts, w.ssm);
   };
+  // the delta update's LDS: the table, then the two lists of PPT entries per
+  // thread (the largest PPT that fits one CU, leaving 1 KB for the rest)
+  const size_t tbl = (size_t)g.Cmax * SW * 8 + (size_t)((g.Cmax + 3) & ~3) * 4;
+  auto dlds = [&](int ppt) { return tbl + (size_t)2 * ACC_NT * ppt * 4; };
+  const int ppt = dlds(16) + 1024 <= MAX_ASSIGN_LDS ? 16 : (dlds(8) + 1024 <= MAX_ASSIGN_LDS ? 8 : 4);
   auto god = [&](auto kern) {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kern<<<grid, ACC_NT, lds, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, cur, labels_of(g, w, it - 2), w.stot,
-                                  w.ntot, parts, w.ssm);
+    const size_t dl = dlds(ppt);
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dl);
+    kern<<<grid, ACC_NT, dl, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, cur, labels_of(g, w, it - 2), w.stot,
+                                 w.ntot, parts, w.ssm);
   };
   const uint16_t *qb = (const uint16_t*)qr, *kb = (const uint16_t*)kr;
   const float *qf = (const float*)qr, *kf = (const float*)kr;
@@ -2285,7 +2291,15 @@ hipError_t launch_update(const Geo& g, const void* qr, const void* kr, const Wor
     if (e != hipSuccess) return e;
   }
   if (delta) {
-    if (SW == 32) god(accum_delta_kernel<32>); else god(accum_delta_kernel<16>);
+    if (SW == 32) {
+      if (ppt == 16) god(accum_delta_kernel<32, 16>);
+      else if (ppt == 8) god(accum_delta_kernel<32, 8>);
+      else god(accum_delta_kernel<32, 4>);
+    } else {
+      if (ppt == 16) god(accum_delta_kernel<16, 16>);
+      else if (ppt == 8) god(accum_delta_kernel<16, 8>);
+      else god(accum_delta_kernel<16, 4>);
+    }
   } else if (g.bf16) {
     if (SW == 32) go(accum_kernel<uint16_t, 32>, qb, kb); else go(accum_kernel<uint16_t, 16>, qb, kb);
   } else {
