@@ -1920,7 +1920,10 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
         const int L = __ffsll((unsigned long long)amb) - 1;
         amb &= amb - 1;
         const int pp = __shfl(p, L);
-        for (int ch = lane; ch < dm; ch += 64) xs[ch] = (double)bf16_to_f32(X[(size_t)pp * d + ch]);
+        // the point's channels, zero up to the padded width (the table rows
+        // are zero there too)
+        const int dp = KB * 16;
+        for (int ch = lane; ch < dp; ch += 64) xs[ch] = ch < dm ? (double)bf16_to_f32(X[(size_t)pp * d + ch]) : 0.0;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1929,10 +1932,22 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
         for (int c = lane; c < C; c += 64) {
           const uint16_t* row = sc + c * ldc;
           double accd = 0.0;
-          for (int ch = 0; ch < dm; ++ch) {
-            // LDS holds -2 mu; mu = -0.5 * that, exactly
-            const double df = xs[ch] + 0.5 * (double)bf16_to_f32(row[ch]);
-            accd = fma(df, df, accd);
+          // 8 channels per 16-byte read (rows are 16-byte aligned: ldc = dpad
+          // + 8 with dpad a multiple of 16), added in channel order; the padding
+          // channels add exact zeros.  Not unrolled: this rare path must not
+          // raise the kernel's register count.
+#pragma unroll 1
+          for (int c8 = 0; c8 < dp; c8 += 8) {
+            const u32x4_t u = *reinterpret_cast<const u32x4_t*>(row + c8);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t wj = u[j];
+              // LDS holds -2 mu; mu = -0.5 * that, exactly
+              const double d0 = xs[c8 + 2 * j] + 0.5 * (double)__uint_as_float(wj << 16);
+              const double d1 = xs[c8 + 2 * j + 1] + 0.5 * (double)__uint_as_float(wj & 0xFFFF0000u);
+              accd = fma(d0, d0, accd);
+              accd = fma(d1, d1, accd);
+            }
           }
           if (accd < bd) { bd = accd; bc = c; }
         }
