@@ -6,7 +6,7 @@
 // bf16 path (gfx950, wave64): one workgroup of NW waves per (cluster, 32 NW-query
 // chunk) work item (NW = 8 at head dim 128, 4 at 64); each wave owns 32 queries
 // whose Q rows stay in registers as MFMA operands.  The selected keys' K and V rows are gathered 64 at a time
-// straight into LDS (row-major, double buffered).  Per 32-key subtile the wave
+// straight into LDS (row-major, three buffers, gathered two chunks ahead).  Per 32-key subtile the wave
 // computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so each lane holds 16
 // logits of one query: the online-softmax max and sum need one cross-lane
 // exchange, and the probabilities are already laid out as the B operand of
@@ -172,7 +172,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   float mref = 0.f, lsum = 0.f;    // reference (log2 units); set from the first chunk
   f32x16_t cneg = {};              // -mref in every element: the QK^T accumulator's start
   const int nchunks = (r + BN - 1) / BN;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   // upper bound of this query's scaled logits <q'', k'_j> (q'' the scaled bf16
   // row): ||q''|| (fp32 sum of exact bf16 squares) times the head's key-norm
   // bound, with a factor 1 + 2^-12 for the roundings; negative when there is
@@ -329,6 +328,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
           for (int v = 0; v < 16; ++v) cneg[v] = -mref;
         }
       }
+      // the chunk's share of the row sum, in four fp32 partial sums of the
+      // weights before their bf16 rounding: plain adds overlap the other
+      // wave's MFMAs, where a bf16 dot2 on the packed weights stalls them
+      float csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
 #pragma unroll
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
             const float p0 = __builtin_amdgcn_exp2f(s[st][half * 8 + 2 * i]);
             const float p1 = __builtin_amdgcn_exp2f(s[st][half * 8 + 2 * i + 1]);
             pk[i] = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(pk[i], ones, lsum, false);
+            csum[i] += p0 + p1;
           }
           const bf16x8_t bp = __builtin_bit_cast(bf16x8_t, pk);
           const int kofs = (st * 32 + half * 16) * D;
@@ -352,6 +355,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
           }
         }
       }
+      lsum += (csum[0] + csum[1]) + (csum[2] + csum[3]);
     }
     // this chunk's reads are done, and the next chunk's rows (gathered in the
     // previous step) and the indices of chunk kc + 3 (loaded before them) have
