@@ -136,8 +136,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool active = wv * 32 < nq;
-  const int qi = wv * 32 + col;
+  // Split items (8-wave workgroups): an item of at most 4 query blocks (a
+  // cluster's last item, often) would leave every SIMD with one busy wave.
+  // Instead each query block runs on two waves, w and w + 4, which share a
+  // SIMD: each takes one 32-key subtile of every chunk, and their partial
+  // softmax states are merged at the end.
+  constexpr bool CAN_SPLIT = NW == 8;
+  const bool split = CAN_SPLIT && nq <= 16 * NW;
+  const int qw = split ? (wv & (NW / 2 - 1)) : wv;   // query block of the wave
+  const int stb = split ? (wv / (NW / 2)) * 32 : 0;  // first key of its subtile in a chunk
+  const bool active = qw * 32 < nq;
+  const int qi = qw * 32 + col;
   const bool qvalid = qi < nq;
   const int tok = qvalid ? min(max(perm_q[hb + q0 + qi], 0), a.N - 1) : 0;
   bf16x8_t qb[D / 16];
@@ -219,7 +228,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   lds_i32* I0 = (lds_i32*)&Is0[0];
   lds_i32* I1 = (lds_i32*)&Is1[0];
   lds_i32* I2 = (lds_i32*)&Is2[0];
-  auto islot = [&](int c) { const int m = c % 3; return m == 0 ? I0 : (m == 1 ? I1 : I2); };
   int kidx[IPW];
   auto load_idx = [&](int c, lds_i32* slot) {
     __builtin_amdgcn_global_load_lds((gbl_char*)(keyb + (uint32_t)min(c * BN + lane, r - 1) * 4u),
@@ -243,13 +251,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   // dt*32 + 16*((lane >> 4) & 1) + 4*(lane & 3)
   uint32_t kro[D / 16], vro[D / 32];
 #pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) kro[kb] = (uint32_t)(col * D + (((2 * kb) | hi) ^ kswz(col)) * 8);
+  for (int kb = 0; kb < D / 16; ++kb) kro[kb] = (uint32_t)((stb + col) * D + (((2 * kb) | hi) ^ kswz(col)) * 8);
   {
     const int i16 = lane & 15, ra = i16 >> 2, b = i16 & 3, gl = (lane >> 4) & 1;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       const int lp = dt * 4 + 2 * gl + (b >> 1);
-      vro[dt] = (uint32_t)((4 * hi + ra) * D + ((lp ^ vswz(ra)) * 8) + (b & 1) * 4);
+      vro[dt] = (uint32_t)((stb + 4 * hi + ra) * D + ((lp ^ vswz(ra)) * 8) + (b & 1) * 4);
     }
   }
 
@@ -265,9 +273,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   // (the buffer of chunk kc - 1, free since the last barrier) with the
   // indices in slot It, and loads the indices of chunk kc + 4 into slot Il
   // (the slot of chunk kc + 1, whose indices were used in the last step).
-  auto step = [&](auto fast_c, int kc, lds_u16* Kc, lds_u16* Vc, lds_u16* Kg, lds_u16* Vg, lds_i32* It,
-                  lds_i32* Il) {
+  auto step = [&](auto fast_c, auto nst_c, int kc, lds_u16* Kc, lds_u16* Vc, lds_u16* Kg, lds_u16* Vg,
+                  lds_i32* It, lds_i32* Il) __attribute__((always_inline)) {
     constexpr bool FAST = decltype(fast_c)::value;
+    constexpr int NSTW = decltype(nst_c)::value;   // subtiles of the chunk this wave takes
     const bool more = FAST || kc + 2 < nchunks;
     if (more) {
       take_idx(It);                                // indices of chunk kc+2 (landed by the last step's wait)
@@ -275,9 +284,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
       gather(Kg, Vg);                              // rows of chunk kc+2
     }
     if (active) {
-      f32x16_t s[NST];
+      f32x16_t s[NSTW];
 #pragma unroll
-      for (int st = 0; st < NST; ++st) {
+      for (int st = 0; st < NSTW; ++st) {
         bf16x8_t ak[D / 16];
 #pragma unroll
         for (int kb = 0; kb < D / 16; ++kb) ak[kb] = *(const lds_bf16x8*)(Kc + kro[kb] + st * 32 * D);
@@ -293,10 +302,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
         // key offset of this lane's rows, made opaque here so that the 32 key
         // positions are formed in this (last-chunk) branch instead of being
         // kept live in registers across the loop
-        int k4 = 4 * hi;
+        int k4 = 4 * hi + stb;
         asm volatile("" : "+v"(k4));
 #pragma unroll
-        for (int st = 0; st < NST; ++st)
+        for (int st = 0; st < NSTW; ++st)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             if (st * 32 + 8 * (v >> 2) + (v & 3) + k4 >= kleft) s[st][v] = -__builtin_inff();
@@ -307,12 +316,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
         // maximum exceeds it by more than RESCALE_LOG2
         float mloc = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-        for (int e = 2; e < NST * 16; e += 2) mloc = fmaxf(fmaxf(mloc, s[e >> 4][e & 15]), s[e >> 4][(e + 1) & 15]);
+        for (int e = 2; e < NSTW * 16; e += 2) mloc = fmaxf(fmaxf(mloc, s[e >> 4][e & 15]), s[e >> 4][(e + 1) & 15]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
         const bool first = kc == 0;
         const bool grow_m = first || mloc > RESCALE_LOG2;
         if (__ballot(grow_m)) {
-          const float dm = grow_m ? mloc : 0.f;
+          // a split wave's subtile can be empty in the only chunk (r <= 32):
+          // its reference stays 0 and its weights 0
+          const float dm = grow_m && mloc != -__builtin_inff() ? mloc : 0.f;
           const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-dm);
           lsum *= alpha;
 #pragma unroll
@@ -320,7 +331,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
 #pragma unroll
             for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
 #pragma unroll
-          for (int st = 0; st < NST; ++st)
+          for (int st = 0; st < NSTW; ++st)
 #pragma unroll
             for (int v = 0; v < 16; ++v) s[st][v] -= dm;
           mref += dm;
@@ -333,7 +344,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
       // wave's MFMAs, where a bf16 dot2 on the packed weights stalls them
       float csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < NST; ++st) {
+      for (int st = 0; st < NSTW; ++st) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           bf16x2_t pk[4];
@@ -403,7 +414,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   // largest one is >= 2^-64 (the fp32 / bf16 exponent range keeps every weight
   // that is not negligible next to it), so the chunk maximum is no longer
   // needed.
-  auto decide = [&]() {
+  auto decide = [&]() __attribute__((always_inline)) {
     if (nchunks < 2 || !active) return;
     const bool ok = !qvalid || (bound >= mref && bound - mref <= 124.f);
     // the decision is wave-uniform; it is handed over in a VGPR the compiler
@@ -428,29 +439,83 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   };
   const std::false_type general{};
   const std::true_type fast{};
-  // buffer of chunk c, for the steps whose chunk is known only at run time
-  auto kbuf = [&](int c) { const int m = c % 3; return m == 0 ? K0 : (m == 1 ? K1 : K2); };
-  auto vbuf = [&](int c) { const int m = c % 3; return m == 0 ? V0 : (m == 1 ? V1 : V2); };
-  int kc = 1;
-  if (nchunks > 0) {
-    step(general, 0, K0, V0, K2, V2, I2, I1);
-    decide();
-    // middle chunks, three per iteration (kc = 1 mod 3: chunk kc in buffer 1,
-    // kc + 1 in 2, kc + 2 in 0); each gathers the chunk two ahead, so the
-    // loop runs while kc + 4 < nchunks.  A wave-uniform choice, made once.
-    if (fixed && __builtin_amdgcn_readfirstlane((int)fixed)) {
-      for (; kc + 4 < nchunks; kc += 3) {
-        step(fast, kc, K1, V1, K0, V0, I0, I2);
-        step(fast, kc + 1, K2, V2, K1, V1, I1, I0);
-        step(fast, kc + 2, K0, V0, K2, V2, I2, I1);
+  auto run = [&](auto nst_c) __attribute__((always_inline)) {
+    int kc = 1;
+    if (nchunks > 0) {
+      step(general, nst_c, 0, K0, V0, K2, V2, I2, I1);
+      decide();
+      // middle chunks, three per iteration (kc = 1 mod 3: chunk kc in buffer 1,
+      // kc + 1 in 2, kc + 2 in 0); each gathers the chunk two ahead, so the
+      // loop runs while kc + 4 < nchunks.  A wave-uniform choice, made once.
+      if (fixed && __builtin_amdgcn_readfirstlane((int)fixed)) {
+        for (; kc + 4 < nchunks; kc += 3) {
+          step(fast, nst_c, kc, K1, V1, K0, V0, I0, I2);
+          step(fast, nst_c, kc + 1, K2, V2, K1, V1, I1, I0);
+          step(fast, nst_c, kc + 2, K0, V0, K2, V2, I2, I1);
+        }
+      }
+      // the rest (the last chunk may be partial), and every chunk of a wave
+      // that keeps the running maximum: kc = 1 mod 3 here as well, so the
+      // buffers stay compile-time choices (selected at run time, they became
+      // a table in scratch memory)
+      for (; kc < nchunks; kc += 3) {
+        step(general, nst_c, kc, K1, V1, K0, V0, I0, I2);
+        if (kc + 1 >= nchunks) break;
+        step(general, nst_c, kc + 1, K2, V2, K1, V1, I1, I0);
+        if (kc + 2 >= nchunks) break;
+        step(general, nst_c, kc + 2, K0, V0, K2, V2, I2, I1);
       }
     }
-    // the rest (the last chunk may be partial), and every chunk of a wave
-    // that keeps the running maximum
-    for (; kc < nchunks; ++kc)
-      step(general, kc, kbuf(kc), vbuf(kc), kbuf(kc + 2), vbuf(kc + 2), islot(kc + 2), islot(kc + 1));
+  };
+  float ltot = 0.f;
+  bool merged = false;
+  if constexpr (CAN_SPLIT) {
+    if (split) {
+      run(std::integral_constant<int, 1>{});
+      // the waves of the second subtile hand their state to their partners
+      // through the K / V buffers (free: every step ended with a barrier after
+      // its reads, and the last one waited for all gathers): O lane-major in
+      // one 16 KB buffer per query block, the references and row sums in V1
+      typedef __attribute__((address_space(3))) float lds_f32;
+      lds_f32* const xo = (lds_f32*)(qw == 0 ? K0 : (qw == 1 ? K1 : (qw == 2 ? K2 : V0)));
+      lds_f32* const xm = (lds_f32*)V1 + qw * 128;
+      if (stb) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) xo[(dt * 16 + v) * 64 + lane] = o[dt][v];
+        xm[lane] = mref;
+        xm[64 + lane] = lsum;
+      }
+      __syncthreads();
+      if (stb) return;
+      const float m2 = xm[lane], l2 = xm[64 + lane];
+      const float t1 = lsum + __shfl_xor(lsum, 32), t2 = l2 + __shfl_xor(l2, 32);
+      // merge: both sides rescaled to the larger reference; a side without
+      // weight (an empty subtile) takes no part
+      float a1 = 1.f, a2 = 0.f;
+      if (t2 > 0.f) {
+        if (t1 > 0.f) {
+          const float mm = fmaxf(mref, m2);
+          a1 = __builtin_amdgcn_exp2f(mref - mm);
+          a2 = __builtin_amdgcn_exp2f(m2 - mm);
+        } else {
+          a1 = 0.f;
+          a2 = 1.f;
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[dt][v] = o[dt][v] * a1 + xo[(dt * 16 + v) * 64 + lane] * a2;
+      ltot = t1 * a1 + t2 * a2;
+      merged = true;
+    }
   }
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (!merged) {
+    run(std::integral_constant<int, NST>{});
+    ltot = lsum + __shfl_xor(lsum, 32);
+  }
   if (!qvalid) return;
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   uint16_t* orow = out + (hb + tok) * D;
