@@ -136,15 +136,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Split items (8-wave workgroups): an item of at most 4 query blocks (a
-  // cluster's last item, often) would leave every SIMD with one busy wave.
-  // Instead each query block runs on two waves, w and w + 4, which share a
-  // SIMD: each takes one 32-key subtile of every chunk, and their partial
-  // softmax states are merged at the end.
+  // Split items (8-wave workgroups; waves w and w + 4 share a SIMD).  An item
+  // of nb <= 6 query blocks (a cluster's last item, often) would leave SIMDs
+  // with one busy wave beside SIMDs with two.  Instead some query blocks run
+  // on two waves, each taking one 32-key subtile of every chunk, and the two
+  // partial softmax states are merged at the end:
+  //   nb <= 4: block w on waves w and w + 4 (subtiles 0 and 1);
+  //   nb = 5, 6: blocks 0-3 whole on waves 0-3, block 4 on waves 4 and 6,
+  //   block 5 on waves 5 and 7.
   constexpr bool CAN_SPLIT = NW == 8;
-  const bool split = CAN_SPLIT && nq <= 16 * NW;
-  const int qw = split ? (wv & (NW / 2 - 1)) : wv;   // query block of the wave
-  const int stb = split ? (wv / (NW / 2)) * 32 : 0;  // first key of its subtile in a chunk
+  const int nb = (nq + 31) / 32;
+  const bool split = CAN_SPLIT && nb <= 6;           // some blocks split (workgroup-uniform)
+  const bool half = split && (nb <= 4 || wv >= 4);   // this wave takes one subtile
+  // query block of the wave, first key of its subtile in a chunk, and the
+  // merge slot of its pair
+  const int qw = !half ? wv : (nb <= 4 ? (wv & 3) : 4 + (wv & 1));
+  const int stb = !half ? 0 : (nb <= 4 ? (wv >> 2) : (wv >> 1) & 1) * 32;
+  const int mslot = !half ? 0 : (nb <= 4 ? qw : qw - 4);
   const bool active = qw * 32 < nq;
   const int qi = qw * 32 + col;
   const bool qvalid = qi < nq;
@@ -471,15 +479,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   bool merged = false;
   if constexpr (CAN_SPLIT) {
     if (split) {
-      run(std::integral_constant<int, 1>{});
+      if (half) run(std::integral_constant<int, 1>{});
+      else run(std::integral_constant<int, NST>{});
       // the waves of the second subtile hand their state to their partners
       // through the K / V buffers (free: every step ended with a barrier after
       // its reads, and the last one waited for all gathers): O lane-major in
-      // one 16 KB buffer per query block, the references and row sums in V1
+      // one 16 KB buffer per split block, the references and row sums in V1
       typedef __attribute__((address_space(3))) float lds_f32;
-      lds_f32* const xo = (lds_f32*)(qw == 0 ? K0 : (qw == 1 ? K1 : (qw == 2 ? K2 : V0)));
-      lds_f32* const xm = (lds_f32*)V1 + qw * 128;
-      if (stb) {
+      lds_f32* const xo = (lds_f32*)(mslot == 0 ? K0 : (mslot == 1 ? K1 : (mslot == 2 ? K2 : V0)));
+      lds_f32* const xm = (lds_f32*)V1 + mslot * 128;
+      if (half && stb) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -488,8 +497,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
         xm[64 + lane] = lsum;
       }
       __syncthreads();
-      if (stb) return;
-      const float m2 = xm[lane], l2 = xm[64 + lane];
+      if (half && stb) return;
+      const float m2 = half ? xm[lane] : 0.f, l2 = half ? xm[64 + lane] : 0.f;
       const float t1 = lsum + __shfl_xor(lsum, 32), t2 = l2 + __shfl_xor(l2, 32);
       // merge: both sides rescaled to the larger reference; a side without
       // weight (an empty subtile) takes no part
@@ -504,10 +513,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
           a2 = 1.f;
         }
       }
+      if (half) {
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[dt][v] = o[dt][v] * a1 + xo[(dt * 16 + v) * 64 + lane] * a2;
+          for (int v = 0; v < 16; ++v) o[dt][v] = o[dt][v] * a1 + xo[(dt * 16 + v) * 64 + lane] * a2;
+      }
       ltot = t1 * a1 + t2 * a2;
       merged = true;
     }
