@@ -136,23 +136,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hi = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Split items (8-wave workgroups; waves w and w + 4 share a SIMD).  An item
-  // of nb <= 6 query blocks (a cluster's last item, often) would leave SIMDs
-  // with one busy wave beside SIMDs with two.  Instead some query blocks run
-  // on two waves, each taking one 32-key subtile of every chunk, and the two
-  // partial softmax states are merged at the end:
-  //   nb <= 4: block w on waves w and w + 4 (subtiles 0 and 1);
-  //   nb = 5, 6: blocks 0-3 whole on waves 0-3, block 4 on waves 4 and 6,
-  //   block 5 on waves 5 and 7.
-  constexpr bool CAN_SPLIT = NW == 8;
+  // Split items.  An item of nb <= 3 NW / 4 query blocks (a cluster's last
+  // item, often) would leave waves idle, and with 8 waves SIMDs with one busy
+  // wave beside SIMDs with two (waves w and w + 4 share a SIMD).  Instead
+  // some query blocks run on two waves, each taking one 32-key subtile of
+  // every chunk, and the two partial softmax states are merged at the end
+  // (H = NW / 2):
+  //   nb <= H: block w on waves w and w + H (subtiles 0 and 1);
+  //   H < nb <= 3H/2: blocks 0 .. H-1 whole on waves 0 .. H-1, block H + j on
+  //   waves H + j and H + H/2 + j.
+  constexpr int H = NW / 2;
+  static_assert(NW % 4 == 0 && H <= 4, "split pairs and their merge buffers");
   const int nb = (nq + 31) / 32;
-  const bool split = CAN_SPLIT && nb <= 6;           // some blocks split (workgroup-uniform)
-  const bool half = split && (nb <= 4 || wv >= 4);   // this wave takes one subtile
+  const bool split = 2 * nb <= 3 * H;                // some blocks split (workgroup-uniform)
+  const bool half = split && (nb <= H || wv >= H);   // this wave takes one subtile
   // query block of the wave, first key of its subtile in a chunk, and the
   // merge slot of its pair
-  const int qw = !half ? wv : (nb <= 4 ? (wv & 3) : 4 + (wv & 1));
-  const int stb = !half ? 0 : (nb <= 4 ? (wv >> 2) : (wv >> 1) & 1) * 32;
-  const int mslot = !half ? 0 : (nb <= 4 ? qw : qw - 4);
+  const int qw = !half ? wv : (nb <= H ? wv % H : H + (wv - H) % (H / 2));
+  const int stb = !half ? 0 : (nb <= H ? wv / H : (wv - H) / (H / 2)) * 32;
+  const int mslot = !half ? 0 : (nb <= H ? qw : qw - H);
   const bool active = qw * 32 < nq;
   const int qi = qw * 32 + col;
   const bool qvalid = qi < nq;
@@ -477,14 +479,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   };
   float ltot = 0.f;
   bool merged = false;
-  if constexpr (CAN_SPLIT) {
+  {
     if (split) {
       if (half) run(std::integral_constant<int, 1>{});
       else run(std::integral_constant<int, NST>{});
       // the waves of the second subtile hand their state to their partners
       // through the K / V buffers (free: every step ended with a barrier after
       // its reads, and the last one waited for all gathers): O lane-major in
-      // one 16 KB buffer per split block, the references and row sums in V1
+      // one buffer (64 x D bf16 = 32 D floats per lane) per split block, the
+      // references and row sums in V1
       typedef __attribute__((address_space(3))) float lds_f32;
       lds_f32* const xo = (lds_f32*)(mslot == 0 ? K0 : (mslot == 1 ? K1 : (mslot == 2 ? K2 : V0)));
       lds_f32* const xm = (lds_f32*)V1 + mslot * 128;
