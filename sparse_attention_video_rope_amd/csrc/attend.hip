@@ -477,32 +477,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
       }
     }
   };
-  float ltot = 0.f;
-  bool merged = false;
-  {
-    if (split) {
-      if (half) run(std::integral_constant<int, 1>{});
-      else run(std::integral_constant<int, NST>{});
-      // the waves of the second subtile hand their state to their partners
-      // through the K / V buffers (free: every step ended with a barrier after
-      // its reads, and the last one waited for all gathers): O lane-major in
-      // one buffer (64 x D bf16 = 32 D floats per lane) per split block, the
-      // references and row sums in V1
-      typedef __attribute__((address_space(3))) float lds_f32;
-      lds_f32* const xo = (lds_f32*)(mslot == 0 ? K0 : (mslot == 1 ? K1 : (mslot == 2 ? K2 : V0)));
-      lds_f32* const xm = (lds_f32*)V1 + mslot * 128;
-      if (half && stb) {
+  if (half) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, NST>{});
+  float ltot = lsum + __shfl_xor(lsum, 32);
+  if (split) {
+    // the waves of the second subtile hand their state to their partners
+    // through the K / V buffers (free: every step ended with a barrier after
+    // its reads, and the last one waited for all gathers): O lane-major in
+    // one buffer (64 x D bf16 = 32 D floats per lane) per split block, the
+    // references and row sums in V1
+    typedef __attribute__((address_space(3))) float lds_f32;
+    lds_f32* const xo = (lds_f32*)(mslot == 0 ? K0 : (mslot == 1 ? K1 : (mslot == 2 ? K2 : V0)));
+    lds_f32* const xm = (lds_f32*)V1 + mslot * 128;
+    if (half && stb) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) xo[(dt * 16 + v) * 64 + lane] = o[dt][v];
-        xm[lane] = mref;
-        xm[64 + lane] = lsum;
-      }
-      __syncthreads();
-      if (half && stb) return;
-      const float m2 = half ? xm[lane] : 0.f, l2 = half ? xm[64 + lane] : 0.f;
-      const float t1 = lsum + __shfl_xor(lsum, 32), t2 = l2 + __shfl_xor(l2, 32);
+        for (int v = 0; v < 16; ++v) xo[(dt * 16 + v) * 64 + lane] = o[dt][v];
+      xm[lane] = mref;
+      xm[64 + lane] = lsum;
+    }
+    __syncthreads();
+    if (half && stb) return;
+    if (half) {
+      const float m2 = xm[lane], l2 = xm[64 + lane];
+      const float t1 = ltot, t2 = l2 + __shfl_xor(l2, 32);
       // merge: both sides rescaled to the larger reference; a side without
       // weight (an empty subtile) takes no part
       float a1 = 1.f, a2 = 0.f;
@@ -516,19 +515,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
           a2 = 1.f;
         }
       }
-      if (half) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) o[dt][v] = o[dt][v] * a1 + xo[(dt * 16 + v) * 64 + lane] * a2;
-      }
+        for (int v = 0; v < 16; ++v) o[dt][v] = o[dt][v] * a1 + xo[(dt * 16 + v) * 64 + lane] * a2;
       ltot = t1 * a1 + t2 * a2;
-      merged = true;
     }
-  }
-  if (!merged) {
-    run(std::integral_constant<int, NST>{});
-    ltot = lsum + __shfl_xor(lsum, 32);
   }
   if (!qvalid) return;
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
