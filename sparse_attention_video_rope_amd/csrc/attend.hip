@@ -4,13 +4,15 @@
 //   o_i = sum_{j in S_c(i)} softmax_j(<q'_i, k'_j> / sqrt(d)) v_j.
 //
 // bf16 path (gfx950, wave64): one workgroup of NW waves per (cluster, 32 NW-query
-// chunk) work item (NW = 8 at head dim 128, 4 at 64); each wave owns 32 queries
-// whose Q rows stay in registers as MFMA operands.  The selected keys' K and V rows are gathered 64 at a time
-// straight into LDS (row-major, three buffers, gathered two chunks ahead).  Per 32-key subtile the wave
-// computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so each lane holds 16
-// logits of one query: the online-softmax max and sum need one cross-lane
-// exchange, and the probabilities are already laid out as the B operand of
-// O^T += V^T P^T, whose V^T operand comes from transposing LDS reads.
+// chunk) work item (NW = 8 at head dim 128, 4 at 64); each wave owns a block of
+// 32 queries whose Q rows stay in registers as MFMA operands (in a small item,
+// two waves share a block, one 32-key subtile each).  The selected keys' K and
+// V rows are gathered 64 at a time straight into LDS (row-major, three
+// buffers, gathered two chunks ahead).  Per 32-key subtile the wave computes
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so each lane holds 16 logits of
+// one query: the online-softmax max and sum need one cross-lane exchange, and
+// the probabilities are already laid out as the B operand of O^T += V^T P^T,
+// whose V^T operand comes from transposing LDS reads.
 #include <float.h>
 
 #include <type_traits>
@@ -68,7 +70,7 @@ struct AttArgs {
 //      P V product is read with ds_read_b64_tr_b16 (in each 16-lane group lane
 //      i receives 4 consecutive keys of dim i), 32 lanes per cycle read 4
 //      rows x 64 bytes, and the XOR puts the 4 rows on disjoint banks.
-// The two buffers of each tile are separate LDS arrays, so the compiler can
+// The three buffers of each tile are separate LDS arrays, so the compiler can
 // see that the loads in flight never alias the buffer being read.
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
