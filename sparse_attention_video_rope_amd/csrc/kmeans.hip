@@ -1810,13 +1810,15 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
 // together with the position of the best, and the block of the running best is
 // kept apart.
 // Error of a candidate value against the exact distance (up to the common
-// ||x||^2), M = max ||mu||: accumulation of the dpad products
-// <= dpad 2^-24 * 2 |x| M; rounding of ||mu||^2 and of the sum
-// <= 2^-23 (M^2 + 2 |x| M); the packed bits move a value v by < 2^-19 |v|.
-// EPS covers twice the first two; the packing is charged on the two values
-// compared.  A point whose best two candidates lie within that window is
-// re-decided with fp64 distances (ties to the lowest index), so the
-// labels equal the fp64 argmin.
+// ||x||^2), M = max ||mu||, with every addition (inside the MFMA and after it)
+// off by at most one ulp, i.e. 2^-23 relative (faithful rounding, which
+// covers rounding toward zero): accumulation of the dpad products
+// <= (dpad + 16) 2^-23 * 2 |x| M; rounding of ||mu||^2 and of the sum
+// <= 2^-22 (M^2 + 2 |x| M).  EPS is the sum of the two; the two values
+// compared carry at most 2 EPS between them, and the packed bits move a value
+// v by < 2^-19 |v| (charged at 2^-18 on each).  A point whose best two
+// candidates lie within that window is re-decided with fp64 distances (ties
+// to the lowest index), so the labels equal the fp64 argmin.
 // ---------------------------------------------------------------------------
 constexpr int ASG_WAVES = 12288;   // waves of one assignment, over all heads and clusterings
 
@@ -1912,7 +1914,7 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
       const float ss = fminf(fminf(second[t], os), fmaxf(best[t], ob));
       const float xn = sqrtf(xn2[t] + __shfl_xor(xn2[t], 32)) * 1.0001f;
       const float eps = gamma * 2.f * xn * M + 0x1p-22f * (M * M + 2.f * xn * M);
-      const float window = 4.f * eps + 0x1p-18f * (fabsf(bb) + fabsf(ss));
+      const float window = 2.f * eps + 0x1p-18f * (fabsf(bb) + fabsf(ss));
       const int p = pts[t];
       if (hi == 0 && p < N) lab[p] = ii;
       uint64_t amb = __ballot(hi == 0 && p < N && ss - bb <= window);
