@@ -1872,6 +1872,19 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
     }
     float best[2] = {FLT_MAX, FLT_MAX}, second[2] = {FLT_MAX, FLT_MAX};
     int bcb[2] = {0, 0};
+    // Blocks that may hold the least exact distance: a block is marked when its
+    // best value lies within wmark of the running best (a bound of the final
+    // window, set before the final best and second are known: |v| <= |x|^2 +
+    // 2 |x| M + M^2), so the marks cover every block with a value within the
+    // window of the final best.  The re-decision only visits marked blocks.
+    uint32_t live[2] = {0u, 0u};
+    float wmark[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float xn = sqrtf(xn2[t] + __shfl_xor(xn2[t], 32)) * 1.0001f;
+      const float eps = gamma * 2.f * xn * M + 0x1p-22f * (M * M + 2.f * xn * M);
+      wmark[t] = 2.f * eps + 0x1p-17f * (xn * xn + 2.f * xn * M + M * M);
+    }
     for (int cb = 0; cb < ncb; ++cb) {
       f32x16_t cn;   // ||mu||^2 of rows cb*32 + 8*(v/4) + 4*hi + v%4
 #pragma unroll
@@ -1899,6 +1912,7 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
         }
         second[t] = fminf(fminf(second[t], ks1), fmaxf(best[t], kb1));
         if (kb1 < best[t]) { best[t] = kb1; bcb[t] = cb; }
+        if (kb1 <= best[t] + wmark[t]) live[t] |= 1u << cb;
       }
     }
 #pragma unroll
@@ -1915,6 +1929,7 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
       const float xn = sqrtf(xn2[t] + __shfl_xor(xn2[t], 32)) * 1.0001f;
       const float eps = gamma * 2.f * xn * M + 0x1p-22f * (M * M + 2.f * xn * M);
       const float window = 2.f * eps + 0x1p-18f * (fabsf(bb) + fabsf(ss));
+      const uint32_t lvm = live[t] | __shfl_xor(live[t], 32);
       const int p = pts[t];
       if (hi == 0 && p < N) lab[p] = ii;
       uint64_t amb = __ballot(hi == 0 && p < N && ss - bb <= window);
@@ -1931,7 +1946,17 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         double bd = __builtin_inf();
         int bc = 0x7FFFFFFF;
-        for (int c = lane; c < C; c += 64) {
+        // the marked blocks of the point, two at a time (lanes 0-31 the
+        // first, 32-63 the second; lane col takes row col of its block)
+        uint32_t mm = __shfl(lvm, L);
+        while (mm) {
+          const int cb0 = __ffs(mm) - 1;
+          mm &= mm - 1;
+          const int cb1 = mm ? __ffs(mm) - 1 : -1;
+          if (mm) mm &= mm - 1;
+          const int cbl = hi ? cb1 : cb0;
+          const int c = cbl * 32 + col;
+          if (cbl < 0 || c >= C) continue;
           const uint16_t* row = sc + c * ldc;
           double accd = 0.0;
           // 8 channels per 16-byte read (rows are 16-byte aligned: ldc = dpad
