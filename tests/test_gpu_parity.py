@@ -117,6 +117,58 @@ def upload_oracle_plan(w, heads, pl):
     pl.status.zero_()
 
 
+@pytest.mark.parametrize("w", [w for w in SMALL if w.name in ("s128c", "s64c")], ids=["s128c", "s64c"])
+def test_lloyd_ties_across_blocks_exact(w):
+    """Assignment to centroids with exact and near duplicates in other 32-centroid blocks.
+
+    The initial centroids repeat a set of points three times, so the copies of a
+    centroid sit in different MFMA blocks.  In each copy one channel is set to
+    0, except in the last third, where it is 2^-20: the first two thirds are
+    exact duplicates (every point ties; the lowest index must win), and a point
+    is nearer the last copy exactly when that channel of it is positive, by
+    about 2^-19 |x_ch|, far below what the bf16 filter resolves.  With no Lloyd
+    round the labels must equal the oracle's fp64 argmin exactly, with no
+    near-tie allowance: these points are decided by the exact re-decision and
+    its block marks alone.
+    """
+    say("lloyd ties across blocks", w.name)
+    q, k, v = workloads.generate(w)
+    offs = O.subspace_offsets(w.split)
+    rng = np.random.default_rng(7)
+    init_q, init_k = [], []
+    heads = oracle_heads(w)
+    for bh, o in enumerate(heads):
+        def tripled(X, C):
+            nb = C // 3
+            base = X[rng.choice(X.shape[0], nb, replace=False)].astype(np.float64)
+            ch = rng.integers(0, X.shape[1], size=nb)
+            base[np.arange(nb), ch] = 0.0
+            near = base.copy()
+            near[np.arange(nb), ch] = 2.0 ** -20
+            return np.concatenate([base, base, near, base[: C - 3 * nb]], axis=0)[:C]
+        init_q.append(tripled(o["q_rope"], w.Cq))
+        kc = np.zeros((w.Cm, w.d))
+        for off, dm in zip(offs, w.split):
+            kc[:, off:off + dm] = tripled(o["k_rope"][:, off:off + dm], w.Cm)
+        init_k.append(kc)
+    g = run_gpu(w.with_(iters=0), init_q=np.stack(init_q), init_k=np.stack(init_k), inputs=(q, k, v))
+    for bh in range(w.BH):
+        # the reference assigns the GPU's own RoPE output (the RoPE comparison
+        # is a test of its own)
+        ref = O.kmeans(g["q_rope"][bh], w.Cq, 0, w.dtype, 0, bh, 0, init=init_q[bh])
+        assert np.array_equal(g["q_labels"][bh], ref["labels"]), f"head {bh} query labels"
+        for m, (off, dm) in enumerate(zip(offs, w.split)):
+            X = g["k_rope"][bh][:, off:off + dm]
+            refk = O.kmeans(X, w.Cm, 0, w.dtype, 0, bh, 1 + m, init=init_k[bh][:, off:off + dm])
+            assert np.array_equal(g["k_codes"][bh][:, m], refk["labels"]), f"head {bh} key codes {m}"
+        # the duplicates really tie (no label of the second third), and both
+        # sides of the near pairs occur
+        nb = w.Cq // 3
+        lab = g["q_labels"][bh]
+        assert not np.any((lab >= nb) & (lab < 2 * nb))
+        assert np.any(lab < nb) and np.any((lab >= 2 * nb) & (lab < 3 * nb))
+
+
 @pytest.mark.parametrize("rho", [0.9, 1.0, 0.3])
 @pytest.mark.parametrize("w", SMALL, ids=IDS)
 def test_attend_on_oracle_plan(w, rho):
