@@ -64,8 +64,14 @@ constexpr int SEED_NT = 1024;
 constexpr int SEED_NW = SEED_NT / 64;
 constexpr int SEED_RG = 8;                 // rounds per group
 constexpr int SEED_MAX_GROUPS = 32;        // N <= 2^18
-constexpr int SEED_CACHE_BYTES = 48 * 1024;
 constexpr int SEED_LIST = 512;             // list entries per wave
+// the chosen centres' rows are kept in LDS when they fit beside the lists and
+// the kernel's static arrays (cvec, cvs, cc, chosen, wsum, gscr, scalars)
+constexpr int SEED_CACHE_BYTES = 40 * 1024;
+constexpr int SEED_STATIC_LDS = 8 * 128 + 8 * 136 + 12 * MAX_C + 8 * SEED_MAX_GROUPS * (SEED_NT / 64) +
+                                8 * SEED_RG * 64 + 64;
+static_assert((SEED_NT / 64) * SEED_LIST * 12 + SEED_CACHE_BYTES + SEED_STATIC_LDS <= 160 * 1024,
+              "k-means++ LDS of one workgroup");
 constexpr uint32_t NR_MARK = 0x8000u;      // point is a chosen centre
 constexpr uint32_t NR_ID = 0x7FFFu;
 
@@ -155,6 +161,7 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
   int32_t* sd = seeds + ((size_t)bh * 4 + m) * g.Cmax;
 
   __shared__ double cvec[128];
+  __shared__ double cvs[136];   // centre row shifted right by sh channels, zero outside the subspace
   __shared__ double cc[MAX_C];
   __shared__ int32_t chosen[MAX_C];
   __shared__ double wsum[SEED_MAX_GROUPS * SEED_NW];
@@ -171,10 +178,16 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int R = (N + SEED_NT - 1) / SEED_NT;
   const int G = (R + SEED_RG - 1) / SEED_RG;
-  // 16-byte row loads: rows 16-byte aligned and the rounded-up width inside the row
-  const bool vec16 = sizeof(T) == 2 && ((off * 2) % 16 == 0) && ((d * 2) % 16 == 0) && off + ((dm + 7) & ~7) <= d;
-  int lpr = 1;   // lanes per row: power of two covering ceil(dm / 8) 16-byte chunks
-  while (lpr * 8 < dm) lpr <<= 1;
+  // 16-byte row loads: the aligned 8-channel pieces that cover the subspace,
+  // starting sh = off mod 8 channels before it (even: RoPE pairs), all inside
+  // the row.  Channel pair j of piece p is subspace channel 8 p + 2 j - sh;
+  // pairs outside 0 .. dm - 1 are zeroed in the loaded word and meet a zero
+  // in cvs, so they add exact zeros and the loop needs no per-channel branch.
+  const int sh = off & 7;
+  const bool vec16 = sizeof(T) == 2 && ((d * 2) % 16 == 0) && (sh % 2 == 0) && (dm % 2 == 0) &&
+                     off - sh + ((dm + sh + 7) & ~7) <= d;
+  int lpr = 1;   // lanes per row: power of two covering ceil((dm + sh) / 8) 16-byte pieces
+  while (lpr * 8 < dm + sh) lpr <<= 1;
   const uint64_t stream = ((uint64_t)bh * 4 + m) << 20;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   // point of round k of the group starting at round r0 held by this thread:
@@ -482,6 +495,10 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
       cvec[tid] = Elem<T>::ld(&xv);
       if (cached) cache[(size_t)s * cld + tid] = xv;
     }
+    if (tid < 136) {
+      const int ch = tid - sh;
+      cvs[tid] = ch >= 0 && ch < dm ? Elem<T>::ld(X + (size_t)ci * d + ch) : 0.0;
+    }
     __syncthreads();
     for (int a = tid; a < s; a += SEED_NT) {
       double acc = 0.0;
@@ -543,8 +560,9 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
 #pragma unroll
               for (int u = 0; u < 4; ++u) {
                 const int e = e0 + u * rpi + slot;
-                b[u] = e < nl && sub * 8 < dm ? *reinterpret_cast<const uint4*>(X + (size_t)lp[e] * d + sub * 8)
-                                              : make_uint4(0, 0, 0, 0);
+                b[u] = e < nl && sub * 8 < dm + sh
+                           ? *reinterpret_cast<const uint4*>(X - sh + (size_t)lp[e] * d + sub * 8)
+                           : make_uint4(0, 0, 0, 0);
               }
 #pragma unroll
               for (int u = 0; u < 4; ++u) {
@@ -552,13 +570,11 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
                 double acc = 0.0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                  const int ch = sub * 8 + 2 * j;
-                  if (ch < dm) {
-                    const double p0 = (double)__uint_as_float(w[j] << 16) - cvec[ch];
-                    const double p1 = (double)__uint_as_float(w[j] & 0xFFFF0000u) - cvec[ch + 1];
-                    acc = fma(p0, p0, acc);
-                    acc = fma(p1, p1, acc);
-                  }
+                  const uint32_t wj = (uint32_t)(sub * 8 + 2 * j - sh) < (uint32_t)dm ? w[j] : 0u;
+                  const double p0 = (double)__uint_as_float(wj << 16) - cvs[sub * 8 + 2 * j];
+                  const double p1 = (double)__uint_as_float(wj & 0xFFFF0000u) - cvs[sub * 8 + 2 * j + 1];
+                  acc = fma(p0, p0, acc);
+                  acc = fma(p1, p1, acc);
                 }
                 acc = group_sum_dpp(acc, lpr);
                 const int e = e0 + u * rpi + slot;
