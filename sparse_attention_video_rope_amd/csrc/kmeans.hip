@@ -111,7 +111,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 }
 
 // Exchange area of one clustering when W workgroups share its points
-// (SeedSync::Wq or Wk > 1, a cooperative launch: all of them are resident at once).
+// (SeedSync::W[m] > 1, a cooperative launch: all of them are resident at once).
 // Each workgroup owns a contiguous run of groups; per draw it publishes the
 // sum of its D^2, waits for the others, and the workgroup holding the
 // crossing publishes the drawn index, tagged with the draw, which the others
@@ -121,12 +121,30 @@ constexpr uint32_t SEED_SPIN_LIMIT = 1u << 18;   // polls before giving up: well
 struct SeedSync {
   char* base;        // [BH][4] areas of SEED_SYNC_BYTES: counter, drawn index, part[2][32], lowest[MAX_C]
   int32_t* abort;    // set when a wait ran out (every later wait is then skipped)
-  int Wq, Wk;        // workgroups per query / key clustering (1 and 1: no exchange)
-  int flat;          // 1: blockIdx.x enumerates the nbh*Wq query workgroups, then the
-                     // nk*nbh*Wk key workgroups of heads bh0 .. bh0+nbh-1; 0: grid (BH, 1+nk)
-                     // with one each
+  int W[4];          // workgroups per clustering m of a head (all 1: no exchange)
+  int flat;          // 1: blockIdx.x enumerates the nbh*W[0] query workgroups, then per head
+                     // the W[1] + .. + W[nk] key workgroups (m ascending), heads bh0 ..
+                     // bh0+nbh-1; 0: grid (BH, 1+nk) with one each
   int bh0, nbh;      // heads of this launch (flat)
 };
+
+// (m, head, workgroup within the clustering) of this workgroup
+__device__ __forceinline__ void seed_block(const SeedSync& sy, int nk, int& m, int& bh, int& wg) {
+  m = blockIdx.y; bh = blockIdx.x; wg = 0;
+  if (!sy.flat) return;
+  const int b = blockIdx.x, w0 = sy.W[0], nq = sy.nbh * w0;
+  if (b < nq) {
+    m = 0; bh = b / w0; wg = b - bh * w0;
+  } else {
+    const int w1 = sy.W[1], w2 = nk >= 2 ? sy.W[2] : 0, w3 = nk >= 3 ? sy.W[3] : 0;
+    const int kw = w1 + w2 + w3, r0 = b - nq;
+    bh = r0 / kw;
+    const int r = r0 - bh * kw;
+    m = r < w1 ? 1 : (r < w1 + w2 ? 2 : 3);
+    wg = r - (m == 1 ? 0 : (m == 2 ? w1 : w1 + w2));
+  }
+  bh += sy.bh0;
+}
 
 __global__ void seed_sync_init_kernel(char* base, int chains, int32_t* abort) {
   const int c = blockIdx.x;
@@ -142,18 +160,9 @@ __global__ __launch_bounds__(SEED_NT) void seed_kernel(const T* __restrict__ qr,
                                                        double* __restrict__ d2all, uint16_t* __restrict__ nearall,
                                                        int32_t* __restrict__ seeds, float* __restrict__ qcent,
                                                        float* __restrict__ kcent, SeedSync sy) {
-  int m = blockIdx.y, bh = blockIdx.x, wg = 0;
-  if (sy.flat) {
-    const int b = blockIdx.x, nq = sy.nbh * sy.Wq;
-    if (b < nq) {
-      m = 0; bh = b / sy.Wq; wg = b - bh * sy.Wq;
-    } else {
-      const int c = (b - nq) / sy.Wk;
-      wg = (b - nq) - c * sy.Wk; bh = c / g.nk; m = 1 + (c - bh * g.nk);
-    }
-    bh += sy.bh0;
-  }
-  const int W = m == 0 ? sy.Wq : sy.Wk;
+  int m, bh, wg;
+  seed_block(sy, g.nk, m, bh, wg);
+  const int W = m == 0 ? sy.W[0] : (m == 1 ? sy.W[1] : (m == 2 ? sy.W[2] : sy.W[3]));
   const int N = g.N, d = g.d, dm = g.dm[m], off = g.off[m], C = g.C[m];
   const T* X = (m == 0 ? qr : kr) + (size_t)bh * N * d + off;
   double* D2g = d2all + ((size_t)bh * 4 + m) * N;
@@ -974,20 +983,11 @@ template <bool VEC>
 __global__ __launch_bounds__(SL_NT) void seedl_kernel(const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
                                                       Geo g, double* __restrict__ d2all, int32_t* __restrict__ seeds,
                                                       float* __restrict__ qcent, float* __restrict__ kcent, SeedSync sy) {
-  int m = blockIdx.y, bh = blockIdx.x, wg = 0;
-  if (sy.flat) {
-    const int b = blockIdx.x, nq = sy.nbh * sy.Wq;
-    if (b < nq) {
-      m = 0; bh = b / sy.Wq; wg = b - bh * sy.Wq;
-    } else {
-      const int c = (b - nq) / sy.Wk;
-      wg = (b - nq) - c * sy.Wk; bh = c / g.nk; m = 1 + (c - bh * g.nk);
-    }
-    bh += sy.bh0;
-  }
+  int m, bh, wg;
+  seed_block(sy, g.nk, m, bh, wg);
   // W workgroups share the clustering: this one owns the points
   // [pbase, pbase + N) (local indices below; drawn centres are global)
-  const int W = m == 0 ? sy.Wq : sy.Wk;
+  const int W = m == 0 ? sy.W[0] : (m == 1 ? sy.W[1] : (m == 2 ? sy.W[2] : sy.W[3]));
   const int Nall = g.N;
   const int pbase = (int)((int64_t)wg * Nall / W);
   const int N = (int)((int64_t)(wg + 1) * Nall / W) - pbase;
@@ -2122,8 +2122,8 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
       SeedSync sy;
       sy.base = w.seed_sync;
       sy.abort = status + 2;
-      sy.Wq = Wq;
-      sy.Wk = Wk;
+      sy.W[0] = Wq;
+      sy.W[1] = sy.W[2] = sy.W[3] = Wk;
       sy.flat = 1;
       sy.bh0 = 0;
       sy.nbh = g.BH;
@@ -2140,7 +2140,7 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
         if (hipLaunchCooperativeKernel(fn, dim3(nblk), dim3(SL_NT), args, (unsigned)need, s) == hipSuccess) return;
         (void)hipGetLastError();
       }
-      sy.Wq = sy.Wk = 1;
+      sy.W[0] = sy.W[1] = sy.W[2] = sy.W[3] = 1;
       sy.flat = 0;
       if (vec)
         seedl_kernel<true><<<grid, SL_NT, need, s>>>(q16, k16, g, d2, sd, qc, kc, sy);
@@ -2189,35 +2189,60 @@ static void seed_launch(const Geo& g, const T* qr, const T* kr, const Workspace&
   //
   // Several workgroups per clustering when the chip holds them all at once
   // (a cooperative launch guarantees that, or fails and one is used), with
-  // the point state in global memory.  The slots left after every clustering
-  // has Wk go to the query clusterings (the widest rows).  (One workgroup per
+  // the point state in global memory.  A draw of clustering m costs about
+  // ceil(G / W[m]) groups times (16 + d_m) (the state of every point, the
+  // rows of the points that may move): the resident slots go, a head's
+  // worth at a time, to the clustering with the largest such cost, each step
+  // lowering its groups per workgroup by one; slots left at the end go to
+  // the query clusterings (the widest rows).  (One workgroup per
   // 8192-point group with the state in registers, in launches of a few heads
   // whose rows stay in the Infinity Cache, measured 103.7 ms instead of
   // 56.8 ms at the Hunyuan-like size: the exchange among 15 workgroups per
   // draw and the six sequential launches cost more than the state traffic.)
   const auto kern = seed_kernel<T, false>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  int Wq = 1, Wk = 1, per_cu = 0;
-  if (can_coop && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, SEED_NT, lds) == hipSuccess) {
+  int Wm[4] = {1, 1, 1, 1}, per_cu = 0;
+  if (can_coop && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, SEED_NT, lds) == hipSuccess &&
+      chains <= ncu * per_cu) {
     const int cap = ncu * per_cu;
-    Wk = max(1, min(G, cap / chains));
-    Wq = max(Wk, min(G, (cap - g.nk * g.BH * Wk) / g.BH));
+    int used = chains;
+    auto groups = [&](int m) { return (G + Wm[m] - 1) / Wm[m]; };
+    // one step for clustering m: the fewest workgroups with one group less each
+    auto step = [&](int m) -> bool {
+      const int k = groups(m) - 1;
+      if (k < 1) return false;
+      const int wn = (G + k - 1) / k;
+      if (used + (wn - Wm[m]) * g.BH > cap) return false;
+      used += (wn - Wm[m]) * g.BH;
+      Wm[m] = wn;
+      return true;
+    };
+    for (;;) {
+      int mx = -1;
+      double cmax = 0.0;
+      for (int m = 0; m < ncl; ++m) {
+        const double c = (double)groups(m) * (16 + g.dm[m]);
+        if (groups(m) > 1 && c > cmax) { cmax = c; mx = m; }
+      }
+      if (mx < 0 || !step(mx)) break;
+    }
+    while (step(0)) {}
   }
-  sy.Wq = Wq;
-  sy.Wk = Wk;
+  for (int m = 0; m < 4; ++m) sy.W[m] = m < ncl ? Wm[m] : 1;
   sy.flat = 1;
   sy.bh0 = 0;
   sy.nbh = g.BH;
-  if (Wq > 1 || Wk > 1) {
+  int nblk = 0;
+  for (int m = 0; m < ncl; ++m) nblk += g.BH * Wm[m];
+  if (nblk > chains) {
     void* args[] = {(void*)&qr, (void*)&kr, (void*)&g, (void*)&d2, (void*)&nr, (void*)&sd, (void*)&qc, (void*)&kc,
                     (void*)&sy};
-    const unsigned nblk = (unsigned)(g.BH * Wq + g.nk * g.BH * Wk);
-    if (hipLaunchCooperativeKernel((const void*)kern, dim3(nblk), dim3(SEED_NT), args, (unsigned)lds, s) ==
+    if (hipLaunchCooperativeKernel((const void*)kern, dim3((unsigned)nblk), dim3(SEED_NT), args, (unsigned)lds, s) ==
         hipSuccess)
       return;
     (void)hipGetLastError();
   }
-  sy.Wq = sy.Wk = 1;
+  sy.W[0] = sy.W[1] = sy.W[2] = sy.W[3] = 1;
   sy.flat = 0;
   kern<<<grid, SEED_NT, lds, s>>>(qr, kr, g, d2, nr, sd, qc, kc, sy);
 }
