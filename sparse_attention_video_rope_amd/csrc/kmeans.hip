@@ -1858,8 +1858,9 @@ __device__ __forceinline__ bf16x8_t load_row8(const uint16_t* __restrict__ row, 
 template <int KB>
 __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int N, int d, int dm, int C, int Cpad,
                                              bool vec16, const uint16_t* __restrict__ sc, int ldc,
-                                             const float* __restrict__ scn, float M, double* __restrict__ xs,
-                                             int32_t* __restrict__ lab, int gw, int gstride) {
+                                             const float* __restrict__ scn, float M, int32_t* __restrict__ lab,
+                                             int gw, int gstride, int4* __restrict__ amb,
+                                             int32_t* __restrict__ amb_ctr, int bhm) {
   const int lane = threadIdx.x & 63, hi = lane >> 5, col = lane & 31;
   const int ncb = Cpad / 32;
   const float gamma = (float)(KB * 16 + 16) * 0x1p-23f;
@@ -1948,64 +1949,87 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
       const uint32_t lvm = live[t] | __shfl_xor(live[t], 32);
       const int p = pts[t];
       if (hi == 0 && p < N) lab[p] = ii;
-      uint64_t amb = __ballot(hi == 0 && p < N && ss - bb <= window);
-      while (amb) {
-        const int L = __ffsll((unsigned long long)amb) - 1;
-        amb &= amb - 1;
-        const int pp = __shfl(p, L);
-        // the point's channels, zero up to the padded width (the table rows
-        // are zero there too)
-        const int dp = KB * 16;
-        for (int ch = lane; ch < dp; ch += 64) xs[ch] = ch < dm ? (double)bf16_to_f32(X[(size_t)pp * d + ch]) : 0.0;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        double bd = __builtin_inf();
-        int bc = 0x7FFFFFFF;
-        // the marked blocks of the point, two at a time (lanes 0-31 the
-        // first, 32-63 the second; lane col takes row col of its block)
-        uint32_t mm = __shfl(lvm, L);
-        while (mm) {
-          const int cb0 = __ffs(mm) - 1;
-          mm &= mm - 1;
-          const int cb1 = mm ? __ffs(mm) - 1 : -1;
-          if (mm) mm &= mm - 1;
-          const int cbl = hi ? cb1 : cb0;
-          const int c = cbl * 32 + col;
-          if (cbl < 0 || c >= C) continue;
-          const uint16_t* row = sc + c * ldc;
-          double accd = 0.0;
-          // 8 channels per 16-byte read (rows are 16-byte aligned: ldc = dpad
-          // + 8 with dpad a multiple of 16), added in channel order; the padding
-          // channels add exact zeros.  Not unrolled: this rare path must not
-          // raise the kernel's register count.
-#pragma unroll 1
-          for (int c8 = 0; c8 < dp; c8 += 8) {
-            const u32x4_t u = *reinterpret_cast<const u32x4_t*>(row + c8);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t wj = u[j];
-              // LDS holds -2 mu; mu = -0.5 * that, exactly
-              const double d0 = xs[c8 + 2 * j] + 0.5 * (double)__uint_as_float(wj << 16);
-              const double d1 = xs[c8 + 2 * j + 1] + 0.5 * (double)__uint_as_float(wj & 0xFFFF0000u);
-              accd = fma(d0, d0, accd);
-              accd = fma(d1, d1, accd);
-            }
-          }
-          if (accd < bd) { bd = accd; bc = c; }
-        }
-#pragma unroll
-        for (int o2 = 32; o2 >= 1; o2 >>= 1) {
-          const double od = __shfl_xor(bd, o2);
-          const int oc = __shfl_xor(bc, o2);
-          if (od < bd || (od == bd && oc < bc)) { bd = od; bc = oc; }
-        }
-        if (lane == 0) lab[pp] = bc;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // near ties: appended to the assignment's list with their marked
+      // blocks; asg_exact_kernel re-decides them, spread over the whole chip
+      const bool near = hi == 0 && p < N && ss - bb <= window;
+      const uint64_t nm = __ballot(near);
+      if (nm) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(amb_ctr, __popcll(nm));
+        base = __shfl(base, 0);
+        if (near)
+          amb[base + __popcll(nm & ((1ull << lane) - 1ull))] = make_int4(bhm, p, (int)lvm, 0);
       }
     }
+  }
+}
+
+// Exact re-decision of the near ties of one assignment (the list written by
+// assign2_kernel; every entry is one point, so the order of the list does
+// not matter): fp64 distances to the centroids of the marked blocks, in
+// channel order, ties to the lowest index; the label is overwritten.  One
+// wave per entry, two marked blocks at a time (lanes 0-31 the first, 32-63
+// the second; lane col takes row col of its block).  The bf16 centroid rows
+// are read from global memory 16 bytes at a time (rows zero padded to dpad).
+constexpr int AEX_NT = 256;
+__global__ __launch_bounds__(AEX_NT) void asg_exact_kernel(const uint16_t* __restrict__ qr,
+                                                            const uint16_t* __restrict__ kr, Geo g,
+                                                            const uint16_t* __restrict__ cbf,
+                                                            const int4* __restrict__ amb,
+                                                            const int32_t* __restrict__ amb_ctr,
+                                                            int32_t* __restrict__ labels) {
+  __shared__ double xsh[AEX_NT / 64][128];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hi = lane >> 5, col = lane & 31;
+  double* xs = xsh[wv];
+  const int n = *amb_ctr;
+  for (int e = blockIdx.x * (AEX_NT / 64) + wv; e < n; e += gridDim.x * (AEX_NT / 64)) {
+    const int4 en = amb[e];
+    const int m = en.x & 3, bh = en.x >> 2, pp = en.y;
+    uint32_t mm = (uint32_t)en.z;
+    const int dm = g.dm[m], C = g.C[m], dp = g.dpad[m];
+    const uint16_t* X = (m == 0 ? qr : kr) + ((size_t)bh * g.N + pp) * g.d + g.off[m];
+    // the point's channels, zero up to the padded width (the centroid rows
+    // are zero there too)
+    for (int ch = lane; ch < dp; ch += 64) xs[ch] = ch < dm ? (double)bf16_to_f32(X[ch]) : 0.0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint16_t* gc = cbf + ((size_t)bh * 4 + m) * g.CmaxPad * g.DPmax;
+    double bd = __builtin_inf();
+    int bc = 0x7FFFFFFF;
+    while (mm) {
+      const int cb0 = __ffs(mm) - 1;
+      mm &= mm - 1;
+      const int cb1 = mm ? __ffs(mm) - 1 : -1;
+      if (mm) mm &= mm - 1;
+      const int cbl = hi ? cb1 : cb0;
+      const int c = cbl * 32 + col;
+      if (cbl < 0 || c >= C) continue;
+      const uint16_t* row = gc + (size_t)c * g.DPmax;
+      double accd = 0.0;
+      for (int c8 = 0; c8 < dp; c8 += 8) {
+        const u32x4_t u = *reinterpret_cast<const u32x4_t*>(row + c8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t wj = u[j];
+          const double d0 = xs[c8 + 2 * j] - (double)__uint_as_float(wj << 16);
+          const double d1 = xs[c8 + 2 * j + 1] - (double)__uint_as_float(wj & 0xFFFF0000u);
+          accd = fma(d0, d0, accd);
+          accd = fma(d1, d1, accd);
+        }
+      }
+      if (accd < bd) { bd = accd; bc = c; }
+    }
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+      const double od = __shfl_xor(bd, o2);
+      const int oc = __shfl_xor(bc, o2);
+      if (od < bd || (od == bd && oc < bc)) { bd = od; bc = oc; }
+    }
+    if (lane == 0 && bc != 0x7FFFFFFF) labels[((size_t)bh * 4 + m) * g.N + pp] = bc;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -2024,7 +2048,8 @@ __global__ __launch_bounds__(NT) void assign2_kernel(const uint16_t* __restrict_
                                                          const uint16_t* __restrict__ kr, Geo g,
                                                          const uint16_t* __restrict__ cbf,
                                                          const float* __restrict__ cnorm,
-                                                         int32_t* __restrict__ labels, AsgSplit split) {
+                                                         int32_t* __restrict__ labels, AsgSplit split,
+                                                         int4* __restrict__ amb, int32_t* __restrict__ amb_ctr) {
   const int bx = blockIdx.x, bh = blockIdx.z;
   const int m = bx < split.start[1] ? 0 : (bx < split.start[2] ? 1 : (bx < split.start[3] ? 2 : 3));
   const int part = bx - (m == 0 ? 0 : (m == 1 ? split.start[1] : (m == 2 ? split.start[2] : split.start[3])));
@@ -2035,7 +2060,6 @@ __global__ __launch_bounds__(NT) void assign2_kernel(const uint16_t* __restrict_
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* sc = reinterpret_cast<uint16_t*>(smem_raw);                               // [Cpad][ldc] -2 mu
   float* scn = reinterpret_cast<float*>(smem_raw + (size_t)Cpad * ldc * 2);           // [Cpad] ||mu||^2
-  double* xsh = reinterpret_cast<double*>(smem_raw + (size_t)Cpad * ldc * 2 + (size_t)Cpad * 4);   // [NT/64][128]
   __shared__ float red[NT / 64];
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint16_t* gc = cbf + ((size_t)bh * 4 + m) * g.CmaxPad * g.DPmax;
@@ -2059,12 +2083,12 @@ __global__ __launch_bounds__(NT) void assign2_kernel(const uint16_t* __restrict_
   const bool vec16 = ((off * 2) % 16 == 0) && ((d * 2) % 16 == 0);
   int32_t* lab = labels + ((size_t)bh * 4 + m) * N;
   const int gw = part * (NT / 64) + wv, gstride = nparts * (NT / 64);
-  double* xs = xsh + wv * 128;
   const int kbn = dpad / 16;
   auto run = [&](auto kb) {
     constexpr int KB = decltype(kb)::value;
     if constexpr (KB <= KBMAX)
-      if (kbn == KB) assign_tiles<KB>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, xs, lab, gw, gstride);
+      if (kbn == KB)
+        assign_tiles<KB>(X, N, d, dm, C, Cpad, vec16, sc, ldc, scn, M, lab, gw, gstride, amb, amb_ctr, bh * 4 + m);
   };
   run(std::integral_constant<int, 1>{});
   run(std::integral_constant<int, 2>{});
@@ -2269,6 +2293,7 @@ hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Wor
                          hipStream_t s) {
   int32_t* out = labels_of(g, w, iter);
   if (g.bf16) {
+    if (iter == 0) fill_i32_kernel<<<(g.iters + 256) / 256, 256, 0, s>>>(w.amb_cnt, 0, (size_t)g.iters + 1);
     // ASG_WAVES waves in all, shared among the clusterings of a head in
     // proportion to Cpad (dpad / 16 + 1) (MFMA blocks plus the per-candidate
     // selection work; equal shares left the query clustering, with the widest
@@ -2294,11 +2319,10 @@ hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Wor
       const int vgpr_waves = kbmax <= 4 ? 4 : 3;   // waves per SIMD the kernel's registers allow
       int nt = 256, best = 0;
       for (int cand = 256; cand <= 768; cand += 256) {
-        const int bytes = table + (cand / 64) * 128 * 8;
-        const int per_simd = min((kLdsCU / bytes) * (cand / 256), vgpr_waves);
+        const int per_simd = min((kLdsCU / (table + 1024)) * (cand / 256), vgpr_waves);
         if (per_simd > best) { best = per_simd; nt = cand; }
       }
-      const int bytes = table + (nt / 64) * 128 * 8;
+      const int bytes = table;
       AsgSplit sp;
       sp.start[0] = 0;
       for (int m = 0; m < 4; ++m) {
@@ -2309,7 +2333,8 @@ hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Wor
       auto go = [&](auto kern) {
         if (bytes > 64 * 1024)
           (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-        kern<<<grid, nt, bytes, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, out, sp);
+        kern<<<grid, nt, bytes, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.cnorm, out, sp, w.amb,
+                                     w.amb_cnt + iter);
       };
       if (kbmax == 2) {
         if (nt == 256) go(assign2_kernel<2, 256>); else if (nt == 512) go(assign2_kernel<2, 512>);
@@ -2332,6 +2357,9 @@ hipError_t launch_assign(const Geo& g, const void* qr, const void* kr, const Wor
     } else {
       launch(0, 1 + g.nk);
     }
+    // the near ties of this assignment, over the whole chip
+    asg_exact_kernel<<<1024, AEX_NT, 0, s>>>((const uint16_t*)qr, (const uint16_t*)kr, g, w.cbf, w.amb,
+                                             w.amb_cnt + iter, out);
   } else {
     dim3 grid((g.N + 255) / 256, 1 + g.nk, g.BH);
     assign_exact_f32_kernel<<<grid, 256, 0, s>>>((const float*)qr, (const float*)kr, g, w.qcent, w.kcent, out);

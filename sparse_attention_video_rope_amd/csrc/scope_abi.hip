@@ -81,6 +81,8 @@ Workspace carve(const Geo& g, const scope_plan_t* plan, char* base) {
   w.htot = (int64_t*)take(8 * BH);
   w.hist1 = (int32_t*)take(4 * BH * g.Cq * (size_t)SEL_NB);
   w.seed_sync = (char*)take((size_t)SEED_SYNC_BYTES * BH * 4);
+  w.amb = (int4*)take(16 * BH * 4 * N);
+  w.amb_cnt = (int32_t*)take(4 * (size_t)(g.iters + 1));
   if (g.permute) {
     const size_t rows = (size_t)(g.bf16 ? 2 : 4) * BH * N * g.d;
     w.qperm = take(rows);
@@ -122,8 +124,8 @@ static scope_status validate(const scope_params* p) {
   if ((p->flags & SCOPE_FULL_DIM_KEYS) && (p->flags & SCOPE_PERMUTE_CHANNELS)) return SCOPE_ERR_INVALID;
   if (p->dtype == SCOPE_BF16 && !(p->flags & SCOPE_DENSE)) {
     // the bf16 assignment keeps a clustering's whole centroid table in the
-    // LDS of one CU (bf16 rows padded to 16 channels + 8, fp32 norms, and at
-    // least 4 waves' 1 KB refinement rows)
+    // LDS of one CU (bf16 rows padded to 16 channels + 8, fp32 norms, and the
+    // kernel's own 4 KB)
     const Geo g = make_geo(*p);
     for (int m = 0; m <= g.nk; ++m)
       if ((size_t)g.Cpad[m] * (g.dpad[m] + 8) * 2 + (size_t)g.Cpad[m] * 4 + 4 * 1024 > MAX_ASSIGN_LDS)

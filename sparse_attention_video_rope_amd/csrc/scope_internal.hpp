@@ -79,6 +79,8 @@ struct Workspace {
   int64_t* htot;                // [BH] per-head total of r_c, then the head's offset in sel_idx
   int32_t* hist1;               // [BH][Cq][SEL_NB] level-1 key counts of the Top-p pass (reused by the final selection)
   char* seed_sync;              // [BH][4] k-means++ exchange areas (SEED_SYNC_BYTES) when a clustering spans workgroups
+  int4* amb;                    // [BH * 4 * N] near-tie points of one Lloyd assignment: (bh * 4 + m, point, block marks)
+  int32_t* amb_cnt;             // [iters + 1] entries of amb per assignment (zeroed before the first)
   void* qperm;                  // [BH][N][d] q_rope with reordered channels (SCOPE_PERMUTE_CHANNELS only)
   void* kperm;                  // [BH][N][d] k_rope likewise
   size_t bytes;
