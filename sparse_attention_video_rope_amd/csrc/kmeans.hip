@@ -1970,7 +1970,8 @@ __device__ __forceinline__ void assign_tiles(const uint16_t* __restrict__ X, int
 // channel order, ties to the lowest index; the label is overwritten.  One
 // wave per entry, two marked blocks at a time (lanes 0-31 the first, 32-63
 // the second; lane col takes row col of its block).  The bf16 centroid rows
-// are read from global memory 16 bytes at a time (rows zero padded to dpad).
+// are read from global memory, a whole row (zero padded to dpad) in flight
+// at once in 16-byte pieces.
 constexpr int AEX_NT = 256;
 __global__ __launch_bounds__(AEX_NT) void asg_exact_kernel(const uint16_t* __restrict__ qr,
                                                             const uint16_t* __restrict__ kr, Geo g,
@@ -2006,16 +2007,24 @@ __global__ __launch_bounds__(AEX_NT) void asg_exact_kernel(const uint16_t* __res
       const int c = cbl * 32 + col;
       if (cbl < 0 || c >= C) continue;
       const uint16_t* row = gc + (size_t)c * g.DPmax;
-      double accd = 0.0;
-      for (int c8 = 0; c8 < dp; c8 += 8) {
-        const u32x4_t u = *reinterpret_cast<const u32x4_t*>(row + c8);
+      // the whole row in flight at once (up to 16 pieces of 8 channels), then
+      // the products in channel order
+      u32x4_t ur[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t wj = u[j];
-          const double d0 = xs[c8 + 2 * j] - (double)__uint_as_float(wj << 16);
-          const double d1 = xs[c8 + 2 * j + 1] - (double)__uint_as_float(wj & 0xFFFF0000u);
-          accd = fma(d0, d0, accd);
-          accd = fma(d1, d1, accd);
+      for (int i = 0; i < 16; ++i)
+        ur[i] = i * 8 < dp ? *reinterpret_cast<const u32x4_t*>(row + i * 8) : u32x4_t{0u, 0u, 0u, 0u};
+      double accd = 0.0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i * 8 < dp) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t wj = ur[i][j];
+            const double d0 = xs[i * 8 + 2 * j] - (double)__uint_as_float(wj << 16);
+            const double d1 = xs[i * 8 + 2 * j + 1] - (double)__uint_as_float(wj & 0xFFFF0000u);
+            accd = fma(d0, d0, accd);
+            accd = fma(d1, d1, accd);
+          }
         }
       }
       if (accd < bd) { bd = accd; bc = c; }
