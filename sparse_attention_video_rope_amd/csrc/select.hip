@@ -67,15 +67,22 @@ struct Sel {
   int N;
 };
 
+// No fused multiply-adds in the logit and the bin position: every pass must put
+// a key in the same bin, whichever pass the compiler inlines them into.
 __device__ __forceinline__ double logit(const Sel& S, ushort4 z) {
+#pragma clang fp contract(off)
   return ((S.P0[z.x] + S.P1[z.y]) + S.P2[z.z]) * S.inv_sqrt_d;
 }
 __device__ __forceinline__ uint64_t weight_fx(const Sel& S, ushort4 z) {
   return (uint64_t)__double2ull_rn(((S.E0[z.x] * S.E1[z.y]) * S.E2[z.z]) * S.F * S.fx);
 }
-__device__ __forceinline__ double bin_x(const Sel& S, double s) { return (S.smax - s) * S.scale1; }
+__device__ __forceinline__ double bin_x(const Sel& S, double s) {
+#pragma clang fp contract(off)
+  return (S.smax - s) * S.scale1;
+}
 __device__ __forceinline__ int bin1_of(double x) { return min(max((int)x, 0), SEL_NB - 1); }
 __device__ __forceinline__ int bin2_of(double x, int b1) {
+#pragma clang fp contract(off)
   return min(max((int)((x - (double)b1) * SEL_NB), 0), SEL_NB - 1);
 }
 
@@ -205,6 +212,66 @@ __device__ Boundary resolve_small_bin(const SelSmem& sm, int n, bool by_mass, ui
   return r;
 }
 
+// Exact resolution of a boundary bin of at most SEL_CAP keys (candidates already
+// in sm.cs / cj / cw, ncand of them, bin bases bm / bc): a bitonic sort in LDS
+// by (s desc, j asc), then the first position whose running weight reaches tgt
+// (mass) or position tgt - bc - 1 (count).
+__device__ Boundary resolve_lds_bin(const SelSmem& sm, int ncand, bool by_mass, uint64_t tgt, uint64_t bm,
+                                    int64_t bc) {
+  const int tid = threadIdx.x;
+  Boundary r;
+  int P2 = 1;
+  while (P2 < ncand) P2 <<= 1;
+  for (int k = ncand + tid; k < P2; k += NT) { sm.cs[k] = -__builtin_inf(); sm.cj[k] = 0x7FFFFFFF; sm.cw[k] = 0; }
+  __syncthreads();
+  for (int size = 2; size <= P2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P2 / 2; i += NT) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const double s0 = sm.cs[lo], s1 = sm.cs[hi];
+        const int j0 = sm.cj[lo], j1 = sm.cj[hi];
+        const bool hi_first = s1 > s0 || (s1 == s0 && j1 < j0);
+        if (hi_first == up) {
+          sm.cs[lo] = s1; sm.cs[hi] = s0;
+          sm.cj[lo] = j1; sm.cj[hi] = j0;
+          const uint64_t w0 = sm.cw[lo];
+          sm.cw[lo] = sm.cw[hi]; sm.cw[hi] = w0;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int kb;
+  if (by_mass) {
+    // running mass over the sorted candidates; first position reaching tgt
+    constexpr int PER = SEL_CAP / NT;
+    uint64_t lw = 0;
+    for (int i = 0; i < PER; ++i) { const int k = tid * PER + i; if (k < ncand) lw += sm.cw[k]; }
+    uint64_t tot;
+    uint64_t run = bm + block_incl_scan<uint64_t, NT>(lw, sm.u64tmp, &tot) - lw;
+    if (tid == 0) sm.misc[2] = ncand - 1;
+    __syncthreads();
+    for (int i = 0; i < PER; ++i) {
+      const int k = tid * PER + i;
+      if (k >= ncand) break;
+      if (run < tgt && run + sm.cw[k] >= tgt) { sm.misc[2] = k; break; }
+      run += sm.cw[k];
+    }
+    __syncthreads();
+    kb = sm.misc[2];
+  } else {
+    kb = (int)((int64_t)tgt - bc - 1);
+  }
+  r.tau = sm.cs[kb];
+  int k0 = kb;
+  while (k0 > 0 && sm.cs[k0 - 1] == r.tau) --k0;
+  r.m = kb - k0 + 1;
+  r.count = (int)bc + kb + 1;
+  __syncthreads();
+  return r;
+}
+
 // by_mass with rho > 0: the target is ceil(rho * total mass), the total (returned
 // in *zmass) taken from the level-1 histogram (integer sums, exact).
 // pre_hc: level-1 key counts of the same bins, computed earlier (count mode
@@ -257,6 +324,21 @@ __device__ Boundary find_boundary(const Sel& S, const SelSmem& sm, bool by_mass,
     __syncthreads();
     return resolve_small_bin(sm, n1, by_mass, tgt, bm, bc);
   }
+  if (n1 > 64 && n1 <= SEL_CAP) {
+    // ---- at most SEL_CAP keys in the boundary bin: sort them in LDS (no level-2 pass)
+    if (tid == 0) sm.misc[1] = 0;
+    __syncthreads();
+    each_key(S, [&](int j, ushort4 z) {
+      const double s = logit(S, z);
+      if (bin1_of(bin_x(S, s)) != B1) return;
+      const int k = atomicAdd(&sm.misc[1], 1);
+      sm.cs[k] = s;
+      sm.cj[k] = j;
+      sm.cw[k] = by_mass ? weight_fx(S, z) : 0;
+    });
+    __syncthreads();
+    return resolve_lds_bin(sm, n1, by_mass, tgt, bm, bc);
+  }
   // ---- level 2 ------------------------------------------------------------
   for (int b = tid; b < SEL_NB; b += NT) { sm.hc[b] = 0; sm.hm[b] = 0; }
   __syncthreads();
@@ -285,55 +367,7 @@ __device__ Boundary find_boundary(const Sel& S, const SelSmem& sm, bool by_mass,
       sm.cw[k] = by_mass ? weight_fx(S, z) : 0;
     });
     __syncthreads();
-    int P2 = 1;
-    while (P2 < ncand) P2 <<= 1;
-    for (int k = ncand + tid; k < P2; k += NT) { sm.cs[k] = -__builtin_inf(); sm.cj[k] = 0x7FFFFFFF; sm.cw[k] = 0; }
-    __syncthreads();
-    for (int size = 2; size <= P2; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < P2 / 2; i += NT) {
-          const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
-          const bool up = (lo & size) == 0;
-          const double s0 = sm.cs[lo], s1 = sm.cs[hi];
-          const int j0 = sm.cj[lo], j1 = sm.cj[hi];
-          const bool hi_first = s1 > s0 || (s1 == s0 && j1 < j0);
-          if (hi_first == up) {
-            sm.cs[lo] = s1; sm.cs[hi] = s0;
-            sm.cj[lo] = j1; sm.cj[hi] = j0;
-            const uint64_t w0 = sm.cw[lo];
-            sm.cw[lo] = sm.cw[hi]; sm.cw[hi] = w0;
-          }
-        }
-        __syncthreads();
-      }
-    }
-    int kb;
-    if (by_mass) {
-      // running mass over the sorted candidates; first position reaching tgt
-      constexpr int PER = SEL_CAP / NT;
-      uint64_t lw = 0;
-      for (int i = 0; i < PER; ++i) { const int k = tid * PER + i; if (k < ncand) lw += sm.cw[k]; }
-      uint64_t tot;
-      uint64_t run = bm + block_incl_scan<uint64_t, NT>(lw, sm.u64tmp, &tot) - lw;
-      if (tid == 0) sm.misc[2] = ncand - 1;
-      __syncthreads();
-      for (int i = 0; i < PER; ++i) {
-        const int k = tid * PER + i;
-        if (k >= ncand) break;
-        if (run < tgt && run + sm.cw[k] >= tgt) { sm.misc[2] = k; break; }
-        run += sm.cw[k];
-      }
-      __syncthreads();
-      kb = sm.misc[2];
-    } else {
-      kb = (int)((int64_t)tgt - bc - 1);
-    }
-    r.tau = sm.cs[kb];
-    int k0 = kb;
-    while (k0 > 0 && sm.cs[k0 - 1] == r.tau) --k0;
-    r.m = kb - k0 + 1;
-    r.count = (int)bc + kb + 1;
-    __syncthreads();
+    r = resolve_lds_bin(sm, ncand, by_mass, tgt, bm, bc);
   } else {
     // ---- many keys in one fine bin (ties): walk its distinct logits --------
     double hi = __builtin_inf();
