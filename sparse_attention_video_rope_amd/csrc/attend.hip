@@ -170,33 +170,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
       qb[kb] = __builtin_bit_cast(bf16x8_t, u);
     }
   }
-  // Q scaled by log2(e) / sqrt(d) (rounded to bf16), so the QK^T product gives
-  // the logits in log2 units and the softmax weight of a logit t is exp2(t -
-  // mref); the MFMA accumulator starts at -mref, so the product yields
-  // t - mref directly
-  const float cs = a.scale_log2;
-#pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) {
-    const u32x4_t u = __builtin_bit_cast(u32x4_t, qb[kb]);
-    u32x4_t w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t wj = u[j];   // through a scalar (a bit_cast of u[j] compiles as u[0])
-      const f32x2_t f = __builtin_convertvector(__builtin_bit_cast(bf16x2_t, wj), f32x2_t) * cs;
-      w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-    }
-    qb[kb] = __builtin_bit_cast(bf16x8_t, w);
-  }
+  // Q stays the exact bf16 row: the QK^T product is the logit in natural units,
+  // scaled by cs = log2(e) / sqrt(d) in fp32 right after the MFMA chain, so
+  // that the softmax weight of a scaled logit t is exp2(t - mref).  The MFMA
+  // accumulator starts at -mref / cs, so the scaled product is t - mref
+  // (up to fp32 rounding).  (A Q operand scaled by cs and rounded to bf16
+  // would add an error of up to 2^-9 sum_i |q_i k_i| cs to every scaled
+  // logit: an error in the exponent that grows with the logits.)
+  const float cs = a.scale_log2, inv_cs = 1.f / a.scale_log2;
   f32x16_t o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
   float mref = 0.f, lsum = 0.f;    // reference (log2 units); set from the first chunk
-  f32x16_t cneg = {};              // -mref in every element: the QK^T accumulator's start
+  f32x16_t cneg = {};              // -mref / cs in every element: the QK^T accumulator's start
   const int nchunks = (r + BN - 1) / BN;
-  // upper bound of this query's scaled logits <q'', k'_j> (q'' the scaled bf16
-  // row): ||q''|| (fp32 sum of exact bf16 squares) times the head's key-norm
-  // bound, with a factor 1 + 2^-12 for the roundings; negative when there is
-  // no bound
+  // upper bound of this query's scaled logits cs <q', k'_j>: ||q'|| (fp32 sum
+  // of exact bf16 squares) times the head's key-norm bound times cs, with a
+  // factor 1 + 2^-12 for the roundings; negative when there is no bound
   float bound = -1.f;
   {
     float qn2 = 0.f;
@@ -212,7 +202,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
     }
     qn2 += __shfl_xor(qn2, 32);
     const float kb_ = knm ? knm[bh] : -1.f;
-    if (kb_ > 0.f) bound = sqrtf(qn2) * kb_ * (1.f + 0x1p-12f);
+    if (kb_ > 0.f) bound = sqrtf(qn2) * kb_ * cs * (1.f + 0x1p-12f);
   }
 
   auto kswz = [](int j) { return D == 64 ? (j >> 1) & 7 : j & (PR - 1); };
@@ -308,6 +298,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
         s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], qb[0], cneg, 0, 0, 0);
 #pragma unroll
         for (int kb = 1; kb < D / 16; ++kb) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kb], qb[kb], s[st], 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[st][v] *= cs;
       }
       const int kleft = r - kc * BN;
       if (!FAST && kleft < BN) {
@@ -348,7 +340,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
             for (int v = 0; v < 16; ++v) s[st][v] -= dm;
           mref += dm;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) cneg[v] = -mref;
+          for (int v = 0; v < 16; ++v) cneg[v] = -mref * inv_cs;
         }
       }
       // the chunk's share of the row sum, in four fp32 partial sums of the
@@ -446,7 +438,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
         for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
       mref = mnew;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) cneg[v] = -mref;
+      for (int v = 0; v < 16; ++v) cneg[v] = -mref * inv_cs;
     }
   };
   const std::false_type general{};

@@ -421,6 +421,43 @@ def test_tie_walk_all_queries_at_the_origin(rho):
     say(f"  max {mx:.2e} mean {mn:.2e}")
 
 
+def _boundary_bin_sizes(s_row, count):
+    """Keys in the level-1 selection bin (2048 equal bins over [min, max] of the
+    row, highest logits first) of the count-th key in (s desc, j asc) order."""
+    smax, smin = s_row.max(), s_row.min()
+    x = (smax - s_row) * (2048.0 / (smax - smin))
+    bins = np.clip(x.astype(np.int64), 0, 2047)
+    order = np.lexsort((np.arange(s_row.size), -s_row))
+    return int(np.sum(bins == bins[order[count - 1]]))
+
+
+@pytest.mark.parametrize("rho", [0.9, 0.5])
+def test_boundary_in_level2_bins(rho):
+    """One key 2^10 times longer than the others (all keys scaled by powers of
+    two, so the inputs stay exact) stretches every cluster's logit range: the
+    other keys crowd into a few of the 2048 level-1 bins, the boundary bin holds
+    more than the 1024 keys the selection sorts directly, and the Top-p pass
+    and the final selection find the boundary in the level-2 bins.  Plan and
+    attention against the oracle."""
+    w = workloads.small("lvl2", 9, 61, 67, 64, (16, 24, 24), "bf16", 30, 12, index=115, H=1, rhos=(rho,))
+    say("level-2 boundary bins", w.N, rho)
+    q, k, v = workloads.generate(w)
+    k = k * 2.0 ** -6
+    k[0, 4321] *= 2.0 ** 10
+    heads = [O.workload_head(w, 0, q[0], k[0], v[0])]
+    o = heads[0]
+    big_t = sum(_boundary_bin_sizes(o["scores"][c], o["t"][c]) > 1024 for c in range(w.Cq) if o["n"][c] > 0)
+    big_r = sum(_boundary_bin_sizes(o["scores"][c], o["r"][c]) > 1024
+                for c in range(w.Cq) if 0 < o["r"][c] < w.N and o["r"][c] != o["t"][c])
+    say(f"  clusters with a boundary bin of more than 1024 keys: Top-p {big_t}, final count {big_r}")
+    assert big_t > 0
+    g = run_gpu(w, inputs=(q, k, v))
+    assert g["status"][1] == 0 and g["status"][3] == 0
+    assert_plan_equal(w, g, heads)
+    mx, mn = assert_attention(g["out"][0], o["out"], w.dtype, "level-2 bins")
+    say(f"  max {mx:.2e} mean {mn:.2e}")
+
+
 @pytest.mark.parametrize("rho", [0.9, 0.5])
 def test_tie_walk_one_key_centroid(rho):
     """Cm = 1: every key has the same code triple, so inside each query
